@@ -1,0 +1,376 @@
+// libmoe C ABI: host-side validation, workspace layout and stage orchestration.
+// The operations are defined in moe.h; every check below runs before any
+// work is enqueued, following the Transformers "Expert parallelism" page's
+// convention of rejecting a bad configuration before anything is sharded.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+thread_local char g_err[1024] = "";
+thread_local hipEvent_t g_prof_events[64];
+thread_local int g_prof_count = 0;
+thread_local int g_kernel_idx = 0;
+thread_local int g_last_kernel_count = 0;
+thread_local const char* g_kernel_names[64];
+
+// Resets the per-call kernel counter; on exit records how many kernels ran.
+struct CallScope {
+  CallScope() { g_kernel_idx = 0; }
+  ~CallScope() { g_last_kernel_count = g_kernel_idx; }
+};
+}  // namespace
+
+moe_status set_error(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void prof_before(const char* name, hipStream_t s) {
+  if (g_kernel_idx < 64) g_kernel_names[g_kernel_idx] = name;
+  if (2 * g_kernel_idx + 1 < g_prof_count) (void)hipEventRecord(g_prof_events[2 * g_kernel_idx], s);
+}
+
+moe_status prof_after(const char* name, hipStream_t s) {
+  const hipError_t e = hipGetLastError();
+  if (2 * g_kernel_idx + 1 < g_prof_count) (void)hipEventRecord(g_prof_events[2 * g_kernel_idx + 1], s);
+  ++g_kernel_idx;
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_desc(const moe_layer_desc* d) {
+  if (d == nullptr) return set_error(MOE_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->num_tokens < 0) return set_error(MOE_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)d->num_tokens);
+  if (d->hidden <= 0 || d->hidden % 8 != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", d->hidden);
+  if (d->intermediate <= 0 || d->intermediate % 8 != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "intermediate must be a positive multiple of 8 (got %d)", d->intermediate);
+  if (d->num_experts < 1) return set_error(MOE_ERR_INVALID_ARG, "num_experts must be >= 1 (got %d)", d->num_experts);
+  if (d->top_k < 1 || d->top_k > d->num_experts)
+    return set_error(MOE_ERR_INVALID_ARG, "top_k must be in [1, num_experts] (got %d, E=%d)", d->top_k, d->num_experts);
+  if (d->local_begin < 0 || d->local_count < 1 || int64_t(d->local_begin) + d->local_count > d->num_experts)
+    return set_error(MOE_ERR_INVALID_ARG, "local experts [%d, %d+%d) do not fit in [0, %d)", d->local_begin,
+                     d->local_begin, d->local_count, d->num_experts);
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return set_error(MOE_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (isnan(d->capacity_factor) || isinf(d->capacity_factor))
+    return set_error(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
+  if (d->num_tokens * int64_t(d->top_k) > INT32_MAX)
+    return set_error(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be below 2^31");
+  if (d->top_k > 32) return set_error(MOE_ERR_UNSUPPORTED, "top_k above 32 is not supported (got %d)", d->top_k);
+  if (d->num_experts > 4096) return set_error(MOE_ERR_UNSUPPORTED, "num_experts above 4096 is not supported");
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_layer_desc* d) {
+  if (d->capacity_factor <= 0.0f) return -1;
+  const double c = floor(double(d->capacity_factor) * double(d->num_tokens) * double(d->top_k) / double(d->num_experts));
+  return c > double(INT32_MAX) ? int64_t(INT32_MAX) : int64_t(c);
+}
+
+int64_t max_pairs_of(const moe_layer_desc* d) {
+  const int64_t n = d->num_tokens * d->top_k;
+  const int64_t c = capacity_of(d);
+  return c < 0 ? n : std::min<int64_t>(n, int64_t(d->local_count) * c);
+}
+
+// Layout of the moe_layer_forward workspace.
+struct LayerWs {
+  int32_t* topk_ids;
+  float* topk_w;
+  float* topk_logit;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_row;
+  int64_t* num_dropped;
+  void* dispatch;
+  void* x_sorted;
+  void* h;
+  void* y_sorted;
+  size_t bytes;
+};
+
+LayerWs layer_layout(const moe_layer_desc* d, void* base) {
+  const int64_t n = d->num_tokens * d->top_k;
+  const int64_t pm = max_pairs_of(d);
+  const size_t dt = dtype_bytes(d->dtype);
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  LayerWs w{};
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + o : nullptr;
+    o += align_up(bytes, 256);
+    return r;
+  };
+  w.topk_ids = static_cast<int32_t*>(take(size_t(n) * 4));
+  w.topk_w = static_cast<float*>(take(size_t(n) * 4));
+  w.topk_logit = static_cast<float*>(take(size_t(n) * 4));
+  w.counts = static_cast<int32_t*>(take(size_t(d->num_experts) * 4));
+  w.offsets = static_cast<int32_t*>(take(size_t(d->local_count + 1) * 4));
+  w.sorted_pairs = static_cast<int32_t*>(take(size_t(pm) * 4));
+  w.pair_row = static_cast<int32_t*>(take(size_t(n) * 4));
+  w.num_dropped = static_cast<int64_t*>(take(8));
+  w.dispatch = take(dispatch_scratch_bytes(d));
+  w.x_sorted = take(size_t(pm) * d->hidden * dt);
+  w.h = take(size_t(pm) * d->intermediate * dt);
+  w.y_sorted = take(size_t(pm) * d->hidden * dt);
+  w.bytes = o;
+  return w;
+}
+
+size_t stage_bytes(const moe_layer_desc* d, int32_t stage) {
+  switch (stage) {
+    case MOE_STAGE_ROUTE:
+    case MOE_STAGE_COMBINE:
+      return 0;
+    case MOE_STAGE_DISPATCH:
+      return dispatch_scratch_bytes(d);
+    case MOE_STAGE_FFN:
+      return align_up(size_t(max_pairs_of(d)) * d->intermediate * dtype_bytes(d->dtype), 256);
+    case MOE_STAGE_LAYER:
+      return layer_layout(d, nullptr).bytes;
+    default:
+      return 0;
+  }
+}
+
+#define REQUIRE_PTR(p, a)                                                                                  \
+  do {                                                                                                     \
+    if ((p) == nullptr) return set_error(MOE_ERR_INVALID_ARG, "%s is NULL", #p);                           \
+    if (!aligned((p), (a))) return set_error(MOE_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, int(a)); \
+  } while (0)
+#define OPTIONAL_PTR(p, a)                                                                                  \
+  do {                                                                                                     \
+    if ((p) != nullptr && !aligned((p), (a)))                                                              \
+      return set_error(MOE_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, int(a));                       \
+  } while (0)
+
+moe_status check_ws(const moe_layer_desc* d, int32_t stage, const void* ws, size_t ws_bytes) {
+  const size_t need = stage_bytes(d, stage);
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < need)
+    return set_error(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                     ws == nullptr ? " (NULL)" : "");
+  if (!aligned(ws, 256)) return set_error(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+moe_status route_checks(const moe_layer_desc* d, const void* x, const void* w_router, const float* b_router,
+                        const float* logits_in, const float* logits_out, const int32_t* topk_ids, const float* topk_w,
+                        const float* topk_logit) {
+  if (d->num_experts > 256) return set_error(MOE_ERR_UNSUPPORTED, "route: num_experts above 256 is not supported");
+  if (logits_in == nullptr) {
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(w_router, 16);
+    OPTIONAL_PTR(b_router, 4);
+  } else {
+    REQUIRE_PTR(logits_in, 4);
+  }
+  OPTIONAL_PTR(logits_out, 4);
+  REQUIRE_PTR(topk_ids, 4);
+  REQUIRE_PTR(topk_w, 4);
+  OPTIONAL_PTR(topk_logit, 4);
+  return MOE_OK;
+}
+
+moe_status dispatch_checks(const moe_layer_desc* d, const void* x, const int32_t* topk_ids, const float* topk_logit,
+                           const int32_t* counts, const int32_t* offsets, const int32_t* sorted_pairs,
+                           const int32_t* pair_row, const void* x_sorted, const int64_t* num_dropped) {
+  if (d->local_count > 3000) return set_error(MOE_ERR_UNSUPPORTED, "dispatch: local_count above 3000 is not supported");
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(topk_ids, 4);
+  if (d->capacity_factor > 0) {
+    REQUIRE_PTR(topk_logit, 4);
+  }
+  REQUIRE_PTR(counts, 4);
+  REQUIRE_PTR(offsets, 4);
+  REQUIRE_PTR(sorted_pairs, 4);
+  REQUIRE_PTR(pair_row, 4);
+  REQUIRE_PTR(x_sorted, 16);
+  OPTIONAL_PTR(num_dropped, 8);
+  return MOE_OK;
+}
+
+moe_status ffn_checks(const void* x_sorted, const int32_t* offsets, const void* w_gate, const void* w_up,
+                      const void* w_down, const void* y_sorted) {
+  REQUIRE_PTR(x_sorted, 16);
+  REQUIRE_PTR(offsets, 4);
+  REQUIRE_PTR(w_gate, 16);
+  REQUIRE_PTR(w_up, 16);
+  REQUIRE_PTR(w_down, 16);
+  REQUIRE_PTR(y_sorted, 16);
+  return MOE_OK;
+}
+
+moe_status combine_checks(const void* y_sorted, const int32_t* pair_row, const float* topk_w, const void* y) {
+  REQUIRE_PTR(y_sorted, 16);
+  REQUIRE_PTR(pair_row, 4);
+  REQUIRE_PTR(topk_w, 4);
+  REQUIRE_PTR(y, 16);
+  return MOE_OK;
+}
+
+#define TRY(expr)                          \
+  do {                                     \
+    const moe_status _s = (expr);          \
+    if (_s != MOE_OK) return _s;           \
+  } while (0)
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "libmoe 0.1 (gfx950)"; }
+
+moe_status moe_ep_local_range(int32_t num_experts, int32_t ep_size, int32_t rank, int32_t* begin, int32_t* count) {
+  if (begin == nullptr || count == nullptr) return set_error(MOE_ERR_INVALID_ARG, "begin/count are NULL");
+  if (num_experts < 1) return set_error(MOE_ERR_INVALID_ARG, "num_experts must be >= 1");
+  if (ep_size < 1) return set_error(MOE_ERR_INVALID_ARG, "ep_size must be >= 1");
+  if (rank < 0) return set_error(MOE_ERR_INVALID_ARG, "rank must be >= 0");
+  if (num_experts % ep_size != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "ep_size %d does not divide num_experts %d", ep_size, num_experts);
+  const int32_t per = num_experts / ep_size;
+  *begin = (rank % ep_size) * per;
+  *count = per;
+  return MOE_OK;
+}
+
+int64_t moe_capacity(const moe_layer_desc* d) {
+  if (check_desc(d) != MOE_OK) return -1;
+  return capacity_of(d);
+}
+
+int64_t moe_max_pairs(const moe_layer_desc* d) {
+  if (check_desc(d) != MOE_OK) return -1;
+  return max_pairs_of(d);
+}
+
+moe_status moe_workspace_size(const moe_layer_desc* d, int32_t stage, size_t* bytes) {
+  TRY(check_desc(d));
+  if (bytes == nullptr) return set_error(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_LAYER) return set_error(MOE_ERR_INVALID_ARG, "unknown stage %d", stage);
+  *bytes = stage_bytes(d, stage);
+  return MOE_OK;
+}
+
+moe_status moe_profile_events(void* const* events, int32_t count) {
+  if (events == nullptr || count <= 0) {
+    g_prof_count = 0;
+    return MOE_OK;
+  }
+  if (count > 64) return set_error(MOE_ERR_INVALID_ARG, "at most 64 profiling events");
+  for (int i = 0; i < count; ++i) {
+    if (events[i] == nullptr) return set_error(MOE_ERR_INVALID_ARG, "profiling event %d is NULL", i);
+    g_prof_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_prof_count = count;
+  return MOE_OK;
+}
+
+const char* moe_profile_kernel_name(int32_t i) {
+  if (i < 0 || i >= g_last_kernel_count || i >= 64) return nullptr;
+  return g_kernel_names[i];
+}
+
+int32_t moe_profile_kernel_count(void) { return g_last_kernel_count; }
+
+moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_router, const float* b_router,
+                     const float* logits_in, float* logits_out, int32_t* topk_ids, float* topk_w, float* topk_logit,
+                     void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(route_checks(d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit));
+  TRY(check_ws(d, MOE_STAGE_ROUTE, ws, ws_bytes));
+  RouteArgs a{d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit,
+              static_cast<hipStream_t>(stream)};
+  return launch_route(a);
+}
+
+moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* topk_ids, const float* topk_logit,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_row, void* x_sorted,
+                        int64_t* num_dropped, void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(dispatch_checks(d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped));
+  TRY(check_ws(d, MOE_STAGE_DISPATCH, ws, ws_bytes));
+  DispatchArgs a{d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped,
+                 carve_dispatch_scratch(d, ws), capacity_of(d), static_cast<hipStream_t>(stream)};
+  return launch_dispatch(a);
+}
+
+moe_status moe_grouped_ffn(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets, const void* w_gate,
+                           const void* w_up, const void* w_down, void* y_sorted, void* ws, size_t ws_bytes,
+                           void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(ffn_checks(x_sorted, offsets, w_gate, w_up, w_down, y_sorted));
+  TRY(check_ws(d, MOE_STAGE_FFN, ws, ws_bytes));
+  FfnArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, ws, max_pairs_of(d), static_cast<hipStream_t>(stream)};
+  return launch_grouped_ffn(a);
+}
+
+moe_status moe_combine(const moe_layer_desc* d, const void* y_sorted, const int32_t* pair_row, const float* topk_w,
+                       void* y, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(combine_checks(y_sorted, pair_row, topk_w, y));
+  CombineArgs a{d, y_sorted, pair_row, topk_w, y, static_cast<hipStream_t>(stream)};
+  return launch_combine(a);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void* w_router, const float* b_router,
+                             const void* w_gate, const void* w_up, const void* w_down, void* y, int32_t* topk_ids_out,
+                             float* topk_w_out, int32_t* counts_out, int64_t* num_dropped_out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(check_ws(d, MOE_STAGE_LAYER, ws, ws_bytes));
+  LayerWs w = layer_layout(d, ws);
+  int32_t* ids = topk_ids_out ? topk_ids_out : w.topk_ids;
+  float* tw = topk_w_out ? topk_w_out : w.topk_w;
+  int32_t* counts = counts_out ? counts_out : w.counts;
+  int64_t* dropped = num_dropped_out ? num_dropped_out : w.num_dropped;
+  const bool cap = capacity_of(d) >= 0;
+  TRY(route_checks(d, x, w_router, b_router, nullptr, nullptr, ids, tw, w.topk_logit));
+  TRY(dispatch_checks(d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped));
+  TRY(ffn_checks(w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted));
+  TRY(combine_checks(w.y_sorted, w.pair_row, tw, y));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, ids, tw, cap ? w.topk_logit : nullptr, s};
+  TRY(launch_route(ra));
+  DispatchArgs da{d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped,
+                  carve_dispatch_scratch(d, w.dispatch), capacity_of(d), s};
+  TRY(launch_dispatch(da));
+  FfnArgs fa{d, w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted, w.h, max_pairs_of(d), s};
+  TRY(launch_grouped_ffn(fa));
+  CombineArgs ca{d, w.y_sorted, w.pair_row, tw, y, s};
+  return launch_combine(ca);
+}
+
+}  // extern "C"

@@ -1,0 +1,378 @@
+// Stage 2: token dispatch on one GPU.
+//
+// Hugging Face Transformers "Expert parallelism", section "Token dispatch":
+// every (token, expert) pair is sent to the owner of its expert, which runs
+// its local experts on what it receives.  On one GPU that is a permutation of
+// the pairs into contiguous per-expert segments: a histogram of pairs per
+// expert (the glossary snippet's bincount), an exclusive scan into segment
+// offsets, and a stable scatter; the glossary's "Load balancing and capacity"
+// adds an optional per-expert limit whose overflow skips the expert.
+//
+// Pair p = t*k + j.  Within a segment, pairs keep ascending p, so the result is
+// unique and matches a stable counting sort exactly:
+//   count     per block of `chunk` pairs, counts over all E experts, built
+//             with a wave64 match-any (ballot over the id bits) so only one
+//             lane per distinct id touches the LDS histogram;
+//   scan      one block: totals per expert, (capacity), exclusive scans into
+//             segment offsets, and for every (block, expert) the first row of
+//             that block's pairs (a column scan over blocks, one wave each);
+//   scatter   per block again, in rounds of 256 pairs: the rank of a pair
+//             among equal experts is its rank within its wave (match-any +
+//             popcount of lower lanes) plus the counts of earlier waves and
+//             earlier rounds -- no atomics, so the order is deterministic;
+//   capacity  (only with a limit) one block per local expert: radix select
+//             of the C-th largest key (logit desc, then token asc) and a
+//             stable compaction of the kept pairs;
+//   gather    row copies x[t] -> x_sorted[row], one wave per row, 16-byte
+//             vectors.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+int dispatch_chunk(int64_t n_pairs, int32_t local_count) {
+  (void)n_pairs;
+  (void)local_count;
+  return 4 * kDispatchThreads;
+}
+
+size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
+  const int64_t n = d->num_tokens * d->top_k;
+  const int64_t nblk = dispatch_blocks(n, d->local_count);
+  size_t b = 0;
+  b += align_up(size_t(nblk) * d->num_experts * 4, 256);
+  b += align_up(size_t(nblk) * d->local_count * 4, 256);
+  b += align_up(size_t(d->local_count + 1) * 4, 256);
+  if (d->capacity_factor > 0) b += align_up(size_t(n) * 4, 256);
+  return b;
+}
+
+DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
+  const int64_t n = d->num_tokens * d->top_k;
+  const int64_t nblk = dispatch_blocks(n, d->local_count);
+  char* p = static_cast<char*>(ws);
+  DispatchScratch s{};
+  s.blk_all = reinterpret_cast<int32_t*>(p);
+  p += align_up(size_t(nblk) * d->num_experts * 4, 256);
+  s.blk_base = reinterpret_cast<int32_t*>(p);
+  p += align_up(size_t(nblk) * d->local_count * 4, 256);
+  s.pre_off = reinterpret_cast<int32_t*>(p);
+  p += align_up(size_t(d->local_count + 1) * 4, 256);
+  s.tmp_sorted = d->capacity_factor > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;
+  return s;
+}
+
+namespace {
+
+__device__ __forceinline__ int bits_for(int maxval) { return 32 - __clz(maxval); }
+
+// Exclusive scan over the block; *total receives the block sum.  `wsum` holds
+// one int per wave.  Every thread of the block must call it.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < nw ? wsum[lane] : 0;
+    s = wave_inclusive_scan(s);
+    if (lane < nw) wsum[lane] = s;
+  }
+  __syncthreads();
+  const int before = wave > 0 ? wsum[wave - 1] : 0;
+  *total = wsum[nw - 1];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// ---- count ------------------------------------------------------------------
+__global__ __launch_bounds__(kDispatchThreads) void count_kernel(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                                 int E, int chunk, int32_t* __restrict__ blk_all) {
+  extern __shared__ int32_t hist[];  // [E]
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t p0 = int64_t(blockIdx.x) * chunk;
+  const int64_t p1 = min(n_pairs, p0 + chunk);
+  const int bits = bits_for(E);
+  for (int64_t base = p0; base < p1; base += blockDim.x) {
+    const int64_t p = base + threadIdx.x;
+    int id = p < p1 ? ids[p] : E;
+    if (id < 0 || id >= E) id = E;  // sentinel: not counted
+    const uint64_t m = match_any(uint32_t(id), bits, ~uint64_t(0));
+    if (id < E && (m & lanemask_lt()) == 0) atomicAdd(&hist[id], int(__popcll(m)));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blk_all[size_t(blockIdx.x) * E + e] = hist[e];
+}
+
+// ---- scan -------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_all, int nblk, int E,
+                                                            int begin, int L, int64_t cap, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ pre_off,
+                                                            int32_t* __restrict__ blk_base,
+                                                            int64_t* __restrict__ num_dropped) {
+  extern __shared__ int32_t sh[];
+  int32_t* cnt = sh;          // [E]
+  int32_t* pre = sh + E;      // [L + 1]
+  __shared__ int wsum[kScanThreads / 64];
+  __shared__ long long dsum[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  for (int e = tid; e < E; e += kScanThreads) cnt[e] = 0;
+  __syncthreads();
+  const int64_t total = int64_t(nblk) * E;
+  for (int64_t idx = tid; idx < total; idx += kScanThreads) {
+    const int v = blk_all[idx];
+    if (v != 0) atomicAdd(&cnt[int(idx % E)], v);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kScanThreads) counts[e] = cnt[e];
+
+  // segment offsets before (pre) and after (offsets) the capacity cut
+  int carry_pre = 0, carry_post = 0;
+  long long dropped = 0;
+  for (int i0 = 0; i0 < L; i0 += kScanThreads) {
+    const int i = i0 + tid;
+    const int n = i < L ? cnt[begin + i] : 0;
+    const int kept = cap < 0 ? n : int(min<int64_t>(n, cap));
+    dropped += n - kept;
+    int tot_n, tot_k;
+    const int ex_n = block_exclusive_scan(n, wsum, &tot_n);
+    const int ex_k = block_exclusive_scan(kept, wsum, &tot_k);
+    if (i < L) {
+      pre[i] = carry_pre + ex_n;
+      pre_off[i] = carry_pre + ex_n;
+      offsets[i] = carry_post + ex_k;
+    }
+    carry_pre += tot_n;
+    carry_post += tot_k;
+  }
+  if (tid == 0) {
+    pre[L] = carry_pre;
+    pre_off[L] = carry_pre;
+    offsets[L] = carry_post;
+  }
+  // dropped pairs: sum over threads
+  for (int d = 1; d < 64; d <<= 1) dropped += __shfl_xor(dropped, d, 64);
+  if (lane == 0) dsum[wave] = dropped;
+  __syncthreads();
+  if (tid == 0 && num_dropped != nullptr) {
+    long long s = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) s += dsum[w];
+    *num_dropped = s;
+  }
+
+  // first pre-capacity row of every block's pairs of local expert i:
+  // pre[i] + sum over earlier blocks of their count of expert begin+i
+  for (int i = wave; i < L; i += kScanThreads / 64) {
+    int carry = pre[i];
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int b = b0 + lane;
+      const int v = b < nblk ? blk_all[size_t(b) * E + begin + i] : 0;
+      const int incl = wave_inclusive_scan(v);
+      if (b < nblk) blk_base[size_t(b) * L + i] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+}
+
+// ---- scatter ----------------------------------------------------------------
+// CAP: the positions are pre-capacity rows in tmp_sorted; the capacity kernel
+// finishes pair_row for local pairs.
+template <bool CAP>
+__global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                                   int begin, int L, int chunk,
+                                                                   const int32_t* __restrict__ blk_base,
+                                                                   int32_t* __restrict__ out_sorted,
+                                                                   int32_t* __restrict__ pair_row) {
+  extern __shared__ int32_t sh[];
+  int32_t* run = sh;       // [L]      next row of each local expert for this block
+  int32_t* cnt = sh + L;   // [4][L]   pairs of each expert in each wave of this round
+  constexpr int kWaves = kDispatchThreads / 64;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  for (int i = tid; i < L; i += kDispatchThreads) run[i] = blk_base[size_t(blockIdx.x) * L + i];
+  for (int i = tid; i < kWaves * L; i += kDispatchThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t p0 = int64_t(blockIdx.x) * chunk;
+  const int64_t p1 = min(n_pairs, p0 + chunk);
+  const int bits = bits_for(L);
+  for (int64_t base = p0; base < p1; base += kDispatchThreads) {
+    const int64_t p = base + tid;
+    const bool valid = p < p1;
+    const int id = valid ? ids[p] : -1;
+    const int li = (id >= begin && id < begin + L) ? id - begin : L;  // L: not local
+    const uint64_t m = match_any(uint32_t(li), bits, ~uint64_t(0));
+    const uint64_t lower = m & lanemask_lt();
+    if (li < L && lower == 0) cnt[wave * L + li] = int(__popcll(m));
+    __syncthreads();
+    if (li < L) {
+      int pos = run[li] + int(__popcll(lower));
+      for (int w = 0; w < wave; ++w) pos += cnt[w * L + li];
+      out_sorted[pos] = int32_t(p);
+      if (!CAP) pair_row[p] = pos;
+    } else if (valid) {
+      pair_row[p] = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < L; i += kDispatchThreads) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        s += cnt[w * L + i];
+        cnt[w * L + i] = 0;
+      }
+      run[i] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- capacity -----------------------------------------------------------------
+// Order-preserving key of a float32 logit (larger logit -> larger key); -0.0
+// and +0.0 map to one key because they compare equal.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kCapThreads = 1024;
+
+__global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ tmp_sorted,
+                                                               const int32_t* __restrict__ pre_off,
+                                                               const int32_t* __restrict__ offsets,
+                                                               const float* __restrict__ topk_logit, int cap,
+                                                               int32_t* __restrict__ sorted_pairs,
+                                                               int32_t* __restrict__ pair_row) {
+  __shared__ int hist[256];
+  __shared__ int wsum[kCapThreads / 64];
+  __shared__ uint32_t s_digit;
+  __shared__ int s_want;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x;
+  const int a = pre_off[i];
+  const int n = pre_off[i + 1] - a;
+  const int out0 = offsets[i];
+  const int32_t* seg = tmp_sorted + a;
+
+  if (n <= cap) {
+    for (int r = tid; r < n; r += kCapThreads) {
+      const int p = seg[r];
+      sorted_pairs[out0 + r] = p;
+      pair_row[p] = out0 + r;
+    }
+    return;
+  }
+
+  // radix select, most significant byte first: find the key value thr of the
+  // cap-th largest key and how many keys equal to thr are still wanted
+  uint32_t prefix = 0, mask = 0;
+  int want = cap;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int j = tid; j < 256; j += kCapThreads) hist[j] = 0;
+    __syncthreads();
+    for (int r = tid; r < n; r += kCapThreads) {
+      const uint32_t key = logit_key(topk_logit[seg[r]]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0;
+      for (int dgt = 255; dgt >= 0; --dgt) {
+        if (cum + hist[dgt] >= want) {
+          s_digit = uint32_t(dgt);
+          s_want = want - cum;
+          break;
+        }
+        cum += hist[dgt];
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    mask |= 0xFFu << shift;
+    want = s_want;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;
+  const int need_eq = want;  // keys equal to thr kept: the first need_eq in segment (= token) order
+
+  int carry_eq = 0, carry_keep = 0;
+  for (int r0 = 0; r0 < n; r0 += kCapThreads) {
+    const int r = r0 + tid;
+    const bool in = r < n;
+    const int p = in ? seg[r] : 0;
+    const uint32_t key = in ? logit_key(topk_logit[p]) : 0u;
+    const int eq = (in && key == thr) ? 1 : 0;
+    int tot_eq, tot_keep;
+    const int ex_eq = block_exclusive_scan(eq, wsum, &tot_eq);
+    const int keep = (in && (key > thr || (eq && carry_eq + ex_eq < need_eq))) ? 1 : 0;
+    const int ex_keep = block_exclusive_scan(keep, wsum, &tot_keep);
+    if (keep) {
+      const int pos = out0 + carry_keep + ex_keep;
+      sorted_pairs[pos] = p;
+      pair_row[p] = pos;
+    } else if (in) {
+      pair_row[p] = -1;
+    }
+    carry_eq += tot_eq;
+    carry_keep += tot_keep;
+  }
+}
+
+// ---- gather -----------------------------------------------------------------
+constexpr int kGatherRowsPerBlock = 4;  // one wave per row
+
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ sorted_pairs,
+                                                     const int32_t* __restrict__ offsets, int L, int k, int vec_per_row,
+                                                     uint4* __restrict__ xs) {
+  const int P = offsets[L];
+  const int lane = threadIdx.x & 63;
+  const int64_t q = int64_t(blockIdx.x) * kGatherRowsPerBlock + (threadIdx.x >> 6);
+  if (q >= P) return;
+  const int t = sorted_pairs[q] / k;
+  const uint4* src = x + size_t(t) * vec_per_row;
+  uint4* dst = xs + size_t(q) * vec_per_row;
+  for (int c = lane; c < vec_per_row; c += 64) dst[c] = src[c];
+}
+
+}  // namespace
+
+moe_status launch_dispatch(const DispatchArgs& a) {
+  const moe_layer_desc* d = a.d;
+  const int64_t n = d->num_tokens * d->top_k;
+  const int chunk = dispatch_chunk(n, d->local_count);
+  const int nblk = int(dispatch_blocks(n, d->local_count));
+  const int E = d->num_experts, L = d->local_count, begin = d->local_begin;
+  const bool cap = a.capacity >= 0;
+
+  MOE_LAUNCH("dispatch_count", count_kernel, dim3(nblk), dim3(kDispatchThreads), size_t(E) * 4, a.s, a.topk_ids, n, E,
+             chunk, a.scr.blk_all);
+  MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all, nblk,
+             E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.num_dropped);
+  const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
+  if (cap) {
+    MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
+               begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row);
+    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), 0, a.s, a.scr.tmp_sorted, a.scr.pre_off,
+               a.offsets, a.topk_logit, int(a.capacity), a.sorted_pairs, a.pair_row);
+  } else {
+    MOE_LAUNCH("dispatch_scatter", scatter_kernel<false>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids,
+               n, begin, L, chunk, a.scr.blk_base, a.sorted_pairs, a.pair_row);
+  }
+  const int64_t max_rows = cap ? (n < int64_t(L) * a.capacity ? n : int64_t(L) * a.capacity) : n;
+  if (max_rows > 0) {
+    const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
+    const dim3 grid(unsigned((max_rows + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock));
+    MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.x), a.sorted_pairs,
+               a.offsets, L, d->top_k, vec_per_row, static_cast<uint4*>(a.x_sorted));
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,225 @@
+// Stage 3: the local experts as one grouped GEMM over ragged segments.
+//
+// Ultralytics glossary "Expert Parallelism", section "How tokens move between
+// GPUs", step 3: each GPU runs its local experts on the tokens it received.
+// The Transformers page names the expert kernel style "grouped_gemm" and says
+// the expert weights are split along the expert dimension, which is the
+// stacked [L, out, in] layout used here.  Expert i owns sorted rows
+// [offsets[i], offsets[i+1]) and computes the SwiGLU feed-forward
+//   h = silu(X Wg_i^T) * (X Wu_i^T)      (gate/up kernel, SwiGLU in its epilogue)
+//   y = h Wd_i^T                         (down kernel)
+// with float32 accumulation; h is rounded to the storage type once.
+//
+// Work split: one block computes a BM x BN output tile (both the gate and the
+// up tile for the gate/up kernel, so SiLU(gate)*up is formed in registers).
+// grid.x enumerates m-tile slots: expert i contributes ceil(n_i / BM) of them,
+// found on the device from `offsets` (no host sync), and the grid is sized for
+// the worst case ceil(P_max / BM) + L so surplus blocks exit at once.
+// grid.y enumerates n-tiles.  Four waves split the tile 2 x 2; each wave owns
+// 64 x 64 per matrix as 2 x 2 MFMA 32x32 blocks (bf16: v_mfma 32x32x16, the
+// lane holds 8 consecutive k of its row/column; f32: eight 32x32x2 steps over
+// the same 8 values).  A and B k-slices are staged through double-buffered LDS
+// with rows padded to 80 bytes so the 16-byte fragment reads of eight lanes
+// fall in distinct banks.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 128, BN = 128, kThreads = 256;
+
+template <typename T> struct Gemm;
+template <> struct Gemm<bf16_t> {
+  static constexpr int BK = 32;       // k per LDS stage
+  static constexpr int kLd = BK + 8;  // LDS row stride in elements (80 bytes)
+  static constexpr int kFragVec = 1;  // uint4 per lane per 16-k chunk
+  __device__ static void mma(const uint4* a, const uint4* b, f32x16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[0]), __builtin_bit_cast(bf16x8_t, b[0]),
+                                                c, 0, 0, 0);
+  }
+};
+template <> struct Gemm<float> {
+  static constexpr int BK = 16;
+  static constexpr int kLd = BK + 4;  // 80 bytes
+  static constexpr int kFragVec = 2;
+  __device__ static void mma(const uint4* a, const uint4* b, f32x16_t& c) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].x), __uint_as_float(b[v].x), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].y), __uint_as_float(b[v].y), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].z), __uint_as_float(b[v].z), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].w), __uint_as_float(b[v].w), c, 0, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// NMAT = 2: gate and up products with the SwiGLU epilogue; NMAT = 1: plain product.
+template <typename T, int NMAT>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restrict__ A,
+                                                                const int32_t* __restrict__ offsets,
+                                                                const T* __restrict__ B0, const T* __restrict__ B1,
+                                                                T* __restrict__ C, int L, int N, int K) {
+  using G = Gemm<T>;
+  constexpr int BK = G::BK, kLd = G::kLd, FV = G::kFragVec;
+  constexpr int EPV = 16 / int(sizeof(T));     // elements per 16-byte vector
+  constexpr int CPR = BK / EPV;                // 16-byte chunks per tile row (4)
+  constexpr int CPT = BM * CPR / kThreads;     // chunks per thread per matrix (2)
+  static_assert(BM == BN, "one chunk map serves A and B");
+
+  // ---- which expert and rows this block owns --------------------------------
+  int g = blockIdx.x;
+  int expert = -1, row0 = 0, rows = 0;
+  {
+    int prev = offsets[0];
+    for (int i = 0; i < L; ++i) {
+      const int nxt = offsets[i + 1];
+      const int tiles = (nxt - prev + BM - 1) / BM;
+      if (g < tiles) {
+        expert = i;
+        row0 = prev + g * BM;
+        rows = min(BM, nxt - row0);
+        break;
+      }
+      g -= tiles;
+      prev = nxt;
+    }
+  }
+  if (expert < 0) return;
+  const int n0 = blockIdx.y * BN;
+  const size_t boff = size_t(expert) * N * K;
+  const T* Bm[2] = {B0 + boff, NMAT > 1 ? B1 + boff : B0 + boff};
+
+  __shared__ __attribute__((aligned(16))) T As[2][BM * kLd];
+  __shared__ __attribute__((aligned(16))) T Bs[2][NMAT][BN * kLd];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+
+  uint4 ra[CPT], rb[NMAT][CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / CPR, col = c % CPR;
+      const int kk = k0 + col * EPV;
+      const bool kok = kk < K;
+      const int ar = min(r, rows - 1);  // rows past the segment repeat its last row; never stored
+      ra[j] = kok ? *reinterpret_cast<const uint4*>(A + size_t(row0 + ar) * K + kk) : zero;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const int nr = n0 + r;
+        rb[m][j] = (kok && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / CPR, col = c % CPR;
+      *reinterpret_cast<uint4*>(&As[buf][r * kLd + col * EPV]) = ra[j];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) *reinterpret_cast<uint4*>(&Bs[buf][m][r * kLd + col * EPV]) = rb[m][j];
+    }
+  };
+
+  f32x16_t acc[NMAT][2][2];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.0f;
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int frow = lane & 31;            // row (A) / column (B) inside a 32-block
+  const int fk = 8 * (lane >> 5);        // first of the lane's 8 k values in a 16-k chunk
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kc = 0; kc < BK / 16; ++kc) {
+      uint4 af[2][FV], bfr[NMAT][2][FV];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4* p = reinterpret_cast<const uint4*>(&As[buf][(wm * 64 + i * 32 + frow) * kLd + kc * 16 + fk]);
+#pragma unroll
+        for (int v = 0; v < FV; ++v) af[i][v] = p[v];
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4* p =
+              reinterpret_cast<const uint4*>(&Bs[buf][m][(wn * 64 + j * 32 + frow) * kLd + kc * 16 + fk]);
+#pragma unroll
+          for (int v = 0; v < FV; ++v) bfr[m][j][v] = p[v];
+        }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) G::mma(af[i], bfr[m][j], acc[m][i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: 32x32 accumulator layout, lane -> column (lane & 31),
+  // register r -> row 8*(r/4) + 4*(lane/32) + r%4 ------------------------------
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rt = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (rt < rows && col < N) {
+          float v;
+          if constexpr (NMAT == 2) {
+            v = silu(acc[0][i][j][r]) * acc[1][i][j][r];
+          } else {
+            v = acc[0][i][j][r];
+          }
+          C[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(v);
+        }
+      }
+    }
+}
+
+template <typename T>
+moe_status launch_t(const FfnArgs& a) {
+  const moe_layer_desc* d = a.d;
+  const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  const unsigned mslots = unsigned((a.max_pairs + BM - 1) / BM + L);
+  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0, a.s,
+             static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
+             static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H);
+  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0, a.s,
+             static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down), static_cast<const T*>(a.w_down),
+             static_cast<T*>(a.y_sorted), L, H, I);
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status launch_grouped_ffn(const FfnArgs& a) {
+  if (a.max_pairs <= 0) return MOE_OK;
+  return a.d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
+}
+
+}  // namespace moe

@@ -1,0 +1,104 @@
+// Host-side interface between the C ABI (api.hip) and the kernel files.
+// Arguments reaching these launchers have been validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---- error and profiling plumbing (defined in api.hip) --------------------
+moe_status set_error(moe_status st, const char* fmt, ...);
+void prof_before(const char* name, hipStream_t s);
+moe_status prof_after(const char* name, hipStream_t s);
+
+#define MOE_LAUNCH(name, kernel, grid, block, lds, stream, ...)                 \
+  do {                                                                          \
+    ::moe::prof_before(name, stream);                                           \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);          \
+    const moe_status _moe_st = ::moe::prof_after(name, stream);                 \
+    if (_moe_st != MOE_OK) return _moe_st;                                      \
+  } while (0)
+
+// ---- sizes ------------------------------------------------------------------
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline size_t dtype_bytes(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+// Pairs handled by one block of the dispatch histogram/scatter kernels.
+constexpr int kDispatchThreads = 256;
+int dispatch_chunk(int64_t n_pairs, int32_t local_count);
+inline int64_t dispatch_blocks(int64_t n_pairs, int32_t local_count) {
+  const int c = dispatch_chunk(n_pairs, local_count);
+  return (n_pairs + c - 1) / c;
+}
+
+// ---- stage launchers --------------------------------------------------------
+struct RouteArgs {
+  const moe_layer_desc* d;
+  const void* x;
+  const void* w_router;
+  const float* b_router;
+  const float* logits_in;
+  float* logits_out;
+  int32_t* topk_ids;
+  float* topk_w;
+  float* topk_logit;
+  hipStream_t s;
+};
+moe_status launch_route(const RouteArgs& a);
+
+// Dispatch scratch, carved from the caller's workspace.
+struct DispatchScratch {
+  int32_t* blk_all;    // [nblk, E]   per-block counts over all experts
+  int32_t* blk_base;   // [nblk, L]   first (pre-capacity) row of each block's pairs
+  int32_t* pre_off;    // [L+1]       pre-capacity segment offsets
+  int32_t* tmp_sorted; // [T*k]       pre-capacity permutation (capacity only)
+};
+size_t dispatch_scratch_bytes(const moe_layer_desc* d);
+DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws);
+
+struct DispatchArgs {
+  const moe_layer_desc* d;
+  const void* x;
+  const int32_t* topk_ids;
+  const float* topk_logit;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_row;
+  void* x_sorted;
+  int64_t* num_dropped;
+  DispatchScratch scr;
+  int64_t capacity;  // -1: none
+  hipStream_t s;
+};
+moe_status launch_dispatch(const DispatchArgs& a);
+
+struct FfnArgs {
+  const moe_layer_desc* d;
+  const void* x_sorted;
+  const int32_t* offsets;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* y_sorted;
+  void* h;  // [P_max, I]
+  int64_t max_pairs;
+  hipStream_t s;
+};
+moe_status launch_grouped_ffn(const FfnArgs& a);
+
+struct CombineArgs {
+  const moe_layer_desc* d;
+  const void* y_sorted;
+  const int32_t* pair_row;
+  const float* topk_w;
+  void* y;
+  hipStream_t s;
+};
+moe_status launch_combine(const CombineArgs& a);
+
+}  // namespace moe

@@ -1,0 +1,238 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of one mixture-of-experts layer
+ * on one GPU's share of the experts, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the four steps named on the Ultralytics glossary page
+ * "Expert Parallelism", section "How tokens move between GPUs": route every
+ * token to its k best experts, dispatch each (token, expert) pair to the
+ * expert, run the experts, and combine the results weighted by the router
+ * scores.  The Hugging Face Transformers page "Expert parallelism", section
+ * "Token dispatch", fixes what one rank does with its share: it runs only
+ * its local experts on the pairs routed to them, and the router yields
+ * global expert ids so that the owner of every expert can be found.  The
+ * collectives that move pairs between GPUs are outside this library: the
+ * calls below are the single-GPU core (permute -> compute -> un-permute).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers marked "device" are GPU memory on the current HIP device;
+ *    "host" pointers are CPU memory.  The caller owns every buffer; the
+ *    library allocates no memory and keeps no state between calls apart from
+ *    a thread-local error message and the optional profiling events.
+ *  - Tensors are dense and row-major.  Device pointers to activations,
+ *    weights and outputs must be 16-byte aligned; index arrays 4-byte aligned.
+ *  - Activations and weights share one element type, desc->dtype: MOE_BF16
+ *    (bfloat16 storage, float32 accumulation) or MOE_F32.  Router bias,
+ *    logits and routing weights are always float32; ids and rows int32.
+ *  - Weights are stored as a linear layer stores them, [out, in]:
+ *      router  w_router [E, H]
+ *      experts w_gate [L, I, H], w_up [L, I, H], w_down [L, H, I]
+ *    so expert e computes y = (silu(v Wg_e^T) * (v Wu_e^T)) Wd_e^T.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and runs asynchronously; no call synchronises or copies device data to
+ *    the host.  Device-side data produced by an earlier call (ids, offsets,
+ *    rows) is trusted.
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    non-OK status means nothing was enqueued, except MOE_ERR_HIP, which
+ *    reports a failed launch.  moe_last_error() describes the failure.
+ *  - Calls on one stream may share a workspace; concurrent calls need
+ *    distinct workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, range or pointer is not acceptable */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -4          /* the HIP runtime reported an error          */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem statement of one layer on one GPU.
+ *   num_tokens       T >= 0 tokens held by this GPU (T == 0: every call is a
+ *                    successful no-op).
+ *   hidden           H > 0, multiple of 8.
+ *   intermediate     I > 0, multiple of 8 (expert FFN width).
+ *   num_experts      E >= 1 experts in the whole layer (global ids 0..E-1).
+ *   top_k            1 <= k <= E experts per token.
+ *   local_begin,     this GPU holds experts [local_begin, local_begin +
+ *   local_count      local_count), 1 <= local_count, local_begin >= 0,
+ *                    local_begin + local_count <= E.
+ *   capacity_factor  <= 0: no limit.  > 0: each local expert keeps at most
+ *                    C = floor(capacity_factor * T * k / E) pairs (the even
+ *                    share T*k/E scaled, glossary section "Load balancing and
+ *                    capacity"); the pairs with the largest router logit are
+ *                    kept, ties to the lower token index.
+ *   dtype            a moe_dtype value.
+ */
+typedef struct {
+  int64_t num_tokens;
+  int32_t hidden;
+  int32_t intermediate;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t local_begin;
+  int32_t local_count;
+  float capacity_factor;
+  int32_t dtype;
+} moe_layer_desc;
+
+/* Stages whose workspace size can be queried. */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_DISPATCH = 1,
+  MOE_STAGE_FFN = 2,
+  MOE_STAGE_COMBINE = 3,
+  MOE_STAGE_LAYER = 4 /* moe_layer_forward: all intermediates of the layer */
+} moe_stage;
+
+/* ------------------------------------------------------------------------ */
+/* Host helpers (no GPU work)                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/* Experts held by `rank` when ep_size ranks split E experts.  Transformers
+ * "Expert parallelism", section "How the sizes combine": ep_size splits the
+ * expert list into ep_size contiguous blocks and ep_size consecutive ranks
+ * hold one full set, so rank r holds block (r mod ep_size).
+ *   begin, count: host outputs.  INVALID_ARG unless E >= 1, ep_size >= 1,
+ *   ep_size divides E and rank >= 0. */
+moe_status moe_ep_local_range(int32_t num_experts, int32_t ep_size, int32_t rank,
+                              int32_t* begin, int32_t* count);
+
+/* Per-expert capacity C (see moe_layer_desc), or -1 when there is no limit.
+ * Returns -1 for an invalid descriptor too (moe_last_error says why). */
+int64_t moe_capacity(const moe_layer_desc* d);
+
+/* Rows that the permuted buffers (sorted_pairs, x_sorted, y_sorted) must
+ * hold: P_max = T*k without capacity, min(T*k, local_count*C) with it. */
+int64_t moe_max_pairs(const moe_layer_desc* d);
+
+/* Workspace bytes the given stage needs (0 is a valid answer). */
+moe_status moe_workspace_size(const moe_layer_desc* d, int32_t stage, size_t* bytes);
+
+/* Optional kernel timing, for benchmarks.  While set (events != NULL), every
+ * library call on this thread records events[2i] on its stream just before
+ * its i-th kernel launch and events[2i+1] just after it, for i < count/2.
+ * events are hipEvent_t handles created by the caller.  count == 0 or
+ * events == NULL switches timing off. */
+moe_status moe_profile_events(void* const* events, int32_t count);
+
+/* Name of the i-th kernel launched by the last library call on this thread,
+ * or NULL if there was none. */
+const char* moe_profile_kernel_name(int32_t i);
+
+/* Number of kernels launched by the last library call on this thread. */
+int32_t moe_profile_kernel_count(void);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 1: route.  Glossary, "How tokens move between GPUs", step 1: score  */
+/* every token against every expert with a linear router and keep the k     */
+/* best.  Ties go to the lower expert id; slot j holds the j-th best.  The  */
+/* routing weights are a softmax over the k chosen logits.  Ids are global  */
+/* (Transformers, "Expert parallelism": dispatch needs global expert ids).  */
+/* ------------------------------------------------------------------------ */
+/*   x           device [T, H] dtype      hidden states
+ *   w_router    device [E, H] dtype      router weight
+ *   b_router    device [E] float32 or NULL
+ *   logits_in   device [T, E] float32 or NULL: if given, x/w_router/b_router
+ *               are ignored and top-k runs on these logits
+ *   logits_out  device [T, E] float32 or NULL: the logits routed on
+ *   topk_ids    device [T, k] int32      global expert ids, best first
+ *   topk_w      device [T, k] float32    softmax over the k chosen logits
+ *   topk_logit  device [T, k] float32 or NULL: the chosen logits (needed by
+ *               moe_dispatch when capacity_factor > 0)
+ *   ws          device workspace of MOE_STAGE_ROUTE bytes (may be NULL if 0) */
+moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_router,
+                     const float* b_router, const float* logits_in, float* logits_out,
+                     int32_t* topk_ids, float* topk_w, float* topk_logit,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 2: dispatch.  Transformers, "Token dispatch": every (token, expert) */
+/* pair goes to the owner of its expert.  On one GPU this is a histogram of  */
+/* pairs per expert (the glossary snippet's bincount), an exclusive scan    */
+/* into per-expert segment offsets, an optional capacity cut, and a stable  */
+/* permutation that gathers the token rows into expert-sorted order.       */
+/* Pair p = t*k + j.  Within a segment pairs appear in ascending p.          */
+/* ------------------------------------------------------------------------ */
+/*   x             device [T, H] dtype
+ *   topk_ids      device [T, k] int32 (from moe_route)
+ *   topk_logit    device [T, k] float32; required iff capacity_factor > 0
+ *   counts        device [E] int32 out: pairs routed to each expert, all E,
+ *                 before any capacity cut
+ *   offsets       device [L+1] int32 out: local segment i is rows
+ *                 [offsets[i], offsets[i+1]); offsets[L] = P kept pairs
+ *   sorted_pairs  device [P_max] int32 out: pair id at each sorted row
+ *                 (rows >= P are left untouched)
+ *   pair_row      device [T*k] int32 out: sorted row of each pair, -1 if its
+ *                 expert is not local or the pair was dropped
+ *   x_sorted      device [P_max, H] dtype out: row q = x[sorted_pairs[q] / k]
+ *   num_dropped   device int64 out (may be NULL): pairs cut by capacity
+ *   ws            device workspace of MOE_STAGE_DISPATCH bytes */
+moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* topk_ids,
+                        const float* topk_logit, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_pairs, int32_t* pair_row, void* x_sorted,
+                        int64_t* num_dropped, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 3: local experts as one grouped GEMM.  Glossary, step 3: each GPU  */
+/* runs its local experts on the tokens it received; Transformers names the */
+/* expert kernel style "grouped_gemm".  Segment i of x_sorted goes through  */
+/* expert local_begin + i:  y = (silu(x Wg^T) * (x Wu^T)) Wd^T, with        */
+/* silu(z) = z / (1 + exp(-z)), float32 accumulation, the gate/up product   */
+/* rounded to dtype once.  Offsets are read on the device (no host sync).   */
+/* ------------------------------------------------------------------------ */
+/*   x_sorted  device [P_max, H] dtype
+ *   offsets   device [L+1] int32 (from moe_dispatch)
+ *   w_gate    device [L, I, H] dtype;  w_up [L, I, H];  w_down [L, H, I]
+ *   y_sorted  device [P_max, H] dtype out (rows >= P untouched)
+ *   ws        device workspace of MOE_STAGE_FFN bytes (holds [P_max, I]) */
+moe_status moe_grouped_ffn(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           void* y_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stage 4: combine.  Glossary, step 4: results return to their token and   */
+/* are weighted by the router scores and summed.  y[t] = sum over slots j   */
+/* in order 0..k-1 with pair_row[t*k+j] >= 0 of topk_w[t,j] *              */
+/* y_sorted[pair_row[t*k+j]], accumulated in float32 and rounded once; a    */
+/* token with no kept local pair gets 0.  The residual branch is not added. */
+/* ------------------------------------------------------------------------ */
+/*   y_sorted  device [P_max, H] dtype;  pair_row device [T*k] int32
+ *   topk_w    device [T, k] float32;    y device [T, H] dtype out */
+moe_status moe_combine(const moe_layer_desc* d, const void* y_sorted, const int32_t* pair_row,
+                       const float* topk_w, void* y, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* All four stages in one call.  The intermediates live in ws (size from    */
+/* MOE_STAGE_LAYER); the optional outputs (NULL to skip) receive copies:    */
+/*   topk_ids_out [T,k] int32, topk_w_out [T,k] float32, counts_out [E]      */
+/*   int32, num_dropped_out int64 -- all device pointers.                    */
+/* ------------------------------------------------------------------------ */
+moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void* w_router,
+                             const float* b_router, const void* w_gate, const void* w_up,
+                             const void* w_down, void* y, int32_t* topk_ids_out,
+                             float* topk_w_out, int32_t* counts_out, int64_t* num_dropped_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,133 @@
+"""GPU edge cases the pages name or the method implies: single tokens and
+uneven slices (Transformers "With tensor parallelism": slices may be uneven or
+empty, even in single-token decoding), experts that receive nothing, capacity
+overflow with tied scores (glossary "Load balancing and capacity"), shapes off
+the tile grid, and the decomposition identities over expert ranges and token
+slices."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._harness import layer_of, np_of, row_error, say, tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _run(s, logits=None):
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    lg_in = None if logits is None else torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
+    g = layer.staged(x, logits_in=lg_in)
+    torch.cuda.synchronize()
+    gpu = {k: (np_of(v) if isinstance(v, torch.Tensor) else v) for k, v in g.items()}
+    return inp, layer, x, gpu
+
+
+def _check(s, inp, gpu, logits=None):
+    ref = oracle.layer_forward(inp, logits=gpu["logits"] if logits is None else logits)
+    np.testing.assert_array_equal(gpu["topk_ids"], ref["topk_ids"])
+    np.testing.assert_array_equal(gpu["counts"], ref["counts"])
+    np.testing.assert_array_equal(gpu["offsets"], ref["offsets"])
+    P = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(gpu["sorted_pairs"][:P], ref["sorted_pairs"])
+    np.testing.assert_array_equal(gpu["pair_row"], ref["pair_row"])
+    assert int(gpu["num_dropped"][0]) == ref["num_dropped"]
+    err = row_error(gpu["y"], ref["y"], s.dtype)
+    assert err <= tol(s.dtype), err
+    return ref
+
+
+@pytest.mark.parametrize("over", [
+    dict(T=1), dict(T=2, k=1), dict(T=3, k=8, E=8, L=8), dict(T=5, E=1, k=1, L=1),
+    dict(T=130, H=72, I=40), dict(T=257, H=136, I=200, E=16, k=3, L=16),
+    dict(T=300, E=32, k=4, local_begin=31, L=1), dict(T=300, E=32, k=4, local_begin=5, L=11),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_shapes(over, dtype):
+    s = synth.spec("gptoss_ep8_share", H=64, I=96, E=8, k=2, local_begin=0, L=8, dtype=dtype,
+                   bias="linear_default").replace(**over)
+    say(f"[edge] {s}")
+    inp, layer, x, gpu = _run(s)
+    _check(s, inp, gpu)
+
+
+def test_all_tokens_to_one_expert_and_empty_experts():
+    s = synth.spec("gptoss_ep8_share", T=700, H=128, I=160, E=16, k=2, L=16)
+    lg = np.full((s.T, s.E), -5.0, dtype=np.float32)
+    lg[:, 3] = 2.0
+    lg[:, 7] = 1.0 + np.arange(s.T, dtype=np.float32) * 1e-3
+    inp, layer, x, gpu = _run(s, logits=lg)
+    ref = _check(s, inp, gpu, logits=lg)
+    assert ref["counts"][3] == s.T and ref["counts"][7] == s.T
+    assert (ref["counts"] == 0).sum() == 14
+
+
+def test_capacity_with_tied_scores():
+    # expert 0 is everyone's first choice with the same score: the lower tokens win
+    s = synth.spec("skewed_capacity", T=2000, H=64, I=64, E=8, k=2, L=8, capacity_factor=1.0)
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((s.T, s.E)).astype(np.float32)
+    lg[:, 0] = 7.0
+    lg[::3, 1] = 7.0       # ties across experts too: lower id first
+    inp, layer, x, gpu = _run(s, logits=lg)
+    ref = _check(s, inp, gpu, logits=lg)
+    C = oracle.capacity_limit(1.0, s.T, s.k, s.E)
+    kept0 = [p // s.k for p in ref["sorted_pairs"][ref["offsets"][0]:ref["offsets"][1]]]
+    assert kept0 == list(range(C))
+    assert ref["num_dropped"] > 0
+
+
+def test_capacity_drops_everything_for_some_tokens():
+    s = synth.spec("skewed_capacity", T=1024, H=64, I=64, E=8, k=1, L=8, capacity_factor=0.5)
+    lg = np.zeros((s.T, s.E), dtype=np.float32)
+    lg[:, 2] = np.linspace(0, 1, s.T, dtype=np.float32)[::-1] + 1
+    inp, layer, x, gpu = _run(s, logits=lg)
+    ref = _check(s, inp, gpu, logits=lg)
+    C = oracle.capacity_limit(0.5, s.T, 1, s.E)
+    assert ref["num_dropped"] == s.T - C
+    assert np.all(gpu["y"][C:] == 0)
+
+
+def test_expert_ranges_sum_to_all_local():
+    base = synth.spec("gptoss_ep8_share", T=512, H=128, I=96, E=16, k=4, L=16, dtype="f32", bias="none")
+    inp = synth.make_layer(base)
+    layer, x = layer_of(inp)
+    full = np_of(layer.forward(x))
+    for ep in (2, 4):
+        acc = np.zeros_like(full, dtype=np.float64)
+        for rank in range(ep):
+            b, n = oracle.ep_local_range(16, ep, rank)
+            part = dict(inp)
+            part["spec"] = base.replace(local_begin=b, L=n)
+            for w in ("w_gate", "w_up", "w_down"):
+                part[w] = inp[w][b:b + n]
+            pl, px = layer_of(part)
+            acc += np_of(pl.forward(px))
+        assert row_error(acc, full.astype(np.float64), "f32") <= 1e-5
+
+
+def test_token_slices_concatenate_bit_exact():
+    s = synth.spec("mixtral_like", T=900, H=256, I=384)
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    full = np_of(layer.forward(x))
+    parts = []
+    for a, b in [(0, 1), (1, 450), (450, 451), (451, 900)]:
+        sub = dict(inp)
+        sub["spec"] = s.replace(T=b - a)
+        sub["x"] = inp["x"][a:b]
+        pl, px = layer_of(sub)
+        parts.append(np_of(pl.forward(px)))
+    np.testing.assert_array_equal(np.concatenate(parts), full)
+
+
+def test_zero_tokens_leave_outputs_untouched():
+    s = synth.spec("mixtral_like", T=0, H=64, I=64)
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    y = torch.full((0, s.H), 1.0, dtype=torch.bfloat16, device="cuda")
+    layer.forward(x, y=y)
+    torch.cuda.synchronize()
