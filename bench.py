@@ -1,0 +1,265 @@
+"""Benchmark: one MoE layer forward (route -> dispatch -> grouped SwiGLU FFN ->
+combine) on one MI355X through the libmoe C ABI.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one moe_layer_forward over one batch of seeded synthetic input that
+is already resident in HBM.  W untimed steps, then exactly K timed steps
+between two device synchronisations.  Every kernel of every timed step is
+also bracketed by HIP events on the launch stream (the library records them),
+which gives each kernel's average duration; the roofline entry uses the
+dominant kernel.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer (1 GPU, bf16) + grouped-GEMM % MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime that torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        st = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int, nblk: int) -> tuple[float, float]:
+    """Algorithmic (bytes, flops) of one launch of a libmoe kernel."""
+    dt = 2 if s.dtype == "bf16" else 4
+    T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
+    cap = s.capacity_factor > 0
+    if name == "route_topk":
+        return (T * H + E * H) * dt + T * k * (12 if cap else 8), 2.0 * T * H * E
+    if name == "dispatch_count":
+        return T * k * 4 + nblk * E * 4, 0.0
+    if name == "dispatch_scan":
+        return nblk * E * 4 * 2, 0.0
+    if name == "dispatch_scatter":
+        return T * k * 4 * 2 + P * 4, 0.0
+    if name == "dispatch_capacity":
+        return T * k * 4 * 3, 0.0
+    if name == "dispatch_gather":
+        return (touched_tokens + P) * H * dt + P * 4, 0.0
+    if name == "ffn_gate_up":
+        return P * H * dt + 2 * touched_experts * I * H * dt + P * I * dt, 4.0 * P * H * I
+    if name == "ffn_down":
+        return P * I * dt + touched_experts * H * I * dt + P * H * dt, 2.0 * P * H * I
+    if name == "combine":
+        return P * H * dt + T * k * 8 + T * H * dt, 0.0
+    return 0.0, 0.0
+
+
+def source_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they still match the source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{workload}:{kernel}")
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "expert_token_dispatch_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or source_digest(src) != rec["source_sha"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(inp, tokens: int) -> dict:
+    """The oracle as it stands, on the first `tokens` tokens of the same layer."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    s = inp["spec"]
+    sub = dict(inp)
+    sub["spec"] = s.replace(T=tokens)
+    sub["x"] = np.ascontiguousarray(inp["x"][:tokens])
+    t0 = time.perf_counter()
+    oracle.layer_forward(sub)
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1), "kind": "oracle",
+            "sample": f"first {tokens} of {s.T} tokens of the same layer, all {s.L} experts' weights; "
+                      f"whole oracle path (float64) in {dt:.1f} s; host has {os.cpu_count()} CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_like")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU exchange is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import expert_token_dispatch_amd as etd
+    from expert_token_dispatch_amd.layer import MoELayer, to_device
+
+    s = synth.spec(args.workload, seed=args.seed)
+    log(f"[bench] generating {s}")
+    inp = synth.make_layer(s)
+    desc = etd.make_desc(s.T, s.H, s.I, s.E, s.k, s.local_begin, s.L, s.capacity_factor, s.dtype)
+    layer = MoELayer.from_host(desc, inp)
+    x = to_device(inp["x"], s.dtype)
+    y = torch.empty_like(x)
+    counts = torch.empty((s.E,), dtype=torch.int32, device="cuda")
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    dropped = torch.zeros((1,), dtype=torch.int64, device="cuda")
+
+    # one run to learn the routing (pairs kept, experts touched) for the work model
+    layer.forward(x, y=y, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
+    torch.cuda.synchronize()
+    names = [etd.moe_profile_kernel_name(i) for i in range(etd.moe_profile_kernel_count())]
+    ids_h = ids.cpu().numpy()
+    cnt_h = counts.cpu().numpy()
+    C = etd.moe_capacity(desc)
+    local = cnt_h[s.local_begin:s.local_begin + s.L]
+    kept = np.minimum(local, C) if C >= 0 else local
+    P = int(kept.sum())
+    touched_experts = int((kept > 0).sum())
+    is_local = (ids_h >= s.local_begin) & (ids_h < s.local_begin + s.L)
+    touched_tokens = int(np.any(is_local, axis=1).sum())  # upper bound when capacity cuts pairs
+    nblk = -(-s.T * s.k // 1024)
+    log(f"[bench] kernels {names}; P={P}, experts touched {touched_experts}, dropped {int(dropped.item())}")
+
+    for _ in range(args.warmup):
+        layer.forward(x, y=y)
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    nk = len(names)
+    evs = [hip.create(2 * nk) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        etd.moe_profile_events(evs[i])
+        layer.forward(x, y=y)
+    stop.record()
+    torch.cuda.synchronize()
+    etd.moe_profile_events(None)
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+
+    per_kernel = {}
+    for j, n in enumerate(names):
+        ts = [hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(args.steps)]
+        per_kernel.setdefault(n, []).append(sum(ts) / len(ts))
+    for e in evs:
+        hip.destroy(e)
+    kern = {}
+    for n, ts in per_kernel.items():
+        us = sum(ts) * 1e3  # a name launched twice in a step adds up
+        b, f = kernel_work(n, s, P, touched_tokens, touched_experts, nblk)
+        b, f = b * len(ts), f * len(ts)
+        gbs = b / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        tfl = f / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        kern[n] = {"us": round(us, 2), "GB/s": round(gbs, 1), "TFLOP/s": round(tfl, 2),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS[s.dtype], 4) if f else None}
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    b, f = kernel_work(dom, s, P, touched_tokens, touched_experts, nblk)
+    us = kern[dom]["us"]
+    gemm_bound_hbm = dom.startswith("ffn") and (f / (MFMA_PEAK_TFLOPS[s.dtype] * 1e12) < b / (HBM_PEAK_GBS * 1e9))
+    if f > 0 and not gemm_bound_hbm:
+        achieved = f / (us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS[s.dtype],
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[s.dtype], 4)}
+    else:
+        achieved = b / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    tb = traffic_for(dom, s.name)
+    roof["traffic"] = tb
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = f if roof["bound"] == "mfma" else b
+
+    gemm_us = sum(kern[n]["us"] for n in kern if n.startswith("ffn"))
+    gemm_frac = 6.0 * P * s.H * s.I / (gemm_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[s.dtype] if gemm_us else None
+    stage = lambda pre: round(sum(kern[n]["us"] for n in kern if n.startswith(pre)), 2)  # noqa: E731
+
+    out = {
+        "metric": METRIC,
+        "value": round(s.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded numpy draws; random-init router and experts)",
+        "config": {"workload": s.name, "tokens": s.T, "hidden": s.H, "intermediate": s.I, "experts": s.E,
+                   "top_k": s.k, "local_experts": [s.local_begin, s.local_begin + s.L],
+                   "capacity_factor": s.capacity_factor, "pairs_kept": P, "seed": s.seed},
+        "grouped_gemm_mfma_frac": round(gemm_frac, 4) if gemm_frac else None,
+        "stages_us": {"route": stage("route"), "dispatch": stage("dispatch"), "grouped_ffn": stage("ffn"),
+                      "combine": stage("combine")},
+        "kernels": kern,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, s.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

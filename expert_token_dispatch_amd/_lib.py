@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(lib_path):
             raise RuntimeError(f"{lib_path} is not built: run `python -m expert_token_dispatch_amd.build`")
+        # torch first: its HIP runtime then serves libmoe too (one runtime per process)
+        import torch  # noqa: F401
         L = ctypes.CDLL(lib_path)
         st = ctypes.c_int
         sig = {
