@@ -13,6 +13,9 @@ typedef uint16_t bf16_t;  // bfloat16 storage: the high half of an IEEE float32
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector: selects and copies of it stay in registers
+// (HIP's uint4 is a struct, which a conditional expression can push to scratch)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
