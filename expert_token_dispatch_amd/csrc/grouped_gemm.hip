@@ -204,27 +204,51 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
 // ---------------------------------------------------------------------------
 // Large-tile bf16 kernel for segments of hundreds of rows and more.
 //
-// 512 threads (8 waves, two per SIMD, so one wave's memory waits overlap the
-// other's MFMAs) own a 256-row x 256-column tile of B rows: for the gate/up
-// product that is 128 gate rows and the same 128 up rows (output 256 x 128),
-// for the down product 256 output columns.  Waves are arranged 2 (M) x 4 (N);
-// a wave holds 4 x 2 MFMA 32x32 accumulators (128 registers).  K advances 64
-// at a time through two LDS stages of 72 KB each (rows padded to 144 bytes so
-// 16-byte fragment reads of 16 lanes touch 64 distinct banks); the next
-// stage's global loads are in flight while the current one is multiplied.
+// One 256-thread block (four waves, one per SIMD) owns a tile of 256 rows by
+// 256 B rows: for the gate/up product that is 128 gate rows and the same 128
+// up rows (output 256 x 128), for the down product 256 output columns.  The
+// waves split it 2 (M) x 2 (N); each holds 4 x 4 MFMA 32x32 accumulators
+// (256 registers, kept in AGPRs), so every fragment read from LDS feeds four
+// MFMAs.
 //
-// Tile order: the blocks that run at the same time on one XCD (the hardware
-// deals workgroups to the 8 XCDs round robin) get consecutive tile numbers,
-// and tile numbers run over (expert, group of kGroupN n-tiles, m-tile, n-tile
-// in group), so one XCD's L2 serves a few weight tiles to all m-tiles of an
-// expert and a few activation tiles to several n-tiles.
+// K advances 64 at a time through two 64 KB LDS stages filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane i of a load writes bytes
+// [16i, 16i+16) of a 1 KB block, no staging registers).  Rows are 128 bytes;
+// 16-byte chunk c of row r sits at physical chunk c ^ ((r/2) % 8), so the
+// fragment reads of 16 lanes (16 rows, one chunk) cover all 64 banks.
+//
+// Schedule of one stage (per wave): for each 16-k chunk, the fragments of the
+// next chunk are read while this chunk's 16 MFMAs issue (pinned with
+// sched_group_barrier).  Before the last chunk the wave waits for its own
+// loads of the next stage and for its own reads of this stage, then a block
+// barrier makes both true for every wave: the next stage's first fragments
+// are read and this stage's slot is refilled (stage kt+2) while the last 16
+// MFMAs run.  The barrier is a bare s_barrier: __syncthreads() would also
+// drain every load in flight.
+//
+// Tile order: the blocks that run at once on one XCD (blocks are dealt to
+// the 8 XCDs round robin) get consecutive tile numbers, and tile numbers run
+// over (expert, group of kGroupN n-tiles, m-tile, n-tile in group), so one
+// XCD's L2 serves a few weight tiles to all m-tiles of an expert and a few
+// activation tiles to several n-tiles.
 namespace big {
 
-constexpr int BM = 256, BNE = 256, BK = 64, LD = BK + 8, kThreads = 512;
-constexpr int kStageA = BM * LD, kStageB = BNE * LD;  // elements
-constexpr size_t kLdsBytes = size_t(2) * (kStageA + kStageB) * sizeof(bf16_t);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2, kThreads = 256;
+constexpr int kRowBytes = BK * 2;              // 128
+constexpr int kStageA = BM * kRowBytes;        // 32 KB
+constexpr int kStage = kStageA + BNE * kRowBytes;
+constexpr size_t kLdsBytes = size_t(kStages) * kStage;  // 128 KB
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at their maxima)
+#define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define MOE_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+bool supported(int K) { return K % BK == 0; }
 
 template <int NMAT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
@@ -268,96 +292,142 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   const bf16_t* Bg = B0 + boff;
   const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
 
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
-  bf16_t* As = lds;                   // [2][BM][LD]
-  bf16_t* Bs = lds + 2 * kStageA;     // [2][BNE][LD]
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  // global -> register staging: 4 A chunks and 4 B chunks of 16 bytes per
-  // thread; chunk j of thread tid is row (tid + j*512) / 8, column (tid % 8)*8
-  constexpr int CPR = BK / 8;  // 16-byte chunks per row (8)
-  const int gcol = (tid % CPR) * 8;
-  const int grow = tid / CPR;  // + j * 64
-  const bf16_t* a_src = A + size_t(row0) * K + gcol;
-  uint32_t a_row[4];
-  uint32_t b_row[4];
-  const bf16_t* b_base[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = grow + j * (kThreads / CPR);
-    a_row[j] = uint32_t(min(r, rows - 1));
-    if (NMAT == 2) {
-      b_base[j] = r < BNE / 2 ? Bg : Bu;
-      b_row[j] = uint32_t(n0 + (r & (BNE / 2 - 1)));
-    } else {
-      b_base[j] = Bg;
-      b_row[j] = uint32_t(n0 + r);
-    }
+  // ---- direct loads: 32 blocks of 8 rows (1 KB) for A and for B per stage;
+  // wave w fills blocks 8w..8w+7 of each.  Lane i of block j writes row
+  // 64w + 8j + i/8, physical chunk i%8, which holds logical chunk
+  // (i%8) ^ ((row/2)%8); that depends on i and the parity of j only.
+  const int lrow = 64 * wave + (lane >> 3);
+  const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
+  const int c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+  const bf16_t* a_base = A + size_t(row0) * K;
+  const bf16_t* b_base;
+  int b_lrow;
+  if (NMAT == 2) {
+    b_base = (wave < 2 ? Bg : Bu) + size_t(n0) * K;  // waves 0-1 load gate rows, 2-3 up rows
+    b_lrow = lrow & (BNE / 2 - 1);
+  } else {
+    b_base = Bg + size_t(n0) * K;
+    b_lrow = lrow;
   }
-  u32x4_t ra[4], rb[4];
-#define MOE_BIG_GLOAD(k0)                                                                                   \
+  const int b_lim = N - 1 - n0;  // B rows past N repeat row N-1: those columns are never stored
+#define MOE_ISSUE(kt_)                                                                                      \
   do {                                                                                                      \
-    const bool kok_ = (k0) + gcol < K;                                                                      \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                         \
-      ra[j] = kok_ ? *reinterpret_cast<const u32x4_t*>(a_src + size_t(a_row[j]) * K + (k0)) : zero;          \
-      rb[j] = (kok_ && int(b_row[j]) < N)                                                                   \
-                  ? *reinterpret_cast<const u32x4_t*>(b_base[j] + size_t(b_row[j]) * K + gcol + (k0))          \
-                  : zero;                                                                                   \
-    }                                                                                                       \
-  } while (0)
-#define MOE_BIG_SSTORE(st)                                                                                  \
-  do {                                                                                                      \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                         \
-      const int r_ = grow + j * (kThreads / CPR);                                                           \
-      *reinterpret_cast<u32x4_t*>(As + (st) * kStageA + r_ * LD + gcol) = ra[j];                              \
-      *reinterpret_cast<u32x4_t*>(Bs + (st) * kStageB + r_ * LD + gcol) = rb[j];                              \
+    char* sa_ = lds + ((kt_) % kStages) * kStage + (8 * wave) * 1024;                                       \
+    const int k0_ = (kt_) * BK;                                                                             \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                         \
+      const int cc_ = (j & 1) ? c_odd : c_even;                                                             \
+      const int ar_ = min(lrow + 8 * j, rows - 1); /* rows past the segment repeat its last row */          \
+      const int br_ = min(b_lrow + 8 * j, b_lim);                                                           \
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(a_base + (uint32_t(ar_) * uint32_t(K) + cc_ * 8 + k0_)), \
+                                       (lds_ptr_t)(sa_ + j * 1024), 16, 0, 0);                             \
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(b_base + (uint32_t(br_) * uint32_t(K) + cc_ * 8 + k0_)), \
+                                       (lds_ptr_t)(sa_ + kStageA + j * 1024), 16, 0, 0);                   \
     }                                                                                                       \
   } while (0)
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // LDS rows this wave reads: A rows wm*128 + i*32 + (lane & 31); B rows below
-  const int frow = lane & 31, fk = 8 * (lane >> 5);
-  const int brow0 = NMAT == 2 ? wn * 32 : wn * 64;
-  const int brow1 = NMAT == 2 ? BNE / 2 + wn * 32 : wn * 64 + 32;
-
-  const int nk = (K + BK - 1) / BK;
-  MOE_BIG_GLOAD(0);
-  MOE_BIG_SSTORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) MOE_BIG_GLOAD((kt + 1) * BK);
-    const bf16_t* as = As + st * kStageA + (wm * 128 + frow) * LD + fk;
-    const bf16_t* bs = Bs + st * kStageB + frow * LD + fk;
+  // ---- fragment addresses: A rows wm*128 + i*32 + (lane & 31); B rows of the
+  // wave's four 32-column blocks (gate/up: two gate blocks, then the two up
+  // blocks of the same columns) --------------------------------------------
+  const int fr = lane & 31;
+  const int sw = (fr >> 1) & 7;
+  const int g = lane >> 5;
+  int boffs[4];
 #pragma unroll
-    for (int kc = 0; kc < BK / 16; ++kc) {
-      bf16x8_t af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * LD + kc * 16);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(bs + (j ? brow1 : brow0) * LD + kc * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) MOE_BIG_SSTORE(st ^ 1);
-    __syncthreads();
+  for (int j = 0; j < 4; ++j) {
+    const int br = NMAT == 2 ? (j < 2 ? wn * 64 + j * 32 : BNE / 2 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
+    boffs[j] = kStageA + (br + fr) * kRowBytes;
   }
-#undef MOE_BIG_GLOAD
-#undef MOE_BIG_SSTORE
+  const int a_off = (wm * 128 + fr) * kRowBytes;
+  bf16x8_t fa[2][4], fb[2][4];
+#define MOE_LOADF(buf_, st_, kc_)                                                                         \
+  do {                                                                                                    \
+    const int co_ = ((2 * (kc_) + g) ^ sw) * 16;                                                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
+      fa[buf_][i] = *reinterpret_cast<const bf16x8_t*>((st_) + a_off + i * 32 * kRowBytes + co_);          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
+      fb[buf_][j] = *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                            \
+  } while (0)
+#define MOE_MMA(buf_)                                                                                     \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                       \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf_][i], fb[buf_][j], acc[i][j], 0, 0, 0); \
+  } while (0)
+  // 8 x {1 MFMA, 1 LDS read}, then the other 8 MFMAs
+#define MOE_PIPE_DS()                                                                                     \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                    \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+    }                                                                                                     \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                                    \
+  } while (0)
+
+  const int nk = K / BK;
+  MOE_ISSUE(0);
+  if (nk > 1) {
+    MOE_ISSUE(1);
+    MOE_VMCNT(16);  // stage 0 landed (16 loads per stage per wave)
+  } else {
+    MOE_VMCNT(0);
+  }
+  __builtin_amdgcn_s_barrier();
+  MOE_LOADF(0, lds, 0);
+  // every iteration has a next stage; the refill issued in it is stage kt+2,
+  // or (near the end) a repeat of the last stage into the free slot
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const char* st = lds + (kt % kStages) * kStage;
+    MOE_LOADF(1, st, 1);
+    MOE_MMA(0);
+    MOE_LOADF(0, st, 2);
+    MOE_MMA(1);
+    MOE_LOADF(1, st, 3);
+    MOE_MMA(0);
+    MOE_PIPE_DS();
+    MOE_PIPE_DS();
+    MOE_PIPE_DS();
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_VMCNT(0);     // this wave's loads of stage kt+1 have landed
+    MOE_LGKMCNT0();   // and its reads of stage kt are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_LOADF(0, lds + ((kt + 1) % kStages) * kStage, 0);
+    MOE_ISSUE(min(kt + 2, nk - 1));
+    MOE_MMA(1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+  {
+    const char* st = lds + ((nk - 1) % kStages) * kStage;
+    MOE_LOADF(1, st, 1);
+    MOE_MMA(0);
+    MOE_LOADF(0, st, 2);
+    MOE_MMA(1);
+    MOE_LOADF(1, st, 3);
+    MOE_MMA(0);
+    MOE_MMA(1);
+  }
+  MOE_VMCNT(0);  // the last refill repeated a stage; let it land before the block ends
+#undef MOE_ISSUE
+#undef MOE_LOADF
+#undef MOE_MMA
+#undef MOE_PIPE_DS
 
   // ---- epilogue (32x32 layout: lane -> column lane & 31, register r -> row
   // 8*(r/4) + 4*(lane/32) + r%4) -----------------------------------------------
@@ -369,18 +439,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
       if (rt >= rows) continue;
       bf16_t* crow = C + size_t(row0 + rt) * N;
       if (NMAT == 2) {
-        const int col = n0 + wn * 32 + frow;
-        if (col < N) crow[col] = f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
-      } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + frow;
+          const int col = n0 + wn * 64 + j * 32 + fr;
+          if (col < N) crow[col] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + 2][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn * 128 + j * 32 + fr;
           if (col < N) crow[col] = f32_to_bf16(acc[i][j][r]);
         }
       }
     }
   }
 }
+#undef MOE_VMCNT
+#undef MOE_LGKMCNT0
 
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
@@ -419,7 +494,8 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
   // large tiles pay off once segments hold a few hundred rows; decode-sized
   // batches (a handful of rows per expert) keep the 128-row tiles
-  if (d->dtype == MOE_BF16 && a.max_pairs >= int64_t(128) * d->local_count) {
+  if (d->dtype == MOE_BF16 && a.max_pairs >= int64_t(128) * d->local_count && big::supported(d->hidden) &&
+      big::supported(d->intermediate)) {
     const int L = d->local_count, H = d->hidden, I = d->intermediate;
     const bf16_t* x = static_cast<const bf16_t*>(a.x_sorted);
     bf16_t* h = static_cast<bf16_t*>(a.h);
