@@ -136,7 +136,10 @@ def main():
     ap.add_argument("--workload", default="mixtral_like")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run one plain device copy of BYTES bytes (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -160,6 +163,16 @@ def main():
     counts = torch.empty((s.E,), dtype=torch.int32, device="cuda")
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     dropped = torch.zeros((1,), dtype=torch.int64, device="cuda")
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {n} bytes done")
 
     # one run to learn the routing (pairs kept, experts touched) for the work model
     layer.forward(x, y=y, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
