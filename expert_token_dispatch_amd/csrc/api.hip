@@ -98,6 +98,7 @@ struct LayerWs {
   int32_t* sorted_pairs;
   int32_t* pair_row;
   int64_t* num_dropped;
+  void* route;
   void* dispatch;
   void* x_sorted;
   void* h;
@@ -125,6 +126,7 @@ LayerWs layer_layout(const moe_layer_desc* d, void* base) {
   w.sorted_pairs = static_cast<int32_t*>(take(size_t(pm) * 4));
   w.pair_row = static_cast<int32_t*>(take(size_t(n) * 4));
   w.num_dropped = static_cast<int64_t*>(take(8));
+  w.route = take(route_scratch_bytes(d));
   w.dispatch = take(dispatch_scratch_bytes(d));
   w.x_sorted = take(size_t(pm) * d->hidden * dt);
   w.h = take(size_t(pm) * d->intermediate * dt);
@@ -136,6 +138,7 @@ LayerWs layer_layout(const moe_layer_desc* d, void* base) {
 size_t stage_bytes(const moe_layer_desc* d, int32_t stage) {
   switch (stage) {
     case MOE_STAGE_ROUTE:
+      return route_scratch_bytes(d);
     case MOE_STAGE_COMBINE:
       return 0;
     case MOE_STAGE_DISPATCH:
@@ -301,9 +304,9 @@ moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_route
   TRY(check_desc(d));
   if (d->num_tokens == 0) return MOE_OK;
   TRY(route_checks(d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit));
-  TRY(check_ws(d, MOE_STAGE_ROUTE, ws, ws_bytes));
+  if (logits_in == nullptr) TRY(check_ws(d, MOE_STAGE_ROUTE, ws, ws_bytes));
   RouteArgs a{d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit,
-              static_cast<hipStream_t>(stream)};
+              static_cast<float*>(ws), static_cast<hipStream_t>(stream)};
   return launch_route(a);
 }
 
@@ -362,7 +365,8 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
   TRY(combine_checks(w.y_sorted, w.pair_row, tw, y));
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
-  RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, ids, tw, cap ? w.topk_logit : nullptr, s};
+  RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, ids, tw, cap ? w.topk_logit : nullptr,
+               static_cast<float*>(w.route), s};
   TRY(launch_route(ra));
   DispatchArgs da{d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped,
                   carve_dispatch_scratch(d, w.dispatch), capacity_of(d), s};

@@ -67,6 +67,16 @@ __device__ __forceinline__ uint4 pack16(const float* f, float) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Block barrier without the memory drain of __syncthreads(): waves meet, but
+// loads in flight stay in flight (callers wait on their own counters first).
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Lanes below this one.
 __device__ __forceinline__ uint64_t lanemask_lt() {
   return (uint64_t(1) << lane_id()) - 1;

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   } else {
     MOE_VMCNT(0);
   }
-  __builtin_amdgcn_s_barrier();
+  block_barrier();
   MOE_LOADF(0, lds, 0);
   // every iteration has a next stage; the refill issued in it is stage kt+2,
   // or (near the end) a repeat of the last stage into the free slot
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     __builtin_amdgcn_sched_barrier(0);
     MOE_VMCNT(0);     // this wave's loads of stage kt+1 have landed
     MOE_LGKMCNT0();   // and its reads of stage kt are done
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
     __builtin_amdgcn_sched_barrier(0);
     MOE_LOADF(0, lds + ((kt + 1) % kStages) * kStage, 0);
     MOE_ISSUE(min(kt + 2, nk - 1));

@@ -46,8 +46,10 @@ struct RouteArgs {
   int32_t* topk_ids;
   float* topk_w;
   float* topk_logit;
+  float* partial;  // route scratch: per-slice partial logits
   hipStream_t s;
 };
+size_t route_scratch_bytes(const moe_layer_desc* d);
 moe_status launch_route(const RouteArgs& a);
 
 // Dispatch scratch, carved from the caller's workspace.

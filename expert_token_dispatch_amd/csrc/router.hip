@@ -7,199 +7,415 @@
 // the lower expert id, and the routing weights are a softmax over the k chosen
 // logits.
 //
-// One block handles 64 tokens with four waves.  Each wave computes a 16-token
-// by E-expert logit tile with MFMA (bf16: 16x16x32, f32: 16x16x4), streaming
-// its 16 rows of x straight from HBM into registers (every x element is used
-// by exactly one wave, so LDS staging would buy nothing) and reading the small
-// router matrix through the caches.  The logits go to LDS, and one thread per
-// token then keeps a sorted list of its k best with a strict compare while
-// walking the experts in ascending id order, which gives lowest-id ties.
+// Two kernels:
+//  route_logits  a skinny GEMM [T, H] x [H, E].  A block owns 64 tokens (four
+//                waves of 16), a group of up to 64 experts and one slice of H;
+//                the grid spans token tiles x expert groups x H slices so that
+//                even a decode batch keeps a few hundred blocks streaming.
+//                x rows and router-weight rows (128 bytes of k per stage) go
+//                through a 4-slot LDS ring filled by direct global->LDS loads
+//                three stages ahead, so the only waits are the explicit ones;
+//                the router-weight rows are shared by the four waves.  MFMA
+//                16x16x32 bf16 (f32: 8 x 16x16x4 per stage).  Each block
+//                writes its partial logits to partial[slice][t][e].
+//  route_topk    sums the slices in slice order (so the logits do not depend
+//                on scheduling) and adds the bias; then four lanes per token
+//                each keep a sorted list of the k best of a contiguous quarter
+//                of the experts (strict compares over ascending ids, so equal
+//                scores keep the lower id first), and one lane merges the four
+//                lists, taking the lower quarter on equal scores, and forms the
+//                softmax over the k chosen.
 #include <math.h>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
 namespace {
 
-constexpr int kRouteTokens = 64;   // tokens per block
-constexpr int kRouteThreads = 256;
+constexpr int kTok = 64;        // tokens per logits block (4 waves x 16)
+constexpr int kThreads = 256;
+constexpr int kMaxGroup = 64;   // experts per logits block
+constexpr int kRowBytes = 128;  // bytes of k per router-weight row and stage
+constexpr int kSlots = 4;       // LDS ring depth
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
+#define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 template <typename T> struct RouterMma;
 template <> struct RouterMma<bf16_t> {
-  static constexpr int kStep = 32;   // k consumed per MFMA step: 4 lane groups x 8
-  static constexpr int kLaneK = 8;   // k values one lane supplies per step
-  __device__ static void mma(const uint4& a, const uint4& b, f32x4_t& c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  static constexpr int kStepK = 64;  // k per 128-byte chunk
+  // two MFMA 16x16x32 per chunk; the lane supplies k = 32*s + 8*(lane/16) .. +7
+  __device__ static void mma(const u32x4_t* a, const u32x4_t* b, f32x4_t& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[0]), __builtin_bit_cast(bf16x8_t, b[0]),
+                                                c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[1]), __builtin_bit_cast(bf16x8_t, b[1]),
+                                                c, 0, 0, 0);
   }
+  // byte offset inside a 128-byte chunk of the lane's 16-byte piece s (s = 0, 1)
+  __device__ static int piece(int lane, int s) { return s * 64 + (lane >> 4) * 16; }
 };
 template <> struct RouterMma<float> {
-  static constexpr int kStep = 16;   // 4 lane groups x 4
-  static constexpr int kLaneK = 4;
-  __device__ static void mma(const uint4& a, const uint4& b, f32x4_t& c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  static constexpr int kStepK = 32;
+  // eight MFMA 16x16x4 per chunk; the lane supplies k = 16*s + 4*(lane/16) .. +3
+  __device__ static void mma(const u32x4_t* a, const u32x4_t* b, f32x4_t& c) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[s][v]), __uint_as_float(b[s][v]), c, 0, 0, 0);
   }
+  __device__ static int piece(int lane, int s) { return s * 64 + (lane >> 4) * 16; }
 };
 
-// NEB: 16-expert column blocks (E <= 16*NEB).  MAXK: register top-k list size (k <= MAXK).
-template <typename T, int NEB, int MAXK>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ br,
-    const float* __restrict__ logits_in, float* __restrict__ logits_out, int32_t* __restrict__ ids,
-    float* __restrict__ tw, float* __restrict__ tl, int ntok, int H, int E, int k) {
-  extern __shared__ float lg[];  // [kRouteTokens][E + 1]
-  const int ld = E + 1;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int tblk = blockIdx.x * kRouteTokens;
+// 16-byte chunk c of router-weight row r lives at physical chunk c ^ ((r/2) % 8)
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-  if (logits_in != nullptr) {
-    for (int idx = tid; idx < kRouteTokens * E; idx += kRouteThreads) {
-      const int m = idx / E, e = idx - m * E;
-      const int t = tblk + m;
-      lg[m * ld + e] = t < ntok ? logits_in[size_t(t) * E + e] : 0.0f;
+// partial[slice][t][e] = sum over the slice's k of x[t,k] * Wr[e,k]
+//
+// Stage layout in LDS: 64 x rows then G router-weight rows, 128 bytes each,
+// 16-byte chunk c of row r at physical chunk c ^ ((r/2) % 8).  Both operands
+// arrive by direct global->LDS loads; wave w loads its own 16 x rows (two
+// 1 KB loads) and router-weight loads w, w+4, ... of the G/8 per stage.
+template <typename T, int NEB>
+__global__ __launch_bounds__(kThreads) void logits_kernel(const T* __restrict__ x, const T* __restrict__ wr,
+                                                          float* __restrict__ partial, int ntok, int H, int E,
+                                                          int k_per_slice) {
+  using M = RouterMma<T>;
+  constexpr int G = NEB * 16;                       // expert rows per block (<= 64)
+  constexpr int kRows = kTok + G;
+  constexpr int kSlotBytes = kRows * kRowBytes;     // <= 16 KB
+  constexpr int EPC = 16 / int(sizeof(T));          // elements per 16-byte chunk
+  constexpr int kWrLoads = G / 8;
+  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kSlotBytes];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kTok;
+  const int e0 = blockIdx.y * G;
+  const int k_begin = blockIdx.z * k_per_slice;
+  const int k_end = min(H, k_begin + k_per_slice);
+  const int nstep = (k_end - k_begin + M::kStepK - 1) / M::kStepK;
+
+  // per-lane source rows and chunk of each direct load (chunks past H re-read
+  // the row start: the matching x values are zeroed after the LDS read)
+  const int lr = lane >> 3;                         // row within a 1 KB load
+  const T* xsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * wave + 8 * j + lr;           // x row within the tile
+    xsrc[j] = x + size_t(min(t0 + r, ntok - 1)) * H + swz(r, lane & 7) * EPC;  // rows past T repeat the last token
+  }
+  // direct loads this wave issues per stage: 2 for x, 0-2 for the router weight
+  const int my_wr = wave < kWrLoads ? (kWrLoads - 1 - wave) / 4 + 1 : 0;
+  auto issue = [&](int s) {
+    char* slot = ring + (s % kSlots) * kSlotBytes;
+    const int kb = k_begin + s * M::kStepK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kk = kb + swz(16 * wave + 8 * j + lr, lane & 7) * EPC;
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(xsrc[j] - swz(16 * wave + 8 * j + lr, lane & 7) * EPC +
+                                                   (kk < H ? kk : 0)),
+                                       (lds_ptr_t)(slot + (2 * wave + j) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < 2; ++j0) {
+      const int j = wave + 4 * j0;
+      if (j < kWrLoads) {
+        const int r = 8 * j + lr;                   // router-weight row within the group
+        const int kk = kb + swz(kTok + r, lane & 7) * EPC;
+        const int e = min(e0 + r, E - 1);           // rows past E repeat expert E-1 (never stored)
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(wr + size_t(e) * H + (kk < H ? kk : 0)),
+                                         (lds_ptr_t)(slot + kTok * kRowBytes + j * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x4_t acc[NEB];
+#pragma unroll
+  for (int i = 0; i < NEB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int arow = 16 * wave + (lane & 15);
+  for (int s = 0; s < kSlots - 1 && s < nstep; ++s) issue(s);
+  for (int s = 0; s < nstep; ++s) {
+    // this wave's loads of stage s have landed once only the later stages'
+    // loads (stages s+1 and s+2, 2 + my_wr each) may still be in flight
+    const int later = (2 + my_wr) * min(2, nstep - 1 - s);
+    switch (later) {
+      case 8: MOE_VMCNT(8); break;
+      case 7: MOE_VMCNT(7); break;
+      case 6: MOE_VMCNT(6); break;
+      case 5: MOE_VMCNT(5); break;
+      case 4: MOE_VMCNT(4); break;
+      case 3: MOE_VMCNT(3); break;
+      case 2: MOE_VMCNT(2); break;
+      default: MOE_VMCNT(0); break;
+    }
+    // all waves' parts of stage s are in LDS; all waves are done with stage s-1
+    block_barrier();
+    if (s + kSlots - 1 < nstep) issue(s + kSlots - 1);
+    const char* slot = ring + (s % kSlots) * kSlotBytes;
+    const int kb = k_begin + s * M::kStepK;
+    u32x4_t a[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = M::piece(lane, p) >> 4;
+      a[p] = *reinterpret_cast<const u32x4_t*>(slot + arow * kRowBytes + swz(arow, c) * 16);
+      if (kb + M::kStepK > k_end && kb + c * EPC >= k_end) a[p] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int nb = 0; nb < NEB; ++nb) {
+      const int r = kTok + nb * 16 + (lane & 15);
+      u32x4_t b[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c = M::piece(lane, p) >> 4;
+        b[p] = *reinterpret_cast<const u32x4_t*>(slot + r * kRowBytes + swz(r, c) * 16);
+      }
+      M::mma(a, b, acc[nb]);
+    }
+  }
+  MOE_VMCNT(0);
+
+  // acc[nb][i] = partial logit of (token t0 + 16*wave + 4*(lane/16) + i, expert e0 + 16*nb + (lane & 15))
+  float* out = partial + size_t(blockIdx.z) * ntok * E;
+#pragma unroll
+  for (int nb = 0; nb < NEB; ++nb) {
+    const int e = e0 + nb * 16 + (lane & 15);
+    if (e < E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * wave + 4 * (lane >> 4) + i;
+        if (t < ntok) out[size_t(t) * E + e] = acc[nb][i];
+      }
+    }
+  }
+}
+
+constexpr int kTopkTok = 64;      // tokens per top-k block
+constexpr int kTopkThreads = 256; // four lanes per token
+
+// Sorted insertion into a descending list; a strict compare keeps the entry
+// seen first (the lower expert id, as experts are walked in ascending order)
+// ahead of an equal score.
+template <int MAXK>
+__device__ __forceinline__ void topk_insert(float (&v)[MAXK], int (&id)[MAXK], float xv, int e) {
+#pragma unroll
+  for (int j = MAXK - 1; j >= 0; --j) {
+    const bool shift = (j > 0) && (v[j > 0 ? j - 1 : 0] < xv);
+    if (shift) {
+      v[j] = v[j - 1];
+      id[j] = id[j - 1];
+    } else if (v[j] < xv) {
+      v[j] = xv;
+      id[j] = e;
+    }
+  }
+}
+
+template <int MAXK>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ partial, int nslice,
+                                                            const float* __restrict__ br, float* __restrict__ logits_out,
+                                                            int32_t* __restrict__ ids, float* __restrict__ tw,
+                                                            float* __restrict__ tl, int ntok, int E, int k) {
+  extern __shared__ float sh[];
+  const int ld = E + 1;
+  float* lg = sh;                                          // [64][E + 1]
+  float* mv = sh + kTopkTok * ld;                          // [64][4][MAXK] merge values
+  int* mi = reinterpret_cast<int*>(mv + kTopkTok * 4 * MAXK);  // [64][4][MAXK] merge ids
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kTopkTok;
+  const int rows = min(kTopkTok, ntok - t0);
+  const int n = rows * E;  // the tile's logits are contiguous in every slice
+  const size_t slice_stride = size_t(ntok) * E;
+  const float* base = partial + size_t(t0) * E;
+
+  // ---- sum the slices in order, add the bias, keep the tile in LDS
+  if ((E & 3) == 0) {
+    const int n4 = n >> 2;
+#pragma unroll 4
+    for (int i = tid; i < n4; i += kTopkThreads) {
+      f32x4_t v = reinterpret_cast<const f32x4_t*>(base)[i];
+      for (int sl = 1; sl < nslice; ++sl) v += reinterpret_cast<const f32x4_t*>(base + sl * slice_stride)[i];
+      const int m = (4 * i) / E, e = 4 * i - m * E;
+      if (br != nullptr) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] += br[e + c];
+      }
+      if (logits_out != nullptr) reinterpret_cast<f32x4_t*>(logits_out + size_t(t0) * E)[i] = v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lg[m * ld + e + c] = v[c];
     }
   } else {
-    using M = RouterMma<T>;
-    const int row = lane & 15;     // A row (token) / B column (expert) this lane feeds
-    const int kg = lane >> 4;      // lane group: which k slice of the step
-    const int t = tblk + wave * 16 + row;
-    const bool tok_ok = t < ntok;
-    const T* xrow = x + size_t(tok_ok ? t : 0) * H;
-    f32x4_t acc[NEB];
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb) acc[eb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int k0 = 0; k0 < H; k0 += M::kStep) {
-      const int kk = k0 + kg * M::kLaneK;
-      const bool k_ok = kk < H;
-      const uint4 a = (tok_ok && k_ok) ? *reinterpret_cast<const uint4*>(xrow + kk) : zero;
-#pragma unroll
-      for (int eb = 0; eb < NEB; ++eb) {
-        const int e = eb * 16 + row;
-        const uint4 b = (e < E && k_ok) ? *reinterpret_cast<const uint4*>(wr + size_t(e) * H + kk) : zero;
-        M::mma(a, b, acc[eb]);
-      }
-    }
-    // acc[eb][r] = logit(token wave*16 + 4*kg + r, expert eb*16 + row)
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb) {
-      const int e = eb * 16 + row;
-      if (e < E) {
-        const float bias = br != nullptr ? br[e] : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lg[(wave * 16 + 4 * kg + r) * ld + e] = acc[eb][r] + bias;
-      }
+    for (int i = tid; i < n; i += kTopkThreads) {
+      float v = base[i];
+      for (int sl = 1; sl < nslice; ++sl) v += base[sl * slice_stride + i];
+      const int m = i / E, e = i - m * E;
+      if (br != nullptr) v += br[e];
+      if (logits_out != nullptr) logits_out[size_t(t0) * E + i] = v;
+      lg[m * ld + e] = v;
     }
   }
   __syncthreads();
 
-  if (logits_out != nullptr) {
-    for (int idx = tid; idx < kRouteTokens * E; idx += kRouteThreads) {
-      const int m = idx / E, e = idx - m * E;
-      const int t = tblk + m;
-      if (t < ntok) logits_out[size_t(t) * E + e] = lg[m * ld + e];
-    }
+  // ---- four lanes per token, each over a contiguous quarter of the experts
+  const int m = tid >> 2, q = tid & 3;
+  const int chunk = (E + 3) >> 2;
+  const int e_lo = q * chunk, e_hi = min(E, e_lo + chunk);
+  float v[MAXK];
+  int id[MAXK];
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    v[j] = -INFINITY;
+    id[j] = -1;
   }
+  if (m < rows) {
+    const float* my = lg + m * ld;
+    for (int e = e_lo; e < e_hi; ++e) topk_insert<MAXK>(v, id, my[e], e);
+  }
+#pragma unroll
+  for (int j = 0; j < MAXK; ++j) {
+    mv[(m * 4 + q) * MAXK + j] = v[j];
+    mi[(m * 4 + q) * MAXK + j] = id[j];
+  }
+  __syncthreads();
 
-  if (tid < kRouteTokens) {
-    const int t = tblk + tid;
-    if (t < ntok) {
-      float v[MAXK];
-      int id[MAXK];
+  // ---- merge the four sorted lists; on equal scores the lower quarter (lower ids) goes first
+  if (q != 0 || m >= rows) return;
+  const int t = t0 + m;
+  int head[4] = {0, 0, 0, 0};
+  float sel_v[MAXK];
+  int sel_i[MAXK];
 #pragma unroll
-      for (int j = 0; j < MAXK; ++j) {
-        v[j] = -INFINITY;
-        id[j] = 0;
-      }
-      const float* my = lg + tid * ld;
-      for (int e = 0; e < E; ++e) {
-        const float xv = my[e];
-        // insert into the descending list; a strict compare keeps earlier (lower) ids ahead of equal scores
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      int best = -1;
+      float bv = -INFINITY;
 #pragma unroll
-        for (int j = MAXK - 1; j >= 0; --j) {
-          const bool shift = (j > 0) && (v[j > 0 ? j - 1 : 0] < xv);
-          if (shift) {
-            v[j] = v[j - 1];
-            id[j] = id[j - 1];
-          } else if (v[j] < xv) {
-            v[j] = xv;
-            id[j] = e;
+      for (int qq = 0; qq < 4; ++qq) {
+        if (head[qq] < MAXK) {
+          const int off = (m * 4 + qq) * MAXK + head[qq];
+          if (mi[off] >= 0 && (best < 0 || mv[off] > bv)) {
+            best = qq;
+            bv = mv[off];
           }
         }
       }
-      const float top = v[0];
-      float ex[MAXK];
-      float sum = 0.0f;
+      const int off = (m * 4 + best) * MAXK + head[best];
+      sel_v[j] = bv;
+      sel_i[j] = mi[off];
+      head[best] += 1;
+    }
+  }
+  const float top = sel_v[0];
+  float ex[MAXK];
+  float sum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < MAXK; ++j) {
-        if (j < k) {
-          ex[j] = expf(v[j] - top);
-          sum += ex[j];
-        }
-      }
-      const float inv = 1.0f / sum;
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      ex[j] = expf(sel_v[j] - top);
+      sum += ex[j];
+    }
+  }
+  const float inv = 1.0f / sum;
 #pragma unroll
-      for (int j = 0; j < MAXK; ++j) {
-        if (j < k) {
-          const size_t o = size_t(t) * k + j;
-          ids[o] = id[j];
-          tw[o] = ex[j] * inv;
-          if (tl != nullptr) tl[o] = v[j];
-        }
-      }
+  for (int j = 0; j < MAXK; ++j) {
+    if (j < k) {
+      const size_t o = size_t(t) * k + j;
+      ids[o] = sel_i[j];
+      tw[o] = ex[j] * inv;
+      if (tl != nullptr) tl[o] = sel_v[j];
     }
   }
 }
 
-template <typename T, int NEB, int MAXK>
-moe_status launch_route_t(const RouteArgs& a) {
-  const moe_layer_desc* d = a.d;
-  const int ntok = int(d->num_tokens);
-  const int E = d->num_experts;
-  const size_t lds = size_t(kRouteTokens) * (E + 1) * sizeof(float);
-  auto kern = route_kernel<T, NEB, MAXK>;
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "route: LDS attribute: %s", hipGetErrorString(e));
-  }
-  const dim3 grid((ntok + kRouteTokens - 1) / kRouteTokens);
-  MOE_LAUNCH("route_topk", kern, grid, dim3(kRouteThreads), lds, a.s, static_cast<const T*>(a.x),
-             static_cast<const T*>(a.w_router), a.b_router, a.logits_in, a.logits_out, a.topk_ids, a.topk_w,
-             a.topk_logit, ntok, d->hidden, E, d->top_k);
-  return MOE_OK;
+// Work split of the logits kernel: token tiles x expert groups x H slices.
+struct Split {
+  int groups, neb, slices, k_per_slice;
+};
+
+template <typename T>
+Split plan(const moe_layer_desc* d) {
+  Split s;
+  const int E = d->num_experts, H = d->hidden;
+  const int e16 = (E + 15) / 16 * 16;
+  const int g = e16 < kMaxGroup ? e16 : kMaxGroup;
+  s.neb = g / 16;
+  s.groups = (E + g - 1) / g;
+  const int64_t tiles = (d->num_tokens + kTok - 1) / kTok;
+  const int step = RouterMma<T>::kStepK;
+  const int nsteps = (H + step - 1) / step;
+  // enough blocks to keep every CU streaming, but each slice at least 4 chunks deep
+  int slices = 1;
+  while (tiles * s.groups * slices < 512 && nsteps / (slices * 2) >= 4) slices *= 2;
+  s.slices = slices;
+  s.k_per_slice = (nsteps + slices - 1) / slices * step;
+  return s;
 }
 
 template <typename T, int NEB>
-moe_status pick_k(const RouteArgs& a) {
+moe_status launch_logits(const RouteArgs& a, const Split& sp, float* partial) {
+  const moe_layer_desc* d = a.d;
+  const int ntok = int(d->num_tokens);
+  const dim3 grid(unsigned((ntok + kTok - 1) / kTok), unsigned(sp.groups), unsigned(sp.slices));
+  MOE_LAUNCH("route_logits", (logits_kernel<T, NEB>), grid, dim3(kThreads), 0, a.s, static_cast<const T*>(a.x),
+             static_cast<const T*>(a.w_router), partial, ntok, d->hidden, d->num_experts, sp.k_per_slice);
+  return MOE_OK;
+}
+
+template <int MAXK>
+moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
+  const moe_layer_desc* d = a.d;
+  const int ntok = int(d->num_tokens);
+  const int E = d->num_experts;
+  const size_t lds = (size_t(kTopkTok) * (E + 1) + size_t(kTopkTok) * 4 * MAXK * 2) * sizeof(float);
+  auto kern = topk_kernel<MAXK>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return set_error(MOE_ERR_HIP, "route_topk: LDS attribute: %s", hipGetErrorString(e));
+  }
+  const dim3 grid(unsigned((ntok + kTopkTok - 1) / kTopkTok));
+  MOE_LAUNCH("route_topk", kern, grid, dim3(kTopkThreads), lds, a.s, partial, nslice, bias, a.logits_out,
+             a.topk_ids, a.topk_w, a.topk_logit, ntok, E, d->top_k);
+  return MOE_OK;
+}
+
+moe_status pick_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
   const int k = a.d->top_k;
-  if (k <= 2) return launch_route_t<T, NEB, 2>(a);
-  if (k <= 4) return launch_route_t<T, NEB, 4>(a);
-  if (k <= 8) return launch_route_t<T, NEB, 8>(a);
-  if (k <= 16) return launch_route_t<T, NEB, 16>(a);
-  return launch_route_t<T, NEB, 32>(a);
+  if (k <= 2) return launch_topk<2>(a, partial, nslice, bias);
+  if (k <= 4) return launch_topk<4>(a, partial, nslice, bias);
+  if (k <= 8) return launch_topk<8>(a, partial, nslice, bias);
+  if (k <= 16) return launch_topk<16>(a, partial, nslice, bias);
+  return launch_topk<32>(a, partial, nslice, bias);
 }
 
 template <typename T>
-moe_status pick_e(const RouteArgs& a) {
-  const int E = a.d->num_experts;
-  if (E <= 16) return pick_k<T, 1>(a);
-  if (E <= 32) return pick_k<T, 2>(a);
-  if (E <= 64) return pick_k<T, 4>(a);
-  if (E <= 128) return pick_k<T, 8>(a);
-  return pick_k<T, 16>(a);
+moe_status route_t(const RouteArgs& a) {
+  const Split sp = plan<T>(a.d);
+  moe_status st;
+  switch (sp.neb) {
+    case 1: st = launch_logits<T, 1>(a, sp, a.partial); break;
+    case 2: st = launch_logits<T, 2>(a, sp, a.partial); break;
+    case 3: st = launch_logits<T, 3>(a, sp, a.partial); break;
+    default: st = launch_logits<T, 4>(a, sp, a.partial); break;
+  }
+  if (st != MOE_OK) return st;
+  return pick_topk(a, a.partial, sp.slices, a.b_router);
 }
 
 }  // namespace
 
+size_t route_scratch_bytes(const moe_layer_desc* d) {
+  const Split sp = d->dtype == MOE_BF16 ? plan<bf16_t>(d) : plan<float>(d);
+  return align_up(size_t(sp.slices) * size_t(d->num_tokens) * d->num_experts * sizeof(float), 256);
+}
+
 moe_status launch_route(const RouteArgs& a) {
-  return a.d->dtype == MOE_BF16 ? pick_e<bf16_t>(a) : pick_e<float>(a);
+  if (a.logits_in != nullptr) return pick_topk(a, a.logits_in, 1, nullptr);
+  return a.d->dtype == MOE_BF16 ? route_t<bf16_t>(a) : route_t<float>(a);
 }
 
 }  // namespace moe

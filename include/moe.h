@@ -157,7 +157,8 @@ int32_t moe_profile_kernel_count(void);
  *   topk_w      device [T, k] float32    softmax over the k chosen logits
  *   topk_logit  device [T, k] float32 or NULL: the chosen logits (needed by
  *               moe_dispatch when capacity_factor > 0)
- *   ws          device workspace of MOE_STAGE_ROUTE bytes (may be NULL if 0) */
+ *   ws          device workspace of MOE_STAGE_ROUTE bytes (partial logits of
+ *               the H slices); not used, and may be NULL, when logits_in is given */
 moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_router,
                      const float* b_router, const float* logits_in, float* logits_out,
                      int32_t* topk_ids, float* topk_w, float* topk_logit,

@@ -66,7 +66,7 @@ def test_workspace_sizes_cover_buffers():
     assert ffn >= 16384 * 14336 * 2
     layer = etd.moe_workspace_size(d, L.MOE_STAGE_LAYER)
     assert layer >= ffn + 2 * 16384 * 4096 * 2
-    assert etd.moe_workspace_size(d, L.MOE_STAGE_ROUTE) == 0
+    assert etd.moe_workspace_size(d, L.MOE_STAGE_ROUTE) >= 8192 * 8 * 4   # per-slice partial logits
     assert etd.moe_workspace_size(d, L.MOE_STAGE_DISPATCH) > 0
 
 
