@@ -68,8 +68,10 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
     dt = 2 if s.dtype == "bf16" else 4
     T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
     cap = s.capacity_factor > 0
+    if name == "route_logits":
+        return (T * H + E * H) * dt + T * E * 4, 2.0 * T * H * E
     if name == "route_topk":
-        return (T * H + E * H) * dt + T * k * (12 if cap else 8), 2.0 * T * H * E
+        return T * E * 4 * 2 + T * k * (12 if cap else 8), 0.0
     if name == "dispatch_count":
         return T * k * 4 + nblk * E * 4, 0.0
     if name == "dispatch_scan":

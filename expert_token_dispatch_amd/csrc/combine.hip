@@ -11,7 +11,8 @@
 // One wave per token: the wave reads the token's k rows of y_sorted through
 // pair_row (the inverse permutation), so the un-permute, the weighting and the
 // sum are one pass with no atomics; each lane keeps a 16-byte slice of the
-// row in float32 and adds the slots in order j = 0..k-1, then rounds once.
+// row in float32, loads the slices of up to eight slots at once and adds them
+// in slot order j = 0..k-1, then rounds once.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,24 +26,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const float* __restrict__ tw, int64_t ntok, int k, int vec_per_row,
                                                       uint4* __restrict__ y) {
   constexpr int EPV = 16 / int(sizeof(T));
+  constexpr int kBatch = 8;  // slots whose rows are in flight together
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
-  const int32_t* rows = pair_row + t * k;
-  const float* w = tw + t * k;
+  // lane j < k holds slot j's sorted row and weight; broadcast per slot below
+  const int my_row = lane < k ? pair_row[t * k + lane] : -1;
+  const float my_w = lane < k ? tw[t * k + lane] : 0.0f;
   uint4* dst = y + size_t(t) * vec_per_row;
   for (int c = lane; c < vec_per_row; c += 64) {
     float acc[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r >= 0) {
-        const float wj = w[j];
-        float f[EPV];
-        unpack16(ys[size_t(r) * vec_per_row + c], T(), f);
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      uint4 v[kBatch];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wj, f[e], acc[e]);
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const int r = __shfl(my_row, j0 + jj, 64);
+        if (j0 + jj < k && r >= 0) v[jj] = ys[size_t(r) * vec_per_row + c];
+      }
+      // accumulate in slot order
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const int r = __shfl(my_row, j0 + jj, 64);
+        const float wj = __shfl(my_w, j0 + jj, 64);
+        if (j0 + jj < k && r >= 0) {
+          float f[EPV];
+          unpack16(v[jj], T(), f);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wj, f[e], acc[e]);
+        }
       }
     }
     dst[c] = pack16(acc, T());

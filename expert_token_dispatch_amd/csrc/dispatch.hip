@@ -23,8 +23,8 @@
 //   capacity  (only with a limit) one block per local expert: radix select
 //             of the C-th largest key (logit desc, then token asc) and a
 //             stable compaction of the kept pairs;
-//   gather    row copies x[t] -> x_sorted[row], one wave per row, 16-byte
-//             vectors.
+//   gather    token-major row copies: one wave reads x[t] once and writes it
+//             to the sorted row of each kept local pair, 16-byte vectors.
 #include "common.h"
 #include "kernels.h"
 
@@ -326,19 +326,40 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
 }
 
 // ---- gather -----------------------------------------------------------------
-constexpr int kGatherRowsPerBlock = 4;  // one wave per row
+// Token-major: one wave per token reads the token's row once and writes it to
+// the sorted row of each of its kept local pairs (pair_row), so x is read once
+// however many experts a token picked.
+constexpr int kGatherTokensPerBlock = 4;
 
-__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ sorted_pairs,
-                                                     const int32_t* __restrict__ offsets, int L, int k, int vec_per_row,
-                                                     uint4* __restrict__ xs) {
-  const int P = offsets[L];
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ pair_row,
+                                                     int64_t ntok, int k, int vec_per_row, uint4* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
-  const int64_t q = int64_t(blockIdx.x) * kGatherRowsPerBlock + (threadIdx.x >> 6);
-  if (q >= P) return;
-  const int t = sorted_pairs[q] / k;
+  const int64_t t = int64_t(blockIdx.x) * kGatherTokensPerBlock + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int my_row = lane < k ? pair_row[t * k + lane] : -1;
+  // destinations as a bit mask over slots (k <= 32)
+  const uint64_t kept = __ballot(my_row >= 0);
+  if (kept == 0) return;
   const uint4* src = x + size_t(t) * vec_per_row;
-  uint4* dst = xs + size_t(q) * vec_per_row;
-  for (int c = lane; c < vec_per_row; c += 64) dst[c] = src[c];
+  constexpr int kUnroll = 4;
+  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kUnroll) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < vec_per_row) v[u] = src[c];
+    }
+    for (uint64_t m = kept; m != 0; m &= m - 1) {
+      const int j = __ffsll((unsigned long long)m) - 1;
+      const int r = __shfl(my_row, j, 64);
+      uint4* dst = xs + size_t(r) * vec_per_row;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < vec_per_row) dst[c] = v[u];
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -365,12 +386,11 @@ moe_status launch_dispatch(const DispatchArgs& a) {
     MOE_LAUNCH("dispatch_scatter", scatter_kernel<false>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids,
                n, begin, L, chunk, a.scr.blk_base, a.sorted_pairs, a.pair_row);
   }
-  const int64_t max_rows = cap ? (n < int64_t(L) * a.capacity ? n : int64_t(L) * a.capacity) : n;
-  if (max_rows > 0) {
+  {
     const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
-    const dim3 grid(unsigned((max_rows + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock));
-    MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.x), a.sorted_pairs,
-               a.offsets, L, d->top_k, vec_per_row, static_cast<uint4*>(a.x_sorted));
+    const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
+    MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.x), a.pair_row,
+               d->num_tokens, d->top_k, vec_per_row, static_cast<uint4*>(a.x_sorted));
   }
   return MOE_OK;
 }

@@ -473,6 +473,114 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
 
 }  // namespace big
 
+// ---------------------------------------------------------------------------
+// Skinny kernel for segments of a few rows (decode-sized batches).
+//
+// With a handful of rows per expert the product is bound by streaming the
+// expert weights from HBM, so the work is split over weight rows: one block
+// of four waves owns one expert and 64 consecutive output columns (each wave
+// 16 weight rows, or 16 gate + 16 up rows).  A wave multiplies up to 64 of the
+// expert's token rows at a time (four MFMA 16x16x32 row blocks) and streams
+// its weight rows straight from HBM into registers, eight k-steps of 32 in
+// flight per matrix (16-byte loads; two consecutive steps cover a 128-byte
+// line of each weight row).  The token rows come through the caches.  An
+// expert that received no rows returns before touching its weights.
+namespace skinny {
+
+constexpr int kThreads = 256, kColsPerBlock = 64, kUnroll = 8, kMaxRowBlocks = 4;
+
+bool supported(int K) { return K % 32 == 0; }
+
+template <int NMAT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+                                                        bf16_t* __restrict__ C, int N, int K) {
+  const int expert = blockIdx.y;
+  const int seg0 = offsets[expert];
+  const int seg_n = offsets[expert + 1] - seg0;
+  if (seg_n <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col0 = blockIdx.x * kColsPerBlock + wave * 16;  // first weight row of this wave
+  if (col0 >= N) return;
+  const size_t boff = size_t(expert) * N * K;
+  const int wrow = min(col0 + (lane & 15), N - 1);            // rows past N repeat row N-1; never stored
+  const int kg = (lane >> 4) * 8;                             // the lane's 8 k values within a step
+  const bf16_t* bg = B0 + boff + size_t(wrow) * K + kg;
+  const bf16_t* bu = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow) * K + kg;
+
+  for (int m0 = 0; m0 < seg_n; m0 += 16 * kMaxRowBlocks) {
+    const int nrb = min(kMaxRowBlocks, (seg_n - m0 + 15) / 16);
+    // token row of each row block for this lane (rows past the segment repeat its last row)
+    const bf16_t* arow[kMaxRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRowBlocks; ++rb)
+      arow[rb] = A + size_t(seg0 + min(m0 + rb * 16 + (lane & 15), seg_n - 1)) * K + kg;
+    f32x4_t acc[NMAT][kMaxRowBlocks];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int rb = 0; rb < kMaxRowBlocks; ++rb) acc[m][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    int k0 = 0;
+    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
+      bf16x8_t wg[kUnroll], wu[kUnroll], a0[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        wg[u] = *reinterpret_cast<const bf16x8_t*>(bg + k0 + 32 * u);
+        if (NMAT == 2) wu[u] = *reinterpret_cast<const bf16x8_t*>(bu + k0 + 32 * u);
+        a0[u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);  // first row block: loaded with the weights
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
+          if (rb < nrb) {
+            const bf16x8_t a = rb == 0 ? a0[u] : *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0 + 32 * u);
+            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wg[u], acc[0][rb], 0, 0, 0);
+            if (NMAT == 2) acc[NMAT - 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wu[u], acc[NMAT - 1][rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    for (; k0 < K; k0 += 32) {
+      const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(bg + k0);
+      const bf16x8_t u = NMAT == 2 ? *reinterpret_cast<const bf16x8_t*>(bu + k0) : g;
+#pragma unroll
+      for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
+        if (rb < nrb) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0);
+          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[0][rb], 0, 0, 0);
+          if (NMAT == 2) acc[NMAT - 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[NMAT - 1][rb], 0, 0, 0);
+        }
+      }
+    }
+    // 16x16 layout: lane -> weight row (column of the output) lane & 15,
+    // register i -> token row 4*(lane/16) + i of the row block
+    const int col = col0 + (lane & 15);
+#pragma unroll
+    for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m0 + rb * 16 + 4 * (lane >> 4) + i;
+        if (rb < nrb && r < seg_n && col < N) {
+          const float v = NMAT == 2 ? silu(acc[0][rb][i]) * acc[NMAT - 1][rb][i] : acc[0][rb][i];
+          C[size_t(seg0 + r) * N + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+template <int NMAT>
+moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
+                  bf16_t* C, int L, int N, int K, hipStream_t s) {
+  const dim3 grid(unsigned((N + kColsPerBlock - 1) / kColsPerBlock), unsigned(L));
+  MOE_LAUNCH(name, gemm_kernel<NMAT>, grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K);
+  return MOE_OK;
+}
+
+}  // namespace skinny
+
 template <typename T>
 moe_status launch_t(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
@@ -505,6 +613,18 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
     return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
                           static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I,
                           a.max_pairs, a.s);
+  }
+  // decode-sized batches: a few rows per expert, bound by streaming the weights
+  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * d->local_count && skinny::supported(d->hidden) &&
+      skinny::supported(d->intermediate)) {
+    const int L = d->local_count, H = d->hidden, I = d->intermediate;
+    bf16_t* h = static_cast<bf16_t*>(a.h);
+    moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
+                                      static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
+                                      H, a.s);
+    if (st != MOE_OK) return st;
+    return skinny::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
+                             static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.s);
   }
   return d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
