@@ -206,6 +206,9 @@ moe_status dispatch_checks(const moe_layer_desc* d, const void* x, const int32_t
   REQUIRE_PTR(pair_row, 4);
   REQUIRE_PTR(x_sorted, 16);
   OPTIONAL_PTR(num_dropped, 8);
+  // the capacity cut holds an expert's pairs (at most one per token) in registers
+  if (d->capacity_factor > 0 && d->num_tokens > 32768)
+    return set_error(MOE_ERR_UNSUPPORTED, "capacity_factor > 0 supports at most 32768 tokens per call");
   return MOE_OK;
 }
 

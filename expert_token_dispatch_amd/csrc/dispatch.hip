@@ -20,9 +20,11 @@
 //             among equal experts is its rank within its wave (match-any +
 //             popcount of lower lanes) plus the counts of earlier waves and
 //             earlier rounds -- no atomics, so the order is deterministic;
-//   capacity  (only with a limit) one block per local expert: radix select
-//             of the C-th largest key (logit desc, then token asc) and a
-//             stable compaction of the kept pairs;
+//   capacity  (only with a limit) one block per local expert: the expert's
+//             keys sit in registers (element j*1024 + thread); radix select of
+//             the C-th largest key (logit desc, then token asc), then a stable
+//             compaction from per-wave ballots and two scans over the 512
+//             (register, wave) slots;
 //   gather    token-major row copies: one wave reads x[t] once and writes it
 //             to the sorted row of each kept local pair, 16-byte vectors.
 #include "common.h"
@@ -243,6 +245,43 @@ __device__ __forceinline__ uint32_t logit_key(float f) {
 }
 
 constexpr int kCapThreads = 1024;
+constexpr int kCapPerThread = 32;  // register-resident keys per thread (segments up to 32768 pairs)
+constexpr int kCapWaves = kCapThreads / 64;
+constexpr int kCapSlots = kCapPerThread * kCapWaves;  // (register, wave) slots in segment order
+
+// Finds the digit (bits [shift, shift+8) of keys matching `prefix` on `mask`)
+// at which the count from the largest digit down reaches `want`; the block's
+// histogram is in hist[256].  Returns the digit and leaves in *left how many
+// of the wanted keys still have to come from that digit.  Wave 0 does a
+// suffix scan over the 256 bins (4 per lane); the result goes through LDS.
+__device__ void pick_digit(const int* hist, int want, uint32_t* s_digit, int* s_want) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // lane L owns bins 255-4L .. 252-4L (largest digits first)
+    int c[4];
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[255 - 4 * lane - q];
+      tot += c[q];
+    }
+    const int incl = wave_inclusive_scan(tot);
+    int before = incl - tot;  // keys in larger digits than this lane's bins
+    // the first lane whose range reaches `want` holds the digit
+    const uint64_t hit = __ballot(before < want && incl >= want);
+    if (hit != 0 && lane == __ffsll((unsigned long long)hit) - 1) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (before + c[q] >= want) {
+          *s_digit = uint32_t(255 - 4 * lane - q);
+          *s_want = want - before;
+          break;
+        }
+        before += c[q];
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ tmp_sorted,
                                                                const int32_t* __restrict__ pre_off,
@@ -252,6 +291,7 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
                                                                int32_t* __restrict__ pair_row) {
   __shared__ int hist[256];
   __shared__ int wsum[kCapThreads / 64];
+  __shared__ int slot_cnt[kCapSlots];
   __shared__ uint32_t s_digit;
   __shared__ int s_want;
   const int tid = threadIdx.x;
@@ -270,29 +310,36 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
     return;
   }
 
-  // radix select, most significant byte first: find the key value thr of the
-  // cap-th largest key and how many keys equal to thr are still wanted
+  if (cap == 0) {  // nothing is kept
+    for (int r = tid; r < n; r += kCapThreads) pair_row[seg[r]] = -1;
+    return;
+  }
+
+  // element r = j*1024 + tid of the segment sits in this thread's register j
+  // (coalesced loads; segment order is j-major, then wave, then lane)
+  const int lane = tid & 63, wave = tid >> 6;
+  int pid[kCapPerThread];
+  uint32_t key[kCapPerThread];
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    const int r = j * kCapThreads + tid;
+    pid[j] = r < n ? seg[r] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) key[j] = pid[j] >= 0 ? logit_key(topk_logit[pid[j]]) : 0u;
+
+  // radix select, most significant byte first: threshold key thr of the cap-th
+  // largest key, and how many keys equal to thr are still wanted
   uint32_t prefix = 0, mask = 0;
   int want = cap;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = tid; j < 256; j += kCapThreads) hist[j] = 0;
+    for (int b = tid; b < 256; b += kCapThreads) hist[b] = 0;
     __syncthreads();
-    for (int r = tid; r < n; r += kCapThreads) {
-      const uint32_t key = logit_key(topk_logit[seg[r]]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < kCapPerThread; ++j)
+      if (pid[j] >= 0 && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xFFu], 1);
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      for (int dgt = 255; dgt >= 0; --dgt) {
-        if (cum + hist[dgt] >= want) {
-          s_digit = uint32_t(dgt);
-          s_want = want - cum;
-          break;
-        }
-        cum += hist[dgt];
-      }
-    }
+    pick_digit(hist, want, &s_digit, &s_want);
     __syncthreads();
     prefix |= s_digit << shift;
     mask |= 0xFFu << shift;
@@ -302,26 +349,52 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
   const uint32_t thr = prefix;
   const int need_eq = want;  // keys equal to thr kept: the first need_eq in segment (= token) order
 
-  int carry_eq = 0, carry_keep = 0;
-  for (int r0 = 0; r0 < n; r0 += kCapThreads) {
-    const int r = r0 + tid;
-    const bool in = r < n;
-    const int p = in ? seg[r] : 0;
-    const uint32_t key = in ? logit_key(topk_logit[p]) : 0u;
-    const int eq = (in && key == thr) ? 1 : 0;
-    int tot_eq, tot_keep;
-    const int ex_eq = block_exclusive_scan(eq, wsum, &tot_eq);
-    const int keep = (in && (key > thr || (eq && carry_eq + ex_eq < need_eq))) ? 1 : 0;
-    const int ex_keep = block_exclusive_scan(keep, wsum, &tot_keep);
-    if (keep) {
-      const int pos = out0 + carry_keep + ex_keep;
-      sorted_pairs[pos] = p;
-      pair_row[p] = pos;
-    } else if (in) {
-      pair_row[p] = -1;
+  // rank of each key equal to thr among the equal keys before it, in segment order:
+  // per (j, wave) counts from ballots, one exclusive scan over the 512 (j, wave) slots
+  uint64_t eqm[kCapPerThread];
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    eqm[j] = __ballot(pid[j] >= 0 && key[j] == thr);
+    if (lane == 0) slot_cnt[j * kCapWaves + wave] = int(__popcll(eqm[j]));
+  }
+  __syncthreads();
+  int tot;
+  {
+    const int v = tid < kCapSlots ? slot_cnt[tid] : 0;
+    const int ex = block_exclusive_scan(v, wsum, &tot);
+    if (tid < kCapSlots) slot_cnt[tid] = ex;
+  }
+  __syncthreads();
+  uint64_t keepm[kCapPerThread];
+  const uint64_t below = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    const bool in = pid[j] >= 0;
+    const bool eq = in && key[j] == thr;
+    const int eq_before = slot_cnt[j * kCapWaves + wave] + int(__popcll(eqm[j] & below));
+    keepm[j] = __ballot(in && (key[j] > thr || (eq && eq_before < need_eq)));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j)
+    if (lane == 0) slot_cnt[j * kCapWaves + wave] = int(__popcll(keepm[j]));
+  __syncthreads();
+  {
+    const int v = tid < kCapSlots ? slot_cnt[tid] : 0;
+    const int ex = block_exclusive_scan(v, wsum, &tot);
+    if (tid < kCapSlots) slot_cnt[tid] = ex;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    if (pid[j] < 0) continue;
+    if ((keepm[j] >> lane) & 1u) {
+      const int pos = out0 + slot_cnt[j * kCapWaves + wave] + int(__popcll(keepm[j] & below));
+      sorted_pairs[pos] = pid[j];
+      pair_row[pid[j]] = pos;
+    } else {
+      pair_row[pid[j]] = -1;
     }
-    carry_eq += tot_eq;
-    carry_keep += tot_keep;
   }
 }
 
