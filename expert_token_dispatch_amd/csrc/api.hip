@@ -309,7 +309,7 @@ moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_route
   TRY(route_checks(d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit));
   if (logits_in == nullptr) TRY(check_ws(d, MOE_STAGE_ROUTE, ws, ws_bytes));
   RouteArgs a{d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit,
-              static_cast<float*>(ws), static_cast<hipStream_t>(stream)};
+              static_cast<float*>(ws), nullptr, static_cast<hipStream_t>(stream)};
   return launch_route(a);
 }
 
@@ -322,7 +322,7 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
   TRY(dispatch_checks(d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped));
   TRY(check_ws(d, MOE_STAGE_DISPATCH, ws, ws_bytes));
   DispatchArgs a{d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped,
-                 carve_dispatch_scratch(d, ws), capacity_of(d), static_cast<hipStream_t>(stream)};
+                 carve_dispatch_scratch(d, ws), capacity_of(d), false, static_cast<hipStream_t>(stream)};
   return launch_dispatch(a);
 }
 
@@ -368,11 +368,13 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
   TRY(combine_checks(w.y_sorted, w.pair_row, tw, y));
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
+  const DispatchScratch scr = carve_dispatch_scratch(d, w.dispatch);
+  // the router's top-k kernel also writes the per-chunk expert histograms
   RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, ids, tw, cap ? w.topk_logit : nullptr,
-               static_cast<float*>(w.route), s};
+               static_cast<float*>(w.route), scr.blk_all, s};
   TRY(launch_route(ra));
   DispatchArgs da{d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped,
-                  carve_dispatch_scratch(d, w.dispatch), capacity_of(d), s};
+                  scr, capacity_of(d), true, s};
   TRY(launch_dispatch(da));
   FfnArgs fa{d, w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted, w.h, max_pairs_of(d), s};
   TRY(launch_grouped_ffn(fa));

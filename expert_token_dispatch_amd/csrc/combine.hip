@@ -39,11 +39,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
     for (int j0 = 0; j0 < k; j0 += kBatch) {
-      uint4 v[kBatch];
+      u32x4_t v[kBatch];
 #pragma unroll
       for (int jj = 0; jj < kBatch; ++jj) {
         const int r = __shfl(my_row, j0 + jj, 64);
-        if (j0 + jj < k && r >= 0) v[jj] = ys[size_t(r) * vec_per_row + c];
+        if (j0 + jj < k && r >= 0) v[jj] = reinterpret_cast<const u32x4_t*>(ys)[size_t(r) * vec_per_row + c];
       }
       // accumulate in slot order
 #pragma unroll
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
         const float wj = __shfl(my_w, j0 + jj, 64);
         if (j0 + jj < k && r >= 0) {
           float f[EPV];
-          unpack16(v[jj], T(), f);
+          unpack16(make_uint4(v[jj][0], v[jj][1], v[jj][2], v[jj][3]), T(), f);
 #pragma unroll
           for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wj, f[e], acc[e]);
         }

@@ -9,13 +9,15 @@
 // adds an optional per-expert limit whose overflow skips the expert.
 //
 // Pair p = t*k + j.  Within a segment, pairs keep ascending p, so the result is
-// unique and matches a stable counting sort exactly:
-//   count     per block of `chunk` pairs, counts over all E experts, built
+// unique and matches a stable counting sort exactly.  Work goes by chunks of
+// 64 tokens (their 64*k pairs):
+//   count     per chunk, counts over all E experts (the router's top-k kernel
+//             writes these itself inside moe_layer_forward), built
 //             with a wave64 match-any (ballot over the id bits) so only one
 //             lane per distinct id touches the LDS histogram;
 //   scan      one block: totals per expert, (capacity), exclusive scans into
-//             segment offsets, and for every (block, expert) the first row of
-//             that block's pairs (a column scan over blocks, one wave each);
+//             segment offsets, and for every (chunk, expert) the first row of
+//             that chunk's pairs (range sums over chunks, then prefixes);
 //   scatter   per block again, in rounds of 256 pairs: the rank of a pair
 //             among equal experts is its rank within its wave (match-any +
 //             popcount of lower lanes) plus the counts of earlier waves and
@@ -25,22 +27,18 @@
 //             the C-th largest key (logit desc, then token asc), then a stable
 //             compaction from per-wave ballots and two scans over the 512
 //             (register, wave) slots;
-//   gather    token-major row copies: one wave reads x[t] once and writes it
-//             to the sorted row of each kept local pair, 16-byte vectors.
+//   place     without a capacity cut, scatter and row copy in one kernel:
+//             ranks as in scatter, then token-major copies (one read of x[t],
+//             one write per kept local pair, 16-byte vectors);
+//   gather    with a capacity cut, the same token-major copy after it.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-int dispatch_chunk(int64_t n_pairs, int32_t local_count) {
-  (void)n_pairs;
-  (void)local_count;
-  return 4 * kDispatchThreads;
-}
-
 size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   const int64_t n = d->num_tokens * d->top_k;
-  const int64_t nblk = dispatch_blocks(n, d->local_count);
+  const int64_t nblk = dispatch_blocks(d->num_tokens);
   size_t b = 0;
   b += align_up(size_t(nblk) * d->num_experts * 4, 256);
   b += align_up(size_t(nblk) * d->local_count * 4, 256);
@@ -50,8 +48,7 @@ size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
 }
 
 DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
-  const int64_t n = d->num_tokens * d->top_k;
-  const int64_t nblk = dispatch_blocks(n, d->local_count);
+  const int64_t nblk = dispatch_blocks(d->num_tokens);
   char* p = static_cast<char*>(ws);
   DispatchScratch s{};
   s.blk_all = reinterpret_cast<int32_t*>(p);
@@ -111,6 +108,7 @@ __global__ __launch_bounds__(kDispatchThreads) void count_kernel(const int32_t* 
 
 // ---- scan -------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
+constexpr int kScanGroups = 16;  // chunk ranges per column: short serial prefixes over the range sums
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_all, int nblk, int E,
                                                             int begin, int L, int64_t cap, int32_t* __restrict__ counts,
@@ -125,15 +123,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  for (int e = tid; e < E; e += kScanThreads) cnt[e] = 0;
-  __syncthreads();
-  const int64_t total = int64_t(nblk) * E;
-  for (int64_t idx = tid; idx < total; idx += kScanThreads) {
-    const int v = blk_all[idx];
-    if (v != 0) atomicAdd(&cnt[int(idx % E)], v);
+  __shared__ int rsum[kScanThreads];
+  // totals per expert: columns in groups of up to 1024; thread t sums column
+  // t % Ec over a contiguous range of chunks (coalesced across the columns)
+  for (int c0 = 0; c0 < E; c0 += kScanThreads) {
+    const int Ec = min(kScanThreads, E - c0);
+    const int G = min(kScanGroups, kScanThreads / Ec);
+    const int per = (nblk + G - 1) / G;
+    const int e = tid % Ec, g = tid / Ec;
+    int sum = 0;
+    if (g < G) {
+      const int b_lo = min(nblk, g * per), b_hi = min(nblk, b_lo + per);
+      const int32_t* col = blk_all + c0 + e;
+      for (int b = b_lo; b < b_hi; ++b) sum += col[size_t(b) * E];
+      rsum[tid] = sum;
+    }
+    __syncthreads();
+    if (tid < Ec) {
+      int tot = 0;
+      for (int gg = 0; gg < G; ++gg) tot += rsum[gg * Ec + tid];
+      cnt[c0 + tid] = tot;
+      counts[c0 + tid] = tot;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = tid; e < E; e += kScanThreads) counts[e] = cnt[e];
 
   // segment offsets before (pre) and after (offsets) the capacity cut
   int carry_pre = 0, carry_post = 0;
@@ -169,17 +182,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     *num_dropped = s;
   }
 
-  // first pre-capacity row of every block's pairs of local expert i:
-  // pre[i] + sum over earlier blocks of their count of expert begin+i
-  for (int i = wave; i < L; i += kScanThreads / 64) {
-    int carry = pre[i];
-    for (int b0 = 0; b0 < nblk; b0 += 64) {
-      const int b = b0 + lane;
-      const int v = b < nblk ? blk_all[size_t(b) * E + begin + i] : 0;
-      const int incl = wave_inclusive_scan(v);
-      if (b < nblk) blk_base[size_t(b) * L + i] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
+  // first pre-capacity row of every chunk's pairs of local expert i:
+  // pre[i] + sum over earlier chunks of their count of expert begin+i.
+  // Columns in groups of up to 1024: thread t takes column t % Lc and a
+  // contiguous range of chunks (group t / Lc); range sums go through LDS.
+  for (int c0 = 0; c0 < L; c0 += kScanThreads) {
+    const int Lc = min(kScanThreads, L - c0);
+    const int G = min(kScanGroups, kScanThreads / Lc);
+    const int per = (nblk + G - 1) / G;
+    const int i = tid % Lc, g = tid / Lc;
+    const bool act = g < G;
+    const int b_lo = act ? min(nblk, g * per) : 0, b_hi = act ? min(nblk, b_lo + per) : 0;
+    const int32_t* col = blk_all + begin + c0 + i;
+    int s = 0;
+    for (int b = b_lo; b < b_hi; ++b) s += col[size_t(b) * E];
+    if (act) rsum[tid] = s;
+    __syncthreads();
+    if (act) {
+      int run = pre[c0 + i];
+      for (int gg = 0; gg < g; ++gg) run += rsum[gg * Lc + i];
+      for (int b = b_lo; b < b_hi; ++b) {
+        blk_base[size_t(b) * L + c0 + i] = run;
+        run += col[size_t(b) * E];
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -404,8 +431,8 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
 // however many experts a token picked.
 constexpr int kGatherTokensPerBlock = 4;
 
-__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ pair_row,
-                                                     int64_t ntok, int k, int vec_per_row, uint4* __restrict__ xs) {
+__global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__ x, const int32_t* __restrict__ pair_row,
+                                                     int64_t ntok, int k, int vec_per_row, u32x4_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kGatherTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
@@ -413,10 +440,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   // destinations as a bit mask over slots (k <= 32)
   const uint64_t kept = __ballot(my_row >= 0);
   if (kept == 0) return;
-  const uint4* src = x + size_t(t) * vec_per_row;
+  const u32x4_t* src = x + size_t(t) * vec_per_row;
   constexpr int kUnroll = 4;
   for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kUnroll) {
-    uint4 v[kUnroll];
+    u32x4_t v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int c = c0 + u * 64 + lane;
@@ -425,11 +452,105 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
     for (uint64_t m = kept; m != 0; m &= m - 1) {
       const int j = __ffsll((unsigned long long)m) - 1;
       const int r = __shfl(my_row, j, 64);
-      uint4* dst = xs + size_t(r) * vec_per_row;
+      u32x4_t* dst = xs + size_t(r) * vec_per_row;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = c0 + u * 64 + lane;
         if (c < vec_per_row) dst[c] = v[u];
+      }
+    }
+  }
+}
+
+// ---- place (scatter + gather in one pass, no capacity cut) -------------------
+// kPlaceSplit blocks share one chunk of kDispatchTokens tokens: each ranks all
+// of the chunk's pairs exactly like the scatter kernel (so the rows are the
+// same), the first also writes sorted_pairs/pair_row, and each copies the
+// rows of its quarter of the chunk's tokens, token-major (one read of x[t],
+// one write per kept local pair).
+constexpr int kPlaceSplit = 4;
+
+__global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* __restrict__ ids, int64_t ntok, int k,
+                                                                 int begin, int L, const int32_t* __restrict__ blk_base,
+                                                                 int32_t* __restrict__ sorted_pairs,
+                                                                 int32_t* __restrict__ pair_row,
+                                                                 const u32x4_t* __restrict__ x, int vec_per_row,
+                                                                 u32x4_t* __restrict__ xs) {
+  extern __shared__ int32_t sh[];
+  constexpr int kWaves = kDispatchThreads / 64;
+  int32_t* run = sh;                      // [L]
+  int32_t* cnt = sh + L;                  // [kWaves][L]
+  int32_t* pos = sh + L * (1 + kWaves);   // [kDispatchTokens * k] row of each of the chunk's pairs, -1 if none
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int chunk = blockIdx.x / kPlaceSplit, part = blockIdx.x % kPlaceSplit;
+  const int64_t t0 = int64_t(chunk) * kDispatchTokens;
+  const int ntk = int(min<int64_t>(kDispatchTokens, ntok - t0));
+  const int np = ntk * k;
+  const int64_t p0 = t0 * k;
+
+  for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
+  for (int q = tid; q < kWaves * L; q += kDispatchThreads) cnt[q] = 0;
+  __syncthreads();
+  const int bits = bits_for(L);
+  for (int base = 0; base < np; base += kDispatchThreads) {
+    const int r = base + tid;
+    const bool valid = r < np;
+    const int id = valid ? ids[p0 + r] : -1;
+    const int li = (id >= begin && id < begin + L) ? id - begin : L;  // L: not local
+    const uint64_t m = match_any(uint32_t(li), bits, ~uint64_t(0));
+    const uint64_t lower = m & lanemask_lt();
+    if (li < L && lower == 0) cnt[wave * L + li] = int(__popcll(m));
+    __syncthreads();
+    if (li < L) {
+      int ps = run[li] + int(__popcll(lower));
+      for (int w = 0; w < wave; ++w) ps += cnt[w * L + li];
+      pos[r] = ps;
+      if (part == 0) {
+        sorted_pairs[ps] = int32_t(p0 + r);
+        pair_row[p0 + r] = ps;
+      }
+    } else if (valid) {
+      pos[r] = -1;
+      if (part == 0) pair_row[p0 + r] = -1;
+    }
+    __syncthreads();
+    for (int q = tid; q < L; q += kDispatchThreads) {
+      int sum = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        sum += cnt[w * L + q];
+        cnt[w * L + q] = 0;
+      }
+      run[q] += sum;
+    }
+    __syncthreads();
+  }
+
+  // copy this part's tokens: wave w takes tokens part*16 + 4w .. +3 of the chunk
+  constexpr int kTokPerPart = kDispatchTokens / kPlaceSplit;
+  constexpr int kUnroll = 4;
+  for (int tt = part * kTokPerPart + wave * (kTokPerPart / kWaves);
+       tt < part * kTokPerPart + (wave + 1) * (kTokPerPart / kWaves) && tt < ntk; ++tt) {
+    const int my_row = lane < k ? pos[tt * k + lane] : -1;
+    const uint64_t kept = __ballot(my_row >= 0);
+    if (kept == 0) continue;
+    const u32x4_t* src = x + size_t(t0 + tt) * vec_per_row;
+    for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kUnroll) {
+      u32x4_t v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < vec_per_row) v[u] = src[c];
+      }
+      for (uint64_t mk = kept; mk != 0; mk &= mk - 1) {
+        const int j = __ffsll((unsigned long long)mk) - 1;
+        const int rrow = __shfl(my_row, j, 64);
+        u32x4_t* dst = xs + size_t(rrow) * vec_per_row;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int c = c0 + u * 64 + lane;
+          if (c < vec_per_row) dst[c] = v[u];
+        }
       }
     }
   }
@@ -440,30 +561,37 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
 moe_status launch_dispatch(const DispatchArgs& a) {
   const moe_layer_desc* d = a.d;
   const int64_t n = d->num_tokens * d->top_k;
-  const int chunk = dispatch_chunk(n, d->local_count);
-  const int nblk = int(dispatch_blocks(n, d->local_count));
+  const int chunk = kDispatchTokens * d->top_k;  // pairs per chunk
+  const int nblk = int(dispatch_blocks(d->num_tokens));
   const int E = d->num_experts, L = d->local_count, begin = d->local_begin;
   const bool cap = a.capacity >= 0;
+  const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
 
-  MOE_LAUNCH("dispatch_count", count_kernel, dim3(nblk), dim3(kDispatchThreads), size_t(E) * 4, a.s, a.topk_ids, n, E,
-             chunk, a.scr.blk_all);
+  if (!a.counts_ready) {
+    MOE_LAUNCH("dispatch_count", count_kernel, dim3(nblk), dim3(kDispatchThreads), size_t(E) * 4, a.s, a.topk_ids, n, E,
+               chunk, a.scr.blk_all);
+  }
   MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all, nblk,
              E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.num_dropped);
-  const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
   if (cap) {
+    const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
     MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
                begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row);
     MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), 0, a.s, a.scr.tmp_sorted, a.scr.pre_off,
                a.offsets, a.topk_logit, int(a.capacity), a.sorted_pairs, a.pair_row);
-  } else {
-    MOE_LAUNCH("dispatch_scatter", scatter_kernel<false>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids,
-               n, begin, L, chunk, a.scr.blk_base, a.sorted_pairs, a.pair_row);
-  }
-  {
-    const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
     const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
-    MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.x), a.pair_row,
-               d->num_tokens, d->top_k, vec_per_row, static_cast<uint4*>(a.x_sorted));
+    MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const u32x4_t*>(a.x), a.pair_row,
+               d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
+  } else {
+    const size_t lds = (size_t(L) * (1 + kDispatchThreads / 64) + size_t(chunk)) * 4;
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(place_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_place: LDS attribute: %s", hipGetErrorString(e));
+    }
+    MOE_LAUNCH("dispatch_place", place_kernel, dim3(unsigned(nblk) * kPlaceSplit), dim3(kDispatchThreads), lds, a.s,
+               a.topk_ids, d->num_tokens, d->top_k, begin, L, a.scr.blk_base, a.sorted_pairs, a.pair_row,
+               static_cast<const u32x4_t*>(a.x), vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
   }
   return MOE_OK;
 }

@@ -27,13 +27,11 @@ moe_status prof_after(const char* name, hipStream_t s);
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t dtype_bytes(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 
-// Pairs handled by one block of the dispatch histogram/scatter kernels.
+// Dispatch works on chunks of kDispatchTokens consecutive tokens (their
+// k pairs each): per-chunk expert histograms, per-chunk segment bases.
 constexpr int kDispatchThreads = 256;
-int dispatch_chunk(int64_t n_pairs, int32_t local_count);
-inline int64_t dispatch_blocks(int64_t n_pairs, int32_t local_count) {
-  const int c = dispatch_chunk(n_pairs, local_count);
-  return (n_pairs + c - 1) / c;
-}
+constexpr int kDispatchTokens = 64;
+inline int64_t dispatch_blocks(int64_t num_tokens) { return (num_tokens + kDispatchTokens - 1) / kDispatchTokens; }
 
 // ---- stage launchers --------------------------------------------------------
 struct RouteArgs {
@@ -46,7 +44,8 @@ struct RouteArgs {
   int32_t* topk_ids;
   float* topk_w;
   float* topk_logit;
-  float* partial;  // route scratch: per-slice partial logits
+  float* partial;       // route scratch: per-slice partial logits
+  int32_t* blk_counts;  // optional [dispatch_blocks(T), E]: per-chunk expert histogram for dispatch
   hipStream_t s;
 };
 size_t route_scratch_bytes(const moe_layer_desc* d);
@@ -74,7 +73,8 @@ struct DispatchArgs {
   void* x_sorted;
   int64_t* num_dropped;
   DispatchScratch scr;
-  int64_t capacity;  // -1: none
+  int64_t capacity;     // -1: none
+  bool counts_ready;    // scr.blk_all already holds the per-chunk histograms (written by the router)
   hipStream_t s;
 };
 moe_status launch_dispatch(const DispatchArgs& a);

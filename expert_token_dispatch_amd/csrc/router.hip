@@ -215,17 +215,23 @@ __device__ __forceinline__ void topk_insert(float (&v)[MAXK], int (&id)[MAXK], f
   }
 }
 
+static_assert(kTopkTok == kDispatchTokens, "a top-k block is one dispatch chunk");
+
 template <int MAXK>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ partial, int nslice,
                                                             const float* __restrict__ br, float* __restrict__ logits_out,
                                                             int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                            float* __restrict__ tl, int ntok, int E, int k) {
+                                                            float* __restrict__ tl, int32_t* __restrict__ blk_counts,
+                                                            int ntok, int E, int k) {
   extern __shared__ float sh[];
   const int ld = E + 1;
   float* lg = sh;                                          // [64][E + 1]
   float* mv = sh + kTopkTok * ld;                          // [64][4][MAXK] merge values
   int* mi = reinterpret_cast<int*>(mv + kTopkTok * 4 * MAXK);  // [64][4][MAXK] merge ids
+  int* hist = mi + kTopkTok * 4 * MAXK;                    // [E] chunk histogram (when blk_counts)
   const int tid = threadIdx.x;
+  if (blk_counts != nullptr)
+    for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
   const int t0 = blockIdx.x * kTopkTok;
   const int rows = min(kTopkTok, ntok - t0);
   const int n = rows * E;  // the tile's logits are contiguous in every slice
@@ -283,51 +289,58 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   __syncthreads();
 
   // ---- merge the four sorted lists; on equal scores the lower quarter (lower ids) goes first
-  if (q != 0 || m >= rows) return;
-  const int t = t0 + m;
-  int head[4] = {0, 0, 0, 0};
-  float sel_v[MAXK];
-  int sel_i[MAXK];
+  if (q == 0 && m < rows) {
+    const int t = t0 + m;
+    int head[4] = {0, 0, 0, 0};
+    float sel_v[MAXK];
+    int sel_i[MAXK];
 #pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    if (j < k) {
-      int best = -1;
-      float bv = -INFINITY;
+    for (int j = 0; j < MAXK; ++j) {
+      if (j < k) {
+        int best = -1;
+        float bv = -INFINITY;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        if (head[qq] < MAXK) {
-          const int off = (m * 4 + qq) * MAXK + head[qq];
-          if (mi[off] >= 0 && (best < 0 || mv[off] > bv)) {
-            best = qq;
-            bv = mv[off];
+        for (int qq = 0; qq < 4; ++qq) {
+          if (head[qq] < MAXK) {
+            const int off = (m * 4 + qq) * MAXK + head[qq];
+            if (mi[off] >= 0 && (best < 0 || mv[off] > bv)) {
+              best = qq;
+              bv = mv[off];
+            }
           }
         }
+        const int off = (m * 4 + best) * MAXK + head[best];
+        sel_v[j] = bv;
+        sel_i[j] = mi[off];
+        head[best] += 1;
       }
-      const int off = (m * 4 + best) * MAXK + head[best];
-      sel_v[j] = bv;
-      sel_i[j] = mi[off];
-      head[best] += 1;
+    }
+    const float top = sel_v[0];
+    float ex[MAXK];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+      if (j < k) {
+        ex[j] = expf(sel_v[j] - top);
+        sum += ex[j];
+      }
+    }
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+      if (j < k) {
+        const size_t o = size_t(t) * k + j;
+        ids[o] = sel_i[j];
+        tw[o] = ex[j] * inv;
+        if (tl != nullptr) tl[o] = sel_v[j];
+        if (blk_counts != nullptr) atomicAdd(&hist[sel_i[j]], 1);
+      }
     }
   }
-  const float top = sel_v[0];
-  float ex[MAXK];
-  float sum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    if (j < k) {
-      ex[j] = expf(sel_v[j] - top);
-      sum += ex[j];
-    }
-  }
-  const float inv = 1.0f / sum;
-#pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    if (j < k) {
-      const size_t o = size_t(t) * k + j;
-      ids[o] = sel_i[j];
-      tw[o] = ex[j] * inv;
-      if (tl != nullptr) tl[o] = sel_v[j];
-    }
+  // the chunk's expert histogram for dispatch (integer counts: order-free)
+  if (blk_counts != nullptr) {
+    __syncthreads();
+    for (int e = tid; e < E; e += kTopkThreads) blk_counts[size_t(blockIdx.x) * E + e] = hist[e];
   }
 }
 
@@ -370,7 +383,7 @@ moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, con
   const moe_layer_desc* d = a.d;
   const int ntok = int(d->num_tokens);
   const int E = d->num_experts;
-  const size_t lds = (size_t(kTopkTok) * (E + 1) + size_t(kTopkTok) * 4 * MAXK * 2) * sizeof(float);
+  const size_t lds = (size_t(kTopkTok) * (E + 1) + size_t(kTopkTok) * 4 * MAXK * 2 + size_t(E)) * sizeof(float);
   auto kern = topk_kernel<MAXK>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -379,7 +392,7 @@ moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, con
   }
   const dim3 grid(unsigned((ntok + kTopkTok - 1) / kTopkTok));
   MOE_LAUNCH("route_topk", kern, grid, dim3(kTopkThreads), lds, a.s, partial, nslice, bias, a.logits_out,
-             a.topk_ids, a.topk_w, a.topk_logit, ntok, E, d->top_k);
+             a.topk_ids, a.topk_w, a.topk_logit, a.blk_counts, ntok, E, d->top_k);
   return MOE_OK;
 }
 
