@@ -218,13 +218,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
 // fragment reads of 16 lanes (16 rows, one chunk) cover all 64 banks.
 //
 // Schedule of one stage (per wave): for each 16-k chunk, the fragments of the
-// next chunk are read while this chunk's 16 MFMAs issue (pinned with
-// sched_group_barrier).  Before the last chunk the wave waits for its own
+// next chunk are read while this chunk's 16 MFMAs issue, one read between
+// every two MFMAs (pinned with sched_group_barrier); reads bunched at the
+// start of the group left the LDS and the matrix core taking turns.  Before the last chunk the wave waits for its own
 // loads of the next stage and for its own reads of this stage, then a block
 // barrier makes both true for every wave: the next stage's first fragments
 // are read and this stage's slot is refilled (stage kt+2) while the last 16
 // MFMAs run.  The barrier is a bare s_barrier: __syncthreads() would also
 // drain every load in flight.
+//
+// The MFMAs take the weight fragment as the left operand, so each lane ends
+// with four adjacent output columns of one token row; the epilogue parks the
+// bf16 tile in LDS and writes it out in whole row pieces.
 //
 // Tile order: the blocks that run at once on one XCD (blocks are dealt to
 // the 8 XCDs round robin) get consecutive tile numbers, and tile numbers run
@@ -240,7 +245,14 @@ constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2, kThreads = 256;
 constexpr int kRowBytes = BK * 2;              // 128
 constexpr int kStageA = BM * kRowBytes;        // 32 KB
 constexpr int kStage = kStageA + BNE * kRowBytes;
-constexpr size_t kLdsBytes = size_t(kStages) * kStage;  // 128 KB
+constexpr size_t kLoopLds = size_t(kStages) * kStage;  // 128 KB
+// epilogue staging: the output tile as bf16 rows of ON columns plus 16 bytes of padding
+template <int NMAT>
+constexpr int stage_row_bytes() { return (NMAT == 2 ? BNE / 2 : BNE) * 2 + 16; }
+template <int NMAT>
+constexpr size_t lds_bytes() {
+  return kLoopLds > size_t(BM) * stage_row_bytes<NMAT>() ? kLoopLds : size_t(BM) * stage_row_bytes<NMAT>();
+}
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
 
@@ -363,16 +375,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   do {                                                                                                    \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                       \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf_][i], fb[buf_][j], acc[i][j], 0, 0, 0); \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][i], acc[i][j], 0, 0, 0); \
   } while (0)
-  // 8 x {1 MFMA, 1 LDS read}, then the other 8 MFMAs
+  // 8 x {MFMA, LDS read, MFMA}: the next chunk's fragment reads spread over the whole group
 #define MOE_PIPE_DS()                                                                                     \
   do {                                                                                                    \
     _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                  \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                  \
     }                                                                                                     \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                                    \
   } while (0)
 
   const int nk = K / BK;
@@ -429,29 +441,47 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 #undef MOE_MMA
 #undef MOE_PIPE_DS
 
-  // ---- epilogue (32x32 layout: lane -> column lane & 31, register r -> row
-  // 8*(r/4) + 4*(lane/32) + r%4) -----------------------------------------------
+  // ---- epilogue.  The products were formed as (weight rows) x (token rows),
+  // so in the 32x32 accumulator layout lane l holds token row l & 31 and
+  // register 4q+u holds output column 8q + 4*(l/32) + u: four adjacent columns
+  // per q.  Each wave converts its part of the tile to bf16 (SwiGLU first for
+  // gate/up) and parks it in LDS, rows padded by 16 bytes; then every thread
+  // copies 16-byte row chunks out, so each store instruction writes whole
+  // 256-byte row pieces.
+  constexpr int TC = NMAT == 2 ? BNE / 2 : BNE;  // output columns of the tile
+  constexpr int RS = stage_row_bytes<NMAT>();
+  constexpr int NJ = NMAT == 2 ? 2 : 4;
+  MOE_LGKMCNT0();
+  block_barrier();  // every wave is done reading the last stage
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int rt = wm * 128 + i * 32 + fr;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rt = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (rt >= rows) continue;
-      bf16_t* crow = C + size_t(row0 + rt) * N;
-      if (NMAT == 2) {
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + fr;
-          if (col < N) crow[col] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else {
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + fr;
-          if (col < N) crow[col] = f32_to_bf16(acc[i][j][r]);
-        }
+        for (int u = 0; u < 4; ++u)
+          v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + 2][4 * q + u] : acc[i][j][4 * q + u];
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        pk.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
+        *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
       }
     }
+  }
+  MOE_LGKMCNT0();
+  block_barrier();
+  constexpr int CPR = TC / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int u = 0; u < BM * CPR / kThreads; ++u) {
+    const int id = tid + kThreads * u;
+    const int r = id / CPR, c = id % CPR;
+    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
+    // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
+    if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(C + size_t(row0 + r) * N + n0 + c * 8) = val;
   }
 }
 #undef MOE_VMCNT
@@ -461,13 +491,14 @@ template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                   bf16_t* C, int L, int N, int K, int64_t max_pairs, hipStream_t s) {
   auto kern = gemm_kernel<NMAT>;
+  constexpr size_t lds = lds_bytes<NMAT>();
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsBytes));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int64_t mslots = (max_pairs + BM - 1) / BM + L;
   const int64_t grid = mslots * ((N + ON - 1) / ON);
-  MOE_LAUNCH(name, kern, dim3(unsigned(grid)), dim3(kThreads), kLdsBytes, s, A, offsets, B0, B1, C, L, N, K);
+  MOE_LAUNCH(name, kern, dim3(unsigned(grid)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K);
   return MOE_OK;
 }
 
