@@ -82,6 +82,9 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
         return T * k * 4 * 3, 0.0
     if name == "dispatch_gather":
         return (touched_tokens + P) * H * dt + P * 4, 0.0
+    if name == "dispatch_place":
+        # ranks from the pair ids and chunk bases, both permutation arrays, and the row copy
+        return T * k * 4 * 2 + nblk * E * 4 + P * 4 + (touched_tokens + P) * H * dt, 0.0
     if name == "ffn_gate_up":
         return P * H * dt + 2 * touched_experts * I * H * dt + P * I * dt, 4.0 * P * H * I
     if name == "ffn_down":

@@ -518,26 +518,36 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
 // expert that received no rows returns before touching its weights.
 namespace skinny {
 
-constexpr int kThreads = 256, kColsPerBlock = 64, kUnroll = 8, kMaxRowBlocks = 4;
+constexpr int kThreads = 256, kUnroll = 8, kMaxRowBlocks = 4;
 
 bool supported(int K) { return K % 32 == 0; }
+
+// Each wave streams two sets of 16 weight rows: for gate/up the gate and the
+// up rows of the same 16 output columns, for down two adjacent groups of 16
+// output columns.  So a block (four waves) covers 64 gate/up columns or 128
+// down columns, and every lane keeps two weight loads per k step in flight.
+template <int NMAT>
+constexpr int cols_per_block() { return NMAT == 2 ? 64 : 128; }
 
 template <int NMAT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                         const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                         bf16_t* __restrict__ C, int N, int K) {
+  constexpr int kWaveCols = NMAT == 2 ? 16 : 32;
   const int expert = blockIdx.y;
   const int seg0 = offsets[expert];
   const int seg_n = offsets[expert + 1] - seg0;
   if (seg_n <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = blockIdx.x * kColsPerBlock + wave * 16;  // first weight row of this wave
+  const int col0 = blockIdx.x * cols_per_block<NMAT>() + wave * kWaveCols;  // first output column of this wave
   if (col0 >= N) return;
   const size_t boff = size_t(expert) * N * K;
-  const int wrow = min(col0 + (lane & 15), N - 1);            // rows past N repeat row N-1; never stored
-  const int kg = (lane >> 4) * 8;                             // the lane's 8 k values within a step
-  const bf16_t* bg = B0 + boff + size_t(wrow) * K + kg;
-  const bf16_t* bu = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow) * K + kg;
+  const int kg = (lane >> 4) * 8;  // the lane's 8 k values within a step
+  // stream 0 / 1 weight row of this lane (rows past N repeat row N-1; never stored)
+  const int wrow0 = min(col0 + (lane & 15), N - 1);
+  const int wrow1 = NMAT == 2 ? wrow0 : min(col0 + 16 + (lane & 15), N - 1);
+  const bf16_t* bs0 = B0 + boff + size_t(wrow0) * K + kg;
+  const bf16_t* bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow1) * K + kg;
 
   for (int m0 = 0; m0 < seg_n; m0 += 16 * kMaxRowBlocks) {
     const int nrb = min(kMaxRowBlocks, (seg_n - m0 + 15) / 16);
@@ -546,19 +556,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 #pragma unroll
     for (int rb = 0; rb < kMaxRowBlocks; ++rb)
       arow[rb] = A + size_t(seg0 + min(m0 + rb * 16 + (lane & 15), seg_n - 1)) * K + kg;
-    f32x4_t acc[NMAT][kMaxRowBlocks];
+    f32x4_t acc[2][kMaxRowBlocks];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int rb = 0; rb < kMaxRowBlocks; ++rb) acc[m][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     int k0 = 0;
     for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
-      bf16x8_t wg[kUnroll], wu[kUnroll], a0[kUnroll];
+      bf16x8_t w0[kUnroll], w1[kUnroll], a0[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        wg[u] = *reinterpret_cast<const bf16x8_t*>(bg + k0 + 32 * u);
-        if (NMAT == 2) wu[u] = *reinterpret_cast<const bf16x8_t*>(bu + k0 + 32 * u);
+        w0[u] = *reinterpret_cast<const bf16x8_t*>(bs0 + k0 + 32 * u);
+        w1[u] = *reinterpret_cast<const bf16x8_t*>(bs1 + k0 + 32 * u);
         a0[u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);  // first row block: loaded with the weights
       }
 #pragma unroll
@@ -567,35 +577,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
         for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
           if (rb < nrb) {
             const bf16x8_t a = rb == 0 ? a0[u] : *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0 + 32 * u);
-            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wg[u], acc[0][rb], 0, 0, 0);
-            if (NMAT == 2) acc[NMAT - 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wu[u], acc[NMAT - 1][rb], 0, 0, 0);
+            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0[u], acc[0][rb], 0, 0, 0);
+            acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1[u], acc[1][rb], 0, 0, 0);
           }
         }
       }
     }
     for (; k0 < K; k0 += 32) {
-      const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(bg + k0);
-      const bf16x8_t u = NMAT == 2 ? *reinterpret_cast<const bf16x8_t*>(bu + k0) : g;
+      const bf16x8_t w0 = *reinterpret_cast<const bf16x8_t*>(bs0 + k0);
+      const bf16x8_t w1 = *reinterpret_cast<const bf16x8_t*>(bs1 + k0);
 #pragma unroll
       for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
         if (rb < nrb) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0);
-          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, g, acc[0][rb], 0, 0, 0);
-          if (NMAT == 2) acc[NMAT - 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, u, acc[NMAT - 1][rb], 0, 0, 0);
+          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0, acc[0][rb], 0, 0, 0);
+          acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1, acc[1][rb], 0, 0, 0);
         }
       }
     }
     // 16x16 layout: lane -> weight row (column of the output) lane & 15,
     // register i -> token row 4*(lane/16) + i of the row block
-    const int col = col0 + (lane & 15);
 #pragma unroll
     for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = m0 + rb * 16 + 4 * (lane >> 4) + i;
-        if (rb < nrb && r < seg_n && col < N) {
-          const float v = NMAT == 2 ? silu(acc[0][rb][i]) * acc[NMAT - 1][rb][i] : acc[0][rb][i];
-          C[size_t(seg0 + r) * N + col] = f32_to_bf16(v);
+        if (rb < nrb && r < seg_n) {
+          bf16_t* crow = C + size_t(seg0 + r) * N;
+          if (NMAT == 2) {
+            const int col = col0 + (lane & 15);
+            if (col < N) crow[col] = f32_to_bf16(silu(acc[0][rb][i]) * acc[1][rb][i]);
+          } else {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              const int col = col0 + 16 * s + (lane & 15);
+              if (col < N) crow[col] = f32_to_bf16(acc[s][rb][i]);
+            }
+          }
         }
       }
     }
@@ -605,7 +623,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                   bf16_t* C, int L, int N, int K, hipStream_t s) {
-  const dim3 grid(unsigned((N + kColsPerBlock - 1) / kColsPerBlock), unsigned(L));
+  const dim3 grid(unsigned((N + cols_per_block<NMAT>() - 1) / cols_per_block<NMAT>()), unsigned(L));
   MOE_LAUNCH(name, gemm_kernel<NMAT>, grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K);
   return MOE_OK;
 }

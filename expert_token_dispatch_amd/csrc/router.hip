@@ -241,18 +241,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   // ---- sum the slices in order, add the bias, keep the tile in LDS
   if ((E & 3) == 0) {
     const int n4 = n >> 2;
-#pragma unroll 4
-    for (int i = tid; i < n4; i += kTopkThreads) {
-      f32x4_t v = reinterpret_cast<const f32x4_t*>(base)[i];
-      for (int sl = 1; sl < nslice; ++sl) v += reinterpret_cast<const f32x4_t*>(base + sl * slice_stride)[i];
-      const int m = (4 * i) / E, e = 4 * i - m * E;
-      if (br != nullptr) {
+    // four float4s per thread per round, their slices' loads issued together and added in slice order
+    for (int i0 = tid; i0 < n4; i0 += 4 * kTopkThreads) {
+      f32x4_t v[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] += br[e + c];
+      for (int c = 0; c < 4; ++c) {
+        const int i = i0 + c * kTopkThreads;
+        if (i < n4) v[c] = reinterpret_cast<const f32x4_t*>(base)[i];
       }
-      if (logits_out != nullptr) reinterpret_cast<f32x4_t*>(logits_out + size_t(t0) * E)[i] = v;
+      for (int s0 = 1; s0 < nslice; s0 += 4) {
+        f32x4_t t[4][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) lg[m * ld + e + c] = v[c];
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + c * kTopkThreads;
+            if (i < n4 && s0 + u < nslice) t[c][u] = reinterpret_cast<const f32x4_t*>(base + (s0 + u) * slice_stride)[i];
+          }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i0 + c * kTopkThreads < n4 && s0 + u < nslice) v[c] += t[c][u];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = i0 + c * kTopkThreads;
+        if (i >= n4) continue;
+        const int m = (4 * i) / E, e = 4 * i - m * E;
+        if (br != nullptr) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[c][q] += br[e + q];
+        }
+        if (logits_out != nullptr) reinterpret_cast<f32x4_t*>(logits_out + size_t(t0) * E)[i] = v[c];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lg[m * ld + e + q] = v[c][q];
+      }
     }
   } else {
     for (int i = tid; i < n; i += kTopkThreads) {
@@ -354,15 +378,22 @@ Split plan(const moe_layer_desc* d) {
   Split s;
   const int E = d->num_experts, H = d->hidden;
   const int e16 = (E + 15) / 16 * 16;
-  const int g = e16 < kMaxGroup ? e16 : kMaxGroup;
+  const int64_t tiles = (d->num_tokens + kTok - 1) / kTok;
+  // widest expert group that still leaves a few hundred blocks (narrower groups re-read the
+  // token tile once per group, which only small batches can afford)
+  int g = e16 < kMaxGroup ? e16 : kMaxGroup;
+  while (g > 16 && tiles * ((E + g - 1) / g) * 4 < 256) g /= 2;
+  g = (g + 15) / 16 * 16;
   s.neb = g / 16;
   s.groups = (E + g - 1) / g;
-  const int64_t tiles = (d->num_tokens + kTok - 1) / kTok;
   const int step = RouterMma<T>::kStepK;
   const int nsteps = (H + step - 1) / step;
-  // enough blocks to keep every CU streaming, but each slice at least 4 chunks deep
+  // enough blocks to keep every CU streaming, but each slice at least 4 chunks deep, and no
+  // more than 128 KB of partial logits for one top-k block to add up
   int slices = 1;
-  while (tiles * s.groups * slices < 512 && nsteps / (slices * 2) >= 4) slices *= 2;
+  while (tiles * s.groups * slices < 512 && nsteps / (slices * 2) >= 4 &&
+         int64_t(slices) * 2 * kTopkTok * E * int64_t(sizeof(float)) <= 128 * 1024)
+    slices *= 2;
   s.slices = slices;
   s.k_per_slice = (nsteps + slices - 1) / slices * step;
   return s;
