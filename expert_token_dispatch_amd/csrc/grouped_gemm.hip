@@ -262,28 +262,79 @@ constexpr int kXcds = 8;
 
 bool supported(int K) { return K % BK == 0; }
 
-template <int NMAT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ C, int L, int N, int K) {
-  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per tile
-  const int NT = (N + ON - 1) / ON;
+// ---- work plan -------------------------------------------------------------
+// Tiles are numbered over (expert, group of kGroupN n-tiles, m-tile, n-tile
+// in group) and dealt to the XCDs in contiguous ranges (block b runs on XCD
+// b % 8).  An XCD with q tiles runs them in rounds of `cpx` (its CU count);
+// when the last round is only partly filled and K is long, its r tiles are
+// cut into s pieces along K (s in {2, 4}, chosen to minimise the rounds the
+// pieces take, ceil(r*s/cpx)/s), so the XCD finishes in F + ceil(r*s/cpx)/s
+// tile times instead of F + 1.  Each piece writes its float32 accumulators;
+// fixup_kernel adds the pieces in piece order (so the result does not depend
+// on timing) and runs the usual epilogue.
+constexpr int kSplitMinSteps = 128;  // K/BK from which the last round is split
+constexpr int kMaxSplit = 4;
+constexpr int kMaxParts = 96;        // pieces per XCD: s = 4 needs r <= 24, s = 2 needs r <= 16
+constexpr int kMaxTail = kMaxParts / kMaxSplit;
+constexpr size_t kPartBytes = size_t(kThreads) * 256 * sizeof(float);  // one piece's accumulators
 
-  // ---- tile number -> (expert, m-tile, n-tile), all from device offsets ----
+__device__ __forceinline__ int split_of(int r, int cpx, int smax, int nk) {
+  int best = 1;
+  for (int s = 2; s <= smax; s *= 2) {
+    if (r == 0 || r > kMaxTail || nk < 16 * s || r * s > kMaxParts) break;
+    // ceil(r*s/cpx)/s < ceil(r*best/cpx)/best
+    if (((r * s + cpx - 1) / cpx) * best < ((r * best + cpx - 1) / cpx) * s) best = s;
+  }
+  return best;
+}
+
+struct Job {
+  int expert, row0, rows, n0;
+  int kb, nks;     // k steps [kb, kb + nks)
+  int part, nparts, pslot;
+};
+
+// The job of block (xcd, loc), or the tile of the XCD's u-th split tile when
+// `tail >= 0`.  Returns false when the block has nothing to do.
+__device__ __forceinline__ bool plan_job(const int32_t* __restrict__ offsets, int L, int NT, int nk, int cpx, int smax,
+                                         int xcd, int loc, int tail, Job& jb) {
   int mt_total = 0;
   for (int i = 0; i < L; ++i) mt_total += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
   const int R = mt_total * NT;
-  const int id = blockIdx.x;
-  if (id >= R) return;
-  const int xcd = id % kXcds, loc = id / kXcds;
   const int q = R / kXcds, rr = R % kXcds;
-  int t = xcd * q + min(xcd, rr) + loc;
-  int expert = 0, seg0 = 0, seg_n = 0, mt_e = 0;
+  const int qx = q + (xcd < rr ? 1 : 0);
+  const int base = xcd * q + min(xcd, rr);
+  const int F = qx / cpx, r = qx - F * cpx;
+  const int s = split_of(r, cpx, smax, nk);
+  int t;
+  if (tail >= 0) {
+    if (s == 1 || tail >= r) return false;
+    t = base + F * cpx + tail;
+    jb.part = 0;
+    jb.nparts = s;
+    jb.pslot = xcd * kMaxParts + tail * s;
+  } else if (loc < F * cpx || s == 1) {
+    if (loc >= qx) return false;
+    t = base + loc;
+    jb.part = 0;
+    jb.nparts = 1;
+    jb.pslot = 0;
+  } else {
+    const int v = loc - F * cpx;
+    if (v >= r * s) return false;
+    const int u = v / s;
+    t = base + F * cpx + u;
+    jb.part = v - u * s;
+    jb.nparts = s;
+    jb.pslot = xcd * kMaxParts + v;
+  }
+  int seg0 = 0, seg_n = 0, mt_e = 0;
+  jb.expert = 0;
   for (int i = 0; i < L; ++i) {
     const int a = offsets[i], b = offsets[i + 1];
     const int m = (b - a + BM - 1) / BM;
     if (t < m * NT) {
-      expert = i;
+      jb.expert = i;
       seg0 = a;
       seg_n = b - a;
       mt_e = m;
@@ -297,10 +348,78 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   const int gsz = min(kGroupN, NT - ng * kGroupN);
   const int mt = rem / gsz;
   const int nt = ng * kGroupN + (rem - mt * gsz);
-  const int row0 = seg0 + mt * BM;
-  const int rows = min(BM, seg_n - mt * BM);
-  const int n0 = nt * ON;
-  const size_t boff = size_t(expert) * N * K;
+  jb.row0 = seg0 + mt * BM;
+  jb.rows = min(BM, seg_n - mt * BM);
+  jb.n0 = nt;  // n-tile index; the caller scales it by the tile's output columns
+  jb.kb = (jb.part * nk) / jb.nparts;
+  jb.nks = ((jb.part + 1) * nk) / jb.nparts - jb.kb;
+  return true;
+}
+
+// ---- epilogue.  The products were formed as (weight rows) x (token rows), so
+// in the 32x32 accumulator layout lane l holds token row l & 31 and register
+// 4q+u holds output column 8q + 4*(l/32) + u: four adjacent columns per q.
+// Each wave converts its part of the tile to bf16 (SwiGLU first for gate/up)
+// and parks it in LDS, rows padded by 16 bytes; then every thread copies
+// 16-byte row chunks out, so each store instruction writes whole 256-byte row
+// pieces.  The caller has made sure no wave still reads the loop's LDS stages.
+template <int NMAT>
+__device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_t* __restrict__ C, int row0, int rows,
+                                         int n0, int N) {
+  constexpr int TC = NMAT == 2 ? BNE / 2 : BNE;  // output columns of the tile
+  constexpr int RS = stage_row_bytes<NMAT>();
+  constexpr int NJ = NMAT == 2 ? 2 : 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1, fr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rt = wm * 128 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + 2][4 * q + u] : acc[i][j][4 * q + u];
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        pk.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
+        *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  block_barrier();
+  constexpr int CPR = TC / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int u = 0; u < BM * CPR / kThreads; ++u) {
+    const int id = tid + kThreads * u;
+    const int r = id / CPR, c = id % CPR;
+    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
+    // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
+    if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(C + size_t(row0 + r) * N + n0 + c * 8) = val;
+  }
+}
+
+// A piece's accumulators, thread-major: float4 number v of thread t at (v*256 + t)
+__device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslot) {
+  return reinterpret_cast<f32x4_t*>(parts + size_t(pslot) * (kPartBytes / sizeof(float)));
+}
+
+template <int NMAT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+                                                        bf16_t* __restrict__ C, int L, int N, int K, int cpx, int smax,
+                                                        float* __restrict__ parts) {
+  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per tile
+  const int NT = (N + ON - 1) / ON;
+  const int nk = K / BK;
+  Job jb;
+  if (!plan_job(offsets, L, NT, nk, cpx, smax, blockIdx.x % kXcds, blockIdx.x / kXcds, -1, jb)) return;
+  const int row0 = jb.row0, rows = jb.rows, n0 = jb.n0 * ON, kb = jb.kb, nks = jb.nks;
+  const size_t boff = size_t(jb.expert) * N * K;
   const bf16_t* Bg = B0 + boff;
   const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
 
@@ -329,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 #define MOE_ISSUE(kt_)                                                                                      \
   do {                                                                                                      \
     char* sa_ = lds + ((kt_) % kStages) * kStage + (8 * wave) * 1024;                                       \
-    const int k0_ = (kt_) * BK;                                                                             \
+    const int k0_ = (kb + (kt_)) * BK;                                                                      \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                         \
       const int cc_ = (j & 1) ? c_odd : c_even;                                                             \
       const int ar_ = min(lrow + 8 * j, rows - 1); /* rows past the segment repeat its last row */          \
@@ -387,9 +506,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     }                                                                                                     \
   } while (0)
 
-  const int nk = K / BK;
   MOE_ISSUE(0);
-  if (nk > 1) {
+  if (nks > 1) {
     MOE_ISSUE(1);
     MOE_VMCNT(16);  // stage 0 landed (16 loads per stage per wave)
   } else {
@@ -399,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   MOE_LOADF(0, lds, 0);
   // every iteration has a next stage; the refill issued in it is stage kt+2,
   // or (near the end) a repeat of the last stage into the free slot
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  for (int kt = 0; kt + 1 < nks; ++kt) {
     const char* st = lds + (kt % kStages) * kStage;
     MOE_LOADF(1, st, 1);
     MOE_MMA(0);
@@ -416,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
     MOE_LOADF(0, lds + ((kt + 1) % kStages) * kStage, 0);
-    MOE_ISSUE(min(kt + 2, nk - 1));
+    MOE_ISSUE(min(kt + 2, nks - 1));
     MOE_MMA(1);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
@@ -426,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     }
   }
   {
-    const char* st = lds + ((nk - 1) % kStages) * kStage;
+    const char* st = lds + ((nks - 1) % kStages) * kStage;
     MOE_LOADF(1, st, 1);
     MOE_MMA(0);
     MOE_LOADF(0, st, 2);
@@ -441,64 +559,114 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 #undef MOE_MMA
 #undef MOE_PIPE_DS
 
-  // ---- epilogue.  The products were formed as (weight rows) x (token rows),
-  // so in the 32x32 accumulator layout lane l holds token row l & 31 and
-  // register 4q+u holds output column 8q + 4*(l/32) + u: four adjacent columns
-  // per q.  Each wave converts its part of the tile to bf16 (SwiGLU first for
-  // gate/up) and parks it in LDS, rows padded by 16 bytes; then every thread
-  // copies 16-byte row chunks out, so each store instruction writes whole
-  // 256-byte row pieces.
-  constexpr int TC = NMAT == 2 ? BNE / 2 : BNE;  // output columns of the tile
-  constexpr int RS = stage_row_bytes<NMAT>();
-  constexpr int NJ = NMAT == 2 ? 2 : 4;
-  MOE_LGKMCNT0();
-  block_barrier();  // every wave is done reading the last stage
+  if (jb.nparts > 1) {
+    // one piece of a split tile: park the accumulators for fixup_kernel
+    f32x4_t* dst = part_ptr(parts, jb.pslot);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rt = wm * 128 + i * 32 + fr;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + 2][4 * q + u] : acc[i][j][4 * q + u];
-        uint2 pk;
-        pk.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-        pk.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
-        const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
-        *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
-      }
-    }
+        for (int c = 0; c < 4; ++c)
+          dst[((i * 4 + j) * 4 + c) * kThreads + tid] =
+              f32x4_t{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+    return;
   }
   MOE_LGKMCNT0();
-  block_barrier();
-  constexpr int CPR = TC / 8;  // 16-byte chunks per row
+  block_barrier();  // every wave is done reading the last stage
+  epilogue<NMAT>(acc, lds, C, row0, rows, n0, N);
+}
+
+// Adds the pieces of each split tile in piece order and writes the tile.
+// kFixSub blocks share a tile; an item is one float4 of the accumulator
+// layout (thread t, float4 v: i = v/16, j = v/4 % 4, q = v % 4), that is four
+// adjacent output columns of one token row (for gate/up: the gate float4 and
+// its up partner j + 2).
+constexpr int kFixSub = 8;
+
+template <int NMAT>
+__global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
+                                                         int L, int N, int K, int cpx, int smax,
+                                                         const float* __restrict__ parts) {
+  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
+  constexpr int NV = NMAT == 2 ? 32 : 64;                 // output float4s per thread of the tile
+  constexpr int kPer = NV * kThreads / (kFixSub * kThreads);  // items per thread of this block
+  const int NT = (N + ON - 1) / ON;
+  const int sub = blockIdx.x % kFixSub, tile = blockIdx.x / kFixSub;
+  Job jb;
+  if (!plan_job(offsets, L, NT, K / BK, cpx, smax, tile % kXcds, 0, tile / kXcds, jb)) return;
+  const int n0 = jb.n0 * ON;
+  const size_t pstride = kPartBytes / sizeof(f32x4_t);  // float4s per piece
+  const f32x4_t* base = reinterpret_cast<const f32x4_t*>(parts) + size_t(jb.pslot) * pstride;
 #pragma unroll
-  for (int u = 0; u < BM * CPR / kThreads; ++u) {
-    const int id = tid + kThreads * u;
-    const int r = id / CPR, c = id % CPR;
-    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
-    // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
-    if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(C + size_t(row0 + r) * N + n0 + c * 8) = val;
+  for (int it = 0; it < kPer; ++it) {
+    const int item = (sub * kPer + it) * kThreads + threadIdx.x;  // consecutive threads: consecutive float4s
+    const int t = item % kThreads, w = item / kThreads;
+    // w -> (i, j, q) of the gate (or plain) float4
+    const int i = NMAT == 2 ? w / 8 : w / 16;
+    const int j = NMAT == 2 ? (w / 4) % 2 : (w / 4) % 4;
+    const int q = w % 4;
+    const int v = (i * 4 + j) * 4 + q;
+    f32x4_t s = base[size_t(v) * kThreads + t];
+    f32x4_t su = NMAT == 2 ? base[size_t(v + 8) * kThreads + t] : s;  // up partner: j + 2
+    for (int p = 1; p < jb.nparts; ++p) {
+      s += base[size_t(p) * pstride + size_t(v) * kThreads + t];
+      if (NMAT == 2) su += base[size_t(p) * pstride + size_t(v + 8) * kThreads + t];
+    }
+    const int wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 1, wn = wave & 1, fr = lane & 31, g = lane >> 5;
+    const int rt = wm * 128 + i * 32 + fr;
+    const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
+    if (rt < jb.rows && n0 + cl < N) {
+      float o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = NMAT == 2 ? silu(s[u]) * su[u] : s[u];
+      uint2 pk;
+      pk.x = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
+      pk.y = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+      *reinterpret_cast<uint2*>(C + size_t(jb.row0 + rt) * N + n0 + cl) = pk;
+    }
   }
 }
 #undef MOE_VMCNT
 #undef MOE_LGKMCNT0
 
+int cus_per_xcd() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds) n = 256;
+    cached[dev] = n / kXcds;
+  }
+  return cached[dev];
+}
+
+// K long enough for the split of a partly filled last round
+bool splits(int K) { return K / BK >= kSplitMinSteps; }
+
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, int64_t max_pairs, hipStream_t s) {
+                  bf16_t* C, int L, int N, int K, int64_t max_pairs, float* parts, hipStream_t s) {
   auto kern = gemm_kernel<NMAT>;
   constexpr size_t lds = lds_bytes<NMAT>();
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     int(lds));
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
-  const int64_t mslots = (max_pairs + BM - 1) / BM + L;
-  const int64_t grid = mslots * ((N + ON - 1) / ON);
-  MOE_LAUNCH(name, kern, dim3(unsigned(grid)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K);
+  const int cpx = cus_per_xcd();
+  const int smax = splits(K) && parts != nullptr ? kMaxSplit : 1;
+  // every XCD's range holds at most ceil(R/8) tiles; splitting adds at most kMaxParts - kMaxTail blocks
+  const int64_t tiles = ((max_pairs + BM - 1) / BM + L) * ((N + ON - 1) / ON);
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds + (smax > 1 ? kMaxParts - kMaxTail : 0);
+  MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K, cpx,
+             smax, parts);
+  if (smax > 1) {
+    const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
+    MOE_LAUNCH(fname, fixup_kernel<NMAT>, dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s, offsets, C,
+               L, N, K, cpx, smax, static_cast<const float*>(parts));
+  }
   return MOE_OK;
 }
 
@@ -644,29 +812,18 @@ moe_status launch_t(const FfnArgs& a) {
   return MOE_OK;
 }
 
-}  // namespace
+// large tiles pay off once segments hold a few hundred rows; decode-sized
+// batches (a handful of rows per expert) take the skinny kernel
+bool use_big(const moe_layer_desc* d, int64_t max_pairs) {
+  return d->dtype == MOE_BF16 && max_pairs >= int64_t(128) * d->local_count && big::supported(d->hidden) &&
+         big::supported(d->intermediate);
+}
 
-moe_status launch_grouped_ffn(const FfnArgs& a) {
-  if (a.max_pairs <= 0) return MOE_OK;
+moe_status launch_small(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
-  // large tiles pay off once segments hold a few hundred rows; decode-sized
-  // batches (a handful of rows per expert) keep the 128-row tiles
-  if (d->dtype == MOE_BF16 && a.max_pairs >= int64_t(128) * d->local_count && big::supported(d->hidden) &&
-      big::supported(d->intermediate)) {
-    const int L = d->local_count, H = d->hidden, I = d->intermediate;
-    const bf16_t* x = static_cast<const bf16_t*>(a.x_sorted);
-    bf16_t* h = static_cast<bf16_t*>(a.h);
-    moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
-                                   static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, a.s);
-    if (st != MOE_OK) return st;
-    return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
-                          static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I,
-                          a.max_pairs, a.s);
-  }
+  const int L = d->local_count, H = d->hidden, I = d->intermediate;
   // decode-sized batches: a few rows per expert, bound by streaming the weights
-  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * d->local_count && skinny::supported(d->hidden) &&
-      skinny::supported(d->intermediate)) {
-    const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I)) {
     bf16_t* h = static_cast<bf16_t*>(a.h);
     moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
                                       static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
@@ -676,6 +833,28 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
                              static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.s);
   }
   return d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
+}
+
+}  // namespace
+
+size_t ffn_parts_bytes(const moe_layer_desc* d, int64_t max_pairs) {
+  if (!use_big(d, max_pairs) || !(big::splits(d->hidden) || big::splits(d->intermediate))) return 0;
+  return size_t(big::kXcds) * big::kMaxParts * big::kPartBytes;
+}
+
+moe_status launch_grouped_ffn(const FfnArgs& a) {
+  if (a.max_pairs <= 0) return MOE_OK;
+  const moe_layer_desc* d = a.d;
+  if (!use_big(d, a.max_pairs)) return launch_small(a);
+  const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  const bf16_t* x = static_cast<const bf16_t*>(a.x_sorted);
+  bf16_t* h = static_cast<bf16_t*>(a.h);
+  moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
+                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, a.parts, a.s);
+  if (st != MOE_OK) return st;
+  return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
+                        static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.max_pairs,
+                        a.parts, a.s);
 }
 
 }  // namespace moe
