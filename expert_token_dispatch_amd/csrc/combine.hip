@@ -21,12 +21,14 @@ namespace {
 
 constexpr int kTokensPerBlock = 4;
 
-template <typename T>
+// KB: slots whose rows are loaded together (k rounded up to 2, 4 or 8; larger k goes in batches of 8);
+// each lane takes kSlices 16-byte slices of the row per pass, so KB * kSlices loads are in flight
+template <typename T, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ ys, const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ tw, int64_t ntok, int k, int vec_per_row,
                                                       uint4* __restrict__ y) {
   constexpr int EPV = 16 / int(sizeof(T));
-  constexpr int kBatch = 8;  // slots whose rows are in flight together
+  constexpr int kSlices = KB <= 2 ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
@@ -34,49 +36,71 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   const int my_row = lane < k ? pair_row[t * k + lane] : -1;
   const float my_w = lane < k ? tw[t * k + lane] : 0.0f;
   uint4* dst = y + size_t(t) * vec_per_row;
-  for (int c = lane; c < vec_per_row; c += 64) {
-    float acc[EPV];
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(ys);
+  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
+    float acc[kSlices][EPV];
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
-    for (int j0 = 0; j0 < k; j0 += kBatch) {
-      u32x4_t v[kBatch];
+    for (int u = 0; u < kSlices; ++u)
 #pragma unroll
-      for (int jj = 0; jj < kBatch; ++jj) {
+      for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      u32x4_t v[kSlices][KB];
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
         const int r = __shfl(my_row, j0 + jj, 64);
-        if (j0 + jj < k && r >= 0) v[jj] = reinterpret_cast<const u32x4_t*>(ys)[size_t(r) * vec_per_row + c];
+#pragma unroll
+        for (int u = 0; u < kSlices; ++u) {
+          const int c = c0 + 64 * u;
+          if (j0 + jj < k && r >= 0 && c < vec_per_row) v[u][jj] = src[size_t(r) * vec_per_row + c];
+        }
       }
       // accumulate in slot order
 #pragma unroll
-      for (int jj = 0; jj < kBatch; ++jj) {
+      for (int jj = 0; jj < KB; ++jj) {
         const int r = __shfl(my_row, j0 + jj, 64);
         const float wj = __shfl(my_w, j0 + jj, 64);
         if (j0 + jj < k && r >= 0) {
-          float f[EPV];
-          unpack16(make_uint4(v[jj][0], v[jj][1], v[jj][2], v[jj][3]), T(), f);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wj, f[e], acc[e]);
+          for (int u = 0; u < kSlices; ++u) {
+            float f[EPV];
+            unpack16(make_uint4(v[u][jj][0], v[u][jj][1], v[u][jj][2], v[u][jj][3]), T(), f);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[u][e] = fmaf(wj, f[e], acc[u][e]);
+          }
         }
       }
     }
-    dst[c] = pack16(acc, T());
+#pragma unroll
+    for (int u = 0; u < kSlices; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < vec_per_row) dst[c] = pack16(acc[u], T());
+    }
   }
+}
+
+template <typename T>
+moe_status launch_t(const CombineArgs& a) {
+  const moe_layer_desc* d = a.d;
+  const int64_t T_ = d->num_tokens;
+  const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
+  const dim3 grid(unsigned((T_ + kTokensPerBlock - 1) / kTokensPerBlock));
+  const int k = d->top_k;
+  const uint4* ys = static_cast<const uint4*>(a.y_sorted);
+  uint4* y = static_cast<uint4*>(a.y);
+  if (k <= 2) {
+    MOE_LAUNCH("combine", (combine_kernel<T, 2>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k, vec_per_row, y);
+  } else if (k <= 4) {
+    MOE_LAUNCH("combine", (combine_kernel<T, 4>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k, vec_per_row, y);
+  } else {
+    MOE_LAUNCH("combine", (combine_kernel<T, 8>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k, vec_per_row, y);
+  }
+  return MOE_OK;
 }
 
 }  // namespace
 
 moe_status launch_combine(const CombineArgs& a) {
-  const moe_layer_desc* d = a.d;
-  const int64_t T = d->num_tokens;
-  const int vec_per_row = int(size_t(d->hidden) * dtype_bytes(d->dtype) / 16);
-  const dim3 grid(unsigned((T + kTokensPerBlock - 1) / kTokensPerBlock));
-  if (d->dtype == MOE_BF16) {
-    MOE_LAUNCH("combine", combine_kernel<bf16_t>, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.y_sorted),
-               a.pair_row, a.topk_w, T, d->top_k, vec_per_row, static_cast<uint4*>(a.y));
-  } else {
-    MOE_LAUNCH("combine", combine_kernel<float>, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.y_sorted),
-               a.pair_row, a.topk_w, T, d->top_k, vec_per_row, static_cast<uint4*>(a.y));
-  }
-  return MOE_OK;
+  return a.d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
 
 }  // namespace moe

@@ -29,7 +29,10 @@
 //             (register, wave) slots;
 //   place     without a capacity cut, scatter and row copy in one kernel:
 //             ranks as in scatter, then token-major copies (one read of x[t],
-//             one write per kept local pair, 16-byte vectors);
+//             one write per kept local pair, 16-byte vectors); when the chunk
+//             histogram table is small (chunks x experts <= 16384) every place
+//             block also sums the columns it needs itself, so no scan launch
+//             sits between the router and the copy;
 //   gather    with a capacity cut, the same token-major copy after it.
 #include "common.h"
 #include "kernels.h"
@@ -469,9 +472,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__
 // rows of its quarter of the chunk's tokens, token-major (one read of x[t],
 // one write per kept local pair).
 constexpr int kPlaceSplit = 4;
+// With few chunks and experts the place blocks find their own bases: every
+// block sums the chunk histograms it needs (no separate scan launch).
+constexpr int kFuseEntries = 16384;  // nblk * E up to which the scan is folded in
 
+// FUSED: run[i] = (pairs of local experts before i) + (pairs of local expert i
+// in earlier chunks), from the chunk histograms; block 0 also writes counts,
+// offsets and the (zero) drop count.  Otherwise blk_base holds them.
+template <bool FUSED>
 __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* __restrict__ ids, int64_t ntok, int k,
                                                                  int begin, int L, const int32_t* __restrict__ blk_base,
+                                                                 const int32_t* __restrict__ blk_all, int nblk, int E,
+                                                                 int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                                 int64_t* __restrict__ num_dropped,
                                                                  int32_t* __restrict__ sorted_pairs,
                                                                  int32_t* __restrict__ pair_row,
                                                                  const u32x4_t* __restrict__ x, int vec_per_row,
@@ -488,7 +501,65 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
   const int np = ntk * k;
   const int64_t p0 = t0 * k;
 
-  for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
+  if (FUSED) {
+    // per local expert i: total over all chunks and over the chunks before this one;
+    // run[i] = (exclusive scan of the totals)[i] + (this expert's pairs in earlier chunks).
+    // Experts in groups of up to 256; within a group, thread t takes expert t % Lg and
+    // every G-th chunk row from t / Lg (rows read coalesced), partial sums meet in LDS.
+    __shared__ int wsum[kWaves];
+    __shared__ int ptot[kDispatchThreads], pbef[kDispatchThreads];
+    int carry = 0;
+    for (int i0 = 0; i0 < L; i0 += kDispatchThreads) {
+      const int Lg = min(kDispatchThreads, L - i0);
+      const int G = kDispatchThreads / Lg;
+      const int il = tid % Lg, g = tid / Lg;
+      int tot = 0, before = 0;
+      if (g < G) {
+        const int32_t* col = blk_all + begin + i0 + il;
+        for (int b = g; b < nblk; b += G) {
+          const int c = col[size_t(b) * E];
+          tot += c;
+          before += b < chunk ? c : 0;
+        }
+      }
+      ptot[tid] = tot;
+      pbef[tid] = before;
+      __syncthreads();
+      tot = 0;
+      before = 0;
+      if (tid < Lg) {
+        for (int gg = 0; gg < G; ++gg) {
+          tot += ptot[gg * Lg + tid];
+          before += pbef[gg * Lg + tid];
+        }
+      }
+      int all;
+      const int ex = carry + block_exclusive_scan(tid < Lg ? tot : 0, wsum, &all);
+      if (tid < Lg) {
+        run[i0 + tid] = ex + before;
+        if (blockIdx.x == 0) {
+          offsets[i0 + tid] = ex;
+          counts[begin + i0 + tid] = tot;
+        }
+      }
+      carry += all;
+    }
+    if (blockIdx.x == 0) {
+      if (tid == 0) {
+        offsets[L] = carry;
+        if (num_dropped != nullptr) *num_dropped = 0;
+      }
+      // experts outside the local range (their totals were not needed above)
+      for (int e = tid; e < E; e += kDispatchThreads) {
+        if (e >= begin && e < begin + L) continue;
+        int tot = 0;
+        for (int b = 0; b < nblk; ++b) tot += blk_all[size_t(b) * E + e];
+        counts[e] = tot;
+      }
+    }
+  } else {
+    for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
+  }
   for (int q = tid; q < kWaves * L; q += kDispatchThreads) cnt[q] = 0;
   __syncthreads();
   const int bits = bits_for(L);
@@ -571,8 +642,12 @@ moe_status launch_dispatch(const DispatchArgs& a) {
     MOE_LAUNCH("dispatch_count", count_kernel, dim3(nblk), dim3(kDispatchThreads), size_t(E) * 4, a.s, a.topk_ids, n, E,
                chunk, a.scr.blk_all);
   }
-  MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all, nblk,
-             E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.num_dropped);
+  // without a capacity cut and with a small chunk-histogram table the place kernel finds its own bases
+  const bool fused = !cap && int64_t(nblk) * E <= kFuseEntries;
+  if (!fused) {
+    MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all,
+               nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.num_dropped);
+  }
   if (cap) {
     const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
     MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
@@ -584,14 +659,16 @@ moe_status launch_dispatch(const DispatchArgs& a) {
                d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
   } else {
     const size_t lds = (size_t(L) * (1 + kDispatchThreads / 64) + size_t(chunk)) * 4;
+    auto kern = fused ? place_kernel<true> : place_kernel<false>;
     if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(place_kernel),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
       if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_place: LDS attribute: %s", hipGetErrorString(e));
     }
-    MOE_LAUNCH("dispatch_place", place_kernel, dim3(unsigned(nblk) * kPlaceSplit), dim3(kDispatchThreads), lds, a.s,
-               a.topk_ids, d->num_tokens, d->top_k, begin, L, a.scr.blk_base, a.sorted_pairs, a.pair_row,
-               static_cast<const u32x4_t*>(a.x), vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
+    MOE_LAUNCH("dispatch_place", kern, dim3(unsigned(nblk) * kPlaceSplit), dim3(kDispatchThreads), lds, a.s,
+               a.topk_ids, d->num_tokens, d->top_k, begin, L, a.scr.blk_base, a.scr.blk_all, nblk, E, a.counts,
+               a.offsets, a.num_dropped, a.sorted_pairs, a.pair_row, static_cast<const u32x4_t*>(a.x), vec_per_row,
+               static_cast<u32x4_t*>(a.x_sorted));
   }
   return MOE_OK;
 }
