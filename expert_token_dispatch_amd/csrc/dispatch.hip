@@ -68,6 +68,19 @@ namespace {
 
 __device__ __forceinline__ int bits_for(int maxval) { return 32 - __clz(maxval); }
 
+// Sum of col[b * stride] for b = b_lo, b_lo + step, ... < b_hi, eight loads in flight
+// (integer sums: the grouping does not change the result).
+__device__ __forceinline__ int column_sum(const int32_t* __restrict__ col, size_t stride, int b_lo, int b_hi, int step) {
+  int s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int b = b_lo;
+  for (; b + 7 * step < b_hi; b += 8 * step) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] += col[size_t(b + u * step) * stride];
+  }
+  for (; b < b_hi; b += step) s[0] += col[size_t(b) * stride];
+  return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
 // Exclusive scan over the block; *total receives the block sum.  `wsum` holds
 // one int per wave.  Every thread of the block must call it.
 __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
@@ -137,8 +150,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     int sum = 0;
     if (g < G) {
       const int b_lo = min(nblk, g * per), b_hi = min(nblk, b_lo + per);
-      const int32_t* col = blk_all + c0 + e;
-      for (int b = b_lo; b < b_hi; ++b) sum += col[size_t(b) * E];
+      sum = column_sum(blk_all + c0 + e, size_t(E), b_lo, b_hi, 1);
       rsum[tid] = sum;
     }
     __syncthreads();
@@ -197,8 +209,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     const bool act = g < G;
     const int b_lo = act ? min(nblk, g * per) : 0, b_hi = act ? min(nblk, b_lo + per) : 0;
     const int32_t* col = blk_all + begin + c0 + i;
-    int s = 0;
-    for (int b = b_lo; b < b_hi; ++b) s += col[size_t(b) * E];
+    const int s = act ? column_sum(col, size_t(E), b_lo, b_hi, 1) : 0;
     if (act) rsum[tid] = s;
     __syncthreads();
     if (act) {
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__
 constexpr int kPlaceSplit = 4;
 // With few chunks and experts the place blocks find their own bases: every
 // block sums the chunk histograms it needs (no separate scan launch).
-constexpr int kFuseEntries = 16384;  // nblk * E up to which the scan is folded in
+constexpr int kFuseEntries = 16384;  // chunks x experts up to which the scan is folded in
 
 // FUSED: run[i] = (pairs of local experts before i) + (pairs of local expert i
 // in earlier chunks), from the chunk histograms; block 0 also writes counts,
@@ -515,12 +526,11 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
       const int il = tid % Lg, g = tid / Lg;
       int tot = 0, before = 0;
       if (g < G) {
+        // chunks g, g + G, ...: those before this chunk, then the rest
         const int32_t* col = blk_all + begin + i0 + il;
-        for (int b = g; b < nblk; b += G) {
-          const int c = col[size_t(b) * E];
-          tot += c;
-          before += b < chunk ? c : 0;
-        }
+        const int split = g < chunk ? g + (chunk - g + G - 1) / G * G : g;  // first of this group's chunks >= chunk
+        before = column_sum(col, size_t(E), g, min(split, nblk), G);
+        tot = before + column_sum(col, size_t(E), split, nblk, G);
       }
       ptot[tid] = tot;
       pbef[tid] = before;
@@ -549,12 +559,23 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
         offsets[L] = carry;
         if (num_dropped != nullptr) *num_dropped = 0;
       }
-      // experts outside the local range (their totals were not needed above)
-      for (int e = tid; e < E; e += kDispatchThreads) {
-        if (e >= begin && e < begin + L) continue;
+      // experts outside the local range (their totals were not needed above), grouped like the local ones
+      for (int e0 = 0; e0 < E; e0 += kDispatchThreads) {
+        const int Eg = min(kDispatchThreads, E - e0);
+        const int G = kDispatchThreads / Eg;
+        const int el = tid % Eg, g = tid / Eg;
+        const int e = e0 + el;
+        const bool outside = e < begin || e >= begin + L;
         int tot = 0;
-        for (int b = 0; b < nblk; ++b) tot += blk_all[size_t(b) * E + e];
-        counts[e] = tot;
+        if (g < G && outside) tot = column_sum(blk_all + e, size_t(E), g, nblk, G);
+        __syncthreads();
+        ptot[tid] = tot;
+        __syncthreads();
+        if (tid < Eg && (e0 + tid < begin || e0 + tid >= begin + L)) {
+          int s = 0;
+          for (int gg = 0; gg < G; ++gg) s += ptot[gg * Eg + tid];
+          counts[e0 + tid] = s;
+        }
       }
     }
   } else {
