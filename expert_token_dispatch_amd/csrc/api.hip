@@ -107,7 +107,7 @@ struct LayerWs {
   void* dispatch;
   void* x_sorted;
   void* h;
-  float* parts;
+  void* ffn_scratch;
   void* y_sorted;
   size_t bytes;
 };
@@ -136,8 +136,8 @@ LayerWs layer_layout(const moe_layer_desc* d, void* base) {
   w.dispatch = take(dispatch_scratch_bytes(d));
   w.x_sorted = take(size_t(pm) * d->hidden * dt);
   w.h = take(size_t(pm) * d->intermediate * dt);
-  const size_t pb = ffn_parts_bytes(d, pm);
-  w.parts = static_cast<float*>(pb ? take(pb) : nullptr);
+  const size_t fb = ffn_scratch_bytes(d, pm);
+  w.ffn_scratch = fb ? take(fb) : nullptr;
   w.y_sorted = take(size_t(pm) * d->hidden * dt);
   w.bytes = o;
   return w;
@@ -152,7 +152,7 @@ size_t stage_bytes(const moe_layer_desc* d, int32_t stage) {
     case MOE_STAGE_DISPATCH:
       return dispatch_scratch_bytes(d);
     case MOE_STAGE_FFN:
-      return ffn_h_bytes(d) + align_up(ffn_parts_bytes(d, max_pairs_of(d)), 256);
+      return ffn_h_bytes(d) + align_up(ffn_scratch_bytes(d, max_pairs_of(d)), 256);
     case MOE_STAGE_LAYER:
       return layer_layout(d, nullptr).bytes;
     default:
@@ -342,9 +342,8 @@ moe_status moe_grouped_ffn(const moe_layer_desc* d, const void* x_sorted, const 
   if (d->num_tokens == 0) return MOE_OK;
   TRY(ffn_checks(x_sorted, offsets, w_gate, w_up, w_down, y_sorted));
   TRY(check_ws(d, MOE_STAGE_FFN, ws, ws_bytes));
-  float* parts = ffn_parts_bytes(d, max_pairs_of(d)) ? reinterpret_cast<float*>(static_cast<char*>(ws) + ffn_h_bytes(d))
-                                                    : nullptr;
-  FfnArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, ws, parts, max_pairs_of(d),
+  void* scratch = ffn_scratch_bytes(d, max_pairs_of(d)) ? static_cast<char*>(ws) + ffn_h_bytes(d) : nullptr;
+  FfnArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, ws, scratch, max_pairs_of(d),
             static_cast<hipStream_t>(stream)};
   return launch_grouped_ffn(a);
 }
@@ -387,7 +386,7 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
   DispatchArgs da{d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped,
                   scr, capacity_of(d), true, s};
   TRY(launch_dispatch(da));
-  FfnArgs fa{d, w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted, w.h, w.parts, max_pairs_of(d), s};
+  FfnArgs fa{d, w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted, w.h, w.ffn_scratch, max_pairs_of(d), s};
   TRY(launch_grouped_ffn(fa));
   CombineArgs ca{d, w.y_sorted, w.pair_row, tw, y, s};
   return launch_combine(ca);

@@ -243,16 +243,6 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2, kThreads = 256;
 constexpr int kRowBytes = BK * 2;              // 128
-constexpr int kStageA = BM * kRowBytes;        // 32 KB
-constexpr int kStage = kStageA + BNE * kRowBytes;
-constexpr size_t kLoopLds = size_t(kStages) * kStage;  // 128 KB
-// epilogue staging: the output tile as bf16 rows of ON columns plus 16 bytes of padding
-template <int NMAT>
-constexpr int stage_row_bytes() { return (NMAT == 2 ? BNE / 2 : BNE) * 2 + 16; }
-template <int NMAT>
-constexpr size_t lds_bytes() {
-  return kLoopLds > size_t(BM) * stage_row_bytes<NMAT>() ? kLoopLds : size_t(BM) * stage_row_bytes<NMAT>();
-}
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
 
@@ -290,87 +280,180 @@ __device__ __forceinline__ int split_of(int r, int cpx, int smax, int nk) {
 
 struct Job {
   int expert, row0, rows, n0;
+  bool wide;       // a segment's tail of at most 128 rows: 128 rows x 512 B rows (two n-tiles)
   int kb, nks;     // k steps [kb, kb + nks)
   int part, nparts, pslot;
 };
 
-// The job of block (xcd, loc), or the tile of the XCD's u-th split tile when
-// `tail >= 0`.  Returns false when the block has nothing to do.
-__device__ __forceinline__ bool plan_job(const int32_t* __restrict__ offsets, int L, int NT, int nk, int cpx, int smax,
-                                         int xcd, int loc, int tail, Job& jb) {
-  int mt_total = 0;
-  for (int i = 0; i < L; ++i) mt_total += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
-  const int R = mt_total * NT;
+// Tiles of one expert with n rows: in every group of up to kGroupN n-tiles,
+// the full 256-row m-tiles, then the tail m-tile: a regular tile per n-tile
+// when the tail has more than 128 rows, else one wide tile per two n-tiles.
+__device__ __forceinline__ int tail_tiles(int tail, int gsz) {
+  return tail == 0 ? 0 : (tail <= BM / 2 ? (gsz + 1) / 2 : gsz);
+}
+__device__ __forceinline__ int expert_tiles(int n, int NT) {
+  const int mf = n / BM, tail = n - mf * BM;
+  const int nfull = NT / kGroupN, last = NT - nfull * kGroupN;
+  return nfull * (mf * kGroupN + tail_tiles(tail, kGroupN)) + (last ? mf * last + tail_tiles(tail, last) : 0);
+}
+
+// One XCD's share of the work: tiles [base, base + qx) in rounds of cpx; the r
+// tiles of a partly filled last round are cut into s pieces (s = 1: not cut).
+struct XcdPlan {
+  int base, qx, F, r, s, units;
+};
+
+__device__ __forceinline__ XcdPlan plan_xcd(int R, int nk, int cpx, int smax, int xcd) {
+  XcdPlan xp;
   const int q = R / kXcds, rr = R % kXcds;
-  const int qx = q + (xcd < rr ? 1 : 0);
-  const int base = xcd * q + min(xcd, rr);
-  const int F = qx / cpx, r = qx - F * cpx;
-  const int s = split_of(r, cpx, smax, nk);
+  xp.qx = q + (xcd < rr ? 1 : 0);
+  xp.base = xcd * q + min(xcd, rr);
+  xp.F = xp.qx / cpx;
+  xp.r = xp.qx - xp.F * cpx;
+  xp.s = split_of(xp.r, cpx, smax, nk);
+  xp.units = xp.s == 1 ? xp.qx : xp.F * cpx + xp.r * xp.s;
+  return xp;
+}
+
+// Per-expert tile counts of both products, as exclusive prefix sums
+// (pre[0..L] for gate/up, pre[L+1..2L+1] for down), so that a GEMM block
+// finds the total and its tile's expert without walking all the offsets.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int L, int NT_gu, int NT_dn,
+                                                    int32_t* __restrict__ pre) {
+  __shared__ int wa[16], wb[16];  // per-wave totals
+  int carry_gu = 0, carry_dn = 0;
+  for (int i0 = 0; i0 < L; i0 += 1024) {
+    const int i = i0 + threadIdx.x;
+    const int n = i < L ? offsets[i + 1] - offsets[i] : 0;
+    const int a = i < L ? expert_tiles(n, NT_gu) : 0;
+    const int b = i < L ? expert_tiles(n, NT_dn) : 0;
+    // two block scans (inclusive within waves, then over the wave totals)
+    int va = a, vb = b;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int ta = __shfl_up(va, d, 64), tb = __shfl_up(vb, d, 64);
+      if (lane >= d) {
+        va += ta;
+        vb += tb;
+      }
+    }
+    if (lane == 63) {
+      wa[wave] = va;
+      wb[wave] = vb;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0, ta = 0, tb = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) {
+        ba += wa[w];
+        bb += wb[w];
+      }
+      ta += wa[w];
+      tb += wb[w];
+    }
+    if (i < L) {
+      pre[i] = carry_gu + ba + va - a;
+      pre[L + 1 + i] = carry_dn + bb + vb - b;
+    }
+    carry_gu += ta;
+    carry_dn += tb;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    pre[L] = carry_gu;
+    pre[2 * L + 1] = carry_dn;
+  }
+}
+
+// expert, rows and columns of tile t; tpre = the product's tile prefix (L + 1 entries)
+__device__ __forceinline__ void tile_of(const int32_t* __restrict__ offsets, const int32_t* tpre, int L, int NT, int t,
+                                        Job& jb) {
+  // the expert: the last i with tpre[i] <= t (experts with no tiles have tpre[i] == tpre[i+1])
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tpre[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  jb.expert = lo;
+  t -= tpre[lo];
+  const int seg0 = offsets[lo];
+  const int seg_n = offsets[lo + 1] - seg0;
+  const int mf = seg_n / BM, tl = seg_n - mf * BM;
+  const int nfull = NT / kGroupN;
+  const int per_group = mf * kGroupN + tail_tiles(tl, kGroupN);
+  int ng = t / per_group;
+  if (ng > nfull) ng = nfull;  // past the full groups: the last, partial group
+  const int rem = t - ng * per_group;
+  const int gsz = ng < nfull ? kGroupN : NT - nfull * kGroupN;
+  if (rem < mf * gsz) {
+    const int mt = rem / gsz;
+    jb.n0 = ng * kGroupN + (rem - mt * gsz);
+    jb.row0 = seg0 + mt * BM;
+    jb.rows = BM;
+    jb.wide = false;
+  } else {
+    const int r2 = rem - mf * gsz;
+    jb.row0 = seg0 + mf * BM;
+    jb.rows = tl;
+    jb.wide = tl <= BM / 2;
+    jb.n0 = ng * kGroupN + (jb.wide ? 2 * r2 : r2);
+  }
+}
+
+// Unit u of the XCD (u < xp.units): a whole tile, or one K piece of a tile of the last round.
+__device__ __forceinline__ void unit_job(const int32_t* __restrict__ offsets, const int32_t* tpre, int L, int NT, int nk,
+                                         int cpx, int xcd, const XcdPlan& xp, int u, Job& jb) {
   int t;
-  if (tail >= 0) {
-    if (s == 1 || tail >= r) return false;
-    t = base + F * cpx + tail;
-    jb.part = 0;
-    jb.nparts = s;
-    jb.pslot = xcd * kMaxParts + tail * s;
-  } else if (loc < F * cpx || s == 1) {
-    if (loc >= qx) return false;
-    t = base + loc;
+  if (u < xp.F * cpx || xp.s == 1) {
+    t = xp.base + u;
     jb.part = 0;
     jb.nparts = 1;
     jb.pslot = 0;
   } else {
-    const int v = loc - F * cpx;
-    if (v >= r * s) return false;
-    const int u = v / s;
-    t = base + F * cpx + u;
-    jb.part = v - u * s;
-    jb.nparts = s;
+    const int v = u - xp.F * cpx;
+    const int w = v / xp.s;
+    t = xp.base + xp.F * cpx + w;
+    jb.part = v - w * xp.s;
+    jb.nparts = xp.s;
     jb.pslot = xcd * kMaxParts + v;
   }
-  int seg0 = 0, seg_n = 0, mt_e = 0;
-  jb.expert = 0;
-  for (int i = 0; i < L; ++i) {
-    const int a = offsets[i], b = offsets[i + 1];
-    const int m = (b - a + BM - 1) / BM;
-    if (t < m * NT) {
-      jb.expert = i;
-      seg0 = a;
-      seg_n = b - a;
-      mt_e = m;
-      break;
-    }
-    t -= m * NT;
-  }
-  const int gfull = mt_e * kGroupN;
-  const int ng = t / gfull;
-  const int rem = t - ng * gfull;
-  const int gsz = min(kGroupN, NT - ng * kGroupN);
-  const int mt = rem / gsz;
-  const int nt = ng * kGroupN + (rem - mt * gsz);
-  jb.row0 = seg0 + mt * BM;
-  jb.rows = min(BM, seg_n - mt * BM);
-  jb.n0 = nt;  // n-tile index; the caller scales it by the tile's output columns
+  tile_of(offsets, tpre, L, NT, t, jb);
   jb.kb = (jb.part * nk) / jb.nparts;
   jb.nks = ((jb.part + 1) * nk) / jb.nparts - jb.kb;
-  return true;
 }
+
+// Tile shapes: regular 256 A rows x 256 B rows, waves 2 (M) x 2 (N); wide 128 A rows
+// x 512 B rows, waves side by side along N.  Either way a wave owns 128 A rows x
+// 128 B rows (4 x 4 MFMA 32x32 accumulators).
+template <bool WIDE>
+struct Shape {
+  static constexpr int kA = WIDE ? BM / 2 : BM;          // A rows
+  static constexpr int kB = WIDE ? 2 * BNE : BNE;        // B rows
+  static constexpr int kStageA = kA * kRowBytes;
+  static constexpr int kStage = (kA + kB) * kRowBytes;   // 64 KB regular, 80 KB wide
+  static constexpr int kLdA = kA / 32, kLdB = kB / 32;   // 1 KB direct loads per wave per stage
+  static constexpr int kLd = kLdA + kLdB;
+  __device__ static int wm(int wave) { return WIDE ? 0 : wave >> 1; }
+  __device__ static int wn(int wave) { return WIDE ? wave : wave & 1; }
+};
+constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true>::kStage;  // 160 KB
 
 // ---- epilogue.  The products were formed as (weight rows) x (token rows), so
 // in the 32x32 accumulator layout lane l holds token row l & 31 and register
 // 4q+u holds output column 8q + 4*(l/32) + u: four adjacent columns per q.
 // Each wave converts its part of the tile to bf16 (SwiGLU first for gate/up)
 // and parks it in LDS, rows padded by 16 bytes; then every thread copies
-// 16-byte row chunks out, so each store instruction writes whole 256-byte row
-// pieces.  The caller has made sure no wave still reads the loop's LDS stages.
-template <int NMAT>
+// 16-byte row chunks out, so each store instruction writes whole row pieces.
+// The caller has made sure no wave still reads the loop's LDS stages.
+template <int NMAT, bool WIDE>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_t* __restrict__ C, int row0, int rows,
                                          int n0, int N) {
-  constexpr int TC = NMAT == 2 ? BNE / 2 : BNE;  // output columns of the tile
-  constexpr int RS = stage_row_bytes<NMAT>();
+  using S = Shape<WIDE>;
+  constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
+  constexpr int RS = TC * 2 + 16;
   constexpr int NJ = NMAT == 2 ? 2 : 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1, fr = lane & 31, g = lane >> 5;
+  const int wm = S::wm(wave), wn = S::wn(wave), fr = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rt = wm * 128 + i * 32 + fr;
@@ -394,7 +477,7 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_
   block_barrier();
   constexpr int CPR = TC / 8;  // 16-byte chunks per row
 #pragma unroll
-  for (int u = 0; u < BM * CPR / kThreads; ++u) {
+  for (int u = 0; u < S::kA * CPR / kThreads; ++u) {
     const int id = tid + kThreads * u;
     const int r = id / CPR, c = id % CPR;
     const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
@@ -403,60 +486,76 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_
   }
 }
 
+template <int NMAT>
+constexpr size_t lds_bytes() {
+  constexpr size_t reg = size_t(Shape<false>::kA) * ((NMAT == 2 ? BNE / 2 : BNE) * 2 + 16);
+  constexpr size_t wide = size_t(Shape<true>::kA) * ((NMAT == 2 ? BNE : 2 * BNE) * 2 + 16);
+  constexpr size_t st = reg > wide ? reg : wide;
+  return kLoopLdsMax > st ? kLoopLdsMax : st;
+}
+
 // A piece's accumulators, thread-major: float4 number v of thread t at (v*256 + t)
 __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslot) {
   return reinterpret_cast<f32x4_t*>(parts + size_t(pslot) * (kPartBytes / sizeof(float)));
 }
 
-template <int NMAT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ C, int L, int N, int K, int cpx, int smax,
-                                                        float* __restrict__ parts) {
-  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per tile
-  const int NT = (N + ON - 1) / ON;
-  const int nk = K / BK;
-  Job jb;
-  if (!plan_job(offsets, L, NT, nk, cpx, smax, blockIdx.x % kXcds, blockIdx.x / kXcds, -1, jb)) return;
+// One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
+template <int NMAT, bool WIDE>
+__device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
+                                          const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
+                                          const Job& jb, float* __restrict__ parts, char* lds) {
+  using S = Shape<WIDE>;
+  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int row0 = jb.row0, rows = jb.rows, n0 = jb.n0 * ON, kb = jb.kb, nks = jb.nks;
-  const size_t boff = size_t(jb.expert) * N * K;
-  const bf16_t* Bg = B0 + boff;
-  const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
-
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = S::wm(wave), wn = S::wn(wave);
 
-  // ---- direct loads: 32 blocks of 8 rows (1 KB) for A and for B per stage;
-  // wave w fills blocks 8w..8w+7 of each.  Lane i of block j writes row
-  // 64w + 8j + i/8, physical chunk i%8, which holds logical chunk
-  // (i%8) ^ ((row/2)%8); that depends on i and the parity of j only.
-  const int lrow = 64 * wave + (lane >> 3);
+  // ---- direct loads: per stage kLdA 1 KB blocks of 8 A rows and kLdB of 8 B
+  // rows per wave; wave w fills A blocks kLdA*w.. and B blocks kLdB*w.. .  Lane
+  // i of block j writes row (first row of the wave) + 8j + i/8, physical chunk
+  // i%8, which holds logical chunk (i%8) ^ ((row/2)%8); as the wave's first row
+  // is a multiple of 16, that depends on i and the parity of j only.
   const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
   const int c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
+  const int a_lrow = (S::kA / 4) * wave + (lane >> 3);
   const bf16_t* a_base = A + size_t(row0) * K;
   const bf16_t* b_base;
   int b_lrow;
   if (NMAT == 2) {
     b_base = (wave < 2 ? Bg : Bu) + size_t(n0) * K;  // waves 0-1 load gate rows, 2-3 up rows
-    b_lrow = lrow & (BNE / 2 - 1);
+    b_lrow = ((S::kB / 4) * wave + (lane >> 3)) & (S::kB / 2 - 1);
   } else {
     b_base = Bg + size_t(n0) * K;
-    b_lrow = lrow;
+    b_lrow = (S::kB / 4) * wave + (lane >> 3);
   }
-  const int b_lim = N - 1 - n0;  // B rows past N repeat row N-1: those columns are never stored
+  // Rows past the segment (A) or past N (B) feed only outputs that are never
+  // stored, so they may read any valid row: A takes the rows that follow (up
+  // to the last row of the buffer), B wraps around to the first rows.  Letting
+  // them all repeat one row would send every lane of the padding to the same
+  // 128 bytes, one L2 channel, on every step.
+  const int a_lim = a_rows - 1 - row0;
+  int a_rel[S::kLdA], b_rel[S::kLdB];
+#pragma unroll
+  for (int j = 0; j < S::kLdA; ++j) a_rel[j] = min(a_lrow + 8 * j, a_lim);
+#pragma unroll
+  for (int j = 0; j < S::kLdB; ++j) {
+    int r = n0 + b_lrow + 8 * j;
+    if (r >= N) r %= N;
+    b_rel[j] = r - n0;
+  }
 #define MOE_ISSUE(kt_)                                                                                      \
   do {                                                                                                      \
-    char* sa_ = lds + ((kt_) % kStages) * kStage + (8 * wave) * 1024;                                       \
+    char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
+    char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
     const int k0_ = (kb + (kt_)) * BK;                                                                      \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                         \
+    _Pragma("unroll") for (int j = 0; j < S::kLdB; ++j) {                                                   \
       const int cc_ = (j & 1) ? c_odd : c_even;                                                             \
-      const int ar_ = min(lrow + 8 * j, rows - 1); /* rows past the segment repeat its last row */          \
-      const int br_ = min(b_lrow + 8 * j, b_lim);                                                           \
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(a_base + (uint32_t(ar_) * uint32_t(K) + cc_ * 8 + k0_)), \
-                                       (lds_ptr_t)(sa_ + j * 1024), 16, 0, 0);                             \
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(b_base + (uint32_t(br_) * uint32_t(K) + cc_ * 8 + k0_)), \
-                                       (lds_ptr_t)(sa_ + kStageA + j * 1024), 16, 0, 0);                   \
+      if (j < S::kLdA) {                                                                                    \
+        __builtin_amdgcn_global_load_lds((glb_ptr_t)(a_base + (int64_t(a_rel[j]) * K + cc_ * 8 + k0_)),     \
+                                         (lds_ptr_t)(sa_ + j * 1024), 16, 0, 0);                           \
+      }                                                                                                     \
+      __builtin_amdgcn_global_load_lds((glb_ptr_t)(b_base + (int64_t(b_rel[j]) * K + cc_ * 8 + k0_)),       \
+                                       (lds_ptr_t)(sb_ + j * 1024), 16, 0, 0);                             \
     }                                                                                                       \
   } while (0)
 
@@ -477,8 +576,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   int boffs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int br = NMAT == 2 ? (j < 2 ? wn * 64 + j * 32 : BNE / 2 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
-    boffs[j] = kStageA + (br + fr) * kRowBytes;
+    const int br = NMAT == 2 ? (j < 2 ? wn * 64 + j * 32 : S::kB / 2 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
+    boffs[j] = S::kStageA + (br + fr) * kRowBytes;
   }
   const int a_off = (wm * 128 + fr) * kRowBytes;
   bf16x8_t fa[2][4], fb[2][4];
@@ -509,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   MOE_ISSUE(0);
   if (nks > 1) {
     MOE_ISSUE(1);
-    MOE_VMCNT(16);  // stage 0 landed (16 loads per stage per wave)
+    MOE_VMCNT(S::kLd);  // stage 0 landed (kLd loads per stage per wave)
   } else {
     MOE_VMCNT(0);
   }
@@ -518,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   // every iteration has a next stage; the refill issued in it is stage kt+2,
   // or (near the end) a repeat of the last stage into the free slot
   for (int kt = 0; kt + 1 < nks; ++kt) {
-    const char* st = lds + (kt % kStages) * kStage;
+    const char* st = lds + (kt % kStages) * S::kStage;
     MOE_LOADF(1, st, 1);
     MOE_MMA(0);
     MOE_LOADF(0, st, 2);
@@ -533,18 +632,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     MOE_LGKMCNT0();   // and its reads of stage kt are done
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_LOADF(0, lds + ((kt + 1) % kStages) * kStage, 0);
+    MOE_LOADF(0, lds + ((kt + 1) % kStages) * S::kStage, 0);
     MOE_ISSUE(min(kt + 2, nks - 1));
     MOE_MMA(1);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    // the stage's kLd loads between the 16 MFMAs: two after each of the first kLd - 16
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
+    for (int p = 0; p < S::kLd - 16; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+#pragma unroll
+    for (int p = S::kLd - 16; p < 16; ++p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
   {
-    const char* st = lds + ((nks - 1) % kStages) * kStage;
+    const char* st = lds + ((nks - 1) % kStages) * S::kStage;
     MOE_LOADF(1, st, 1);
     MOE_MMA(0);
     MOE_LOADF(0, st, 2);
@@ -574,7 +679,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   }
   MOE_LGKMCNT0();
   block_barrier();  // every wave is done reading the last stage
-  epilogue<NMAT>(acc, lds, C, row0, rows, n0, N);
+  epilogue<NMAT, WIDE>(acc, lds, C, row0, rows, n0, N);
+}
+
+template <int NMAT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+                                                        bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
+                                                        const int32_t* __restrict__ tpre, int cpx, int smax,
+                                                        float* __restrict__ parts) {
+  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
+  const int NT = (N + ON - 1) / ON;
+  const int nk = K / BK;
+  // block (xcd, loc) runs unit loc of its XCD (blocks are dealt to the XCDs round robin)
+  const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+  const XcdPlan xp = plan_xcd(tpre[L], nk, cpx, smax, xcd);
+  if (loc >= xp.units) return;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // the tile prefix into LDS for the search (the loop's stages overwrite it later)
+  int32_t* spre = reinterpret_cast<int32_t*>(lds);
+  for (int i = threadIdx.x; i <= L; i += kThreads) spre[i] = tpre[i];
+  __syncthreads();
+  Job jb;
+  unit_job(offsets, spre, L, NT, nk, cpx, xcd, xp, loc, jb);
+  __syncthreads();  // every wave has its job before the first loads land in the LDS
+  const size_t boff = size_t(jb.expert) * N * K;
+  const bf16_t* Bg = B0 + boff;
+  const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
+  if (jb.wide)
+    tile_body<NMAT, true>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
+  else
+    tile_body<NMAT, false>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
 }
 
 // Adds the pieces of each split tile in piece order and writes the tile.
@@ -586,26 +721,30 @@ constexpr int kFixSub = 8;
 
 template <int NMAT>
 __global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
-                                                         int L, int N, int K, int cpx, int smax,
-                                                         const float* __restrict__ parts) {
+                                                         int L, int N, int K, const int32_t* __restrict__ tpre, int cpx,
+                                                         int smax, const float* __restrict__ parts) {
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
-  constexpr int NV = NMAT == 2 ? 32 : 64;                 // output float4s per thread of the tile
-  constexpr int kPer = NV * kThreads / (kFixSub * kThreads);  // items per thread of this block
+  constexpr int NV = NMAT == 2 ? 32 : 64;       // output float4s per thread of the tile
+  constexpr int kPer = NV / kFixSub;            // items per thread of this block
   const int NT = (N + ON - 1) / ON;
   const int sub = blockIdx.x % kFixSub, tile = blockIdx.x / kFixSub;
+  const int xcd = tile % kXcds, w = tile / kXcds;  // w-th split tile of the XCD
+  const XcdPlan xp = plan_xcd(tpre[L], K / BK, cpx, smax, xcd);
+  if (xp.s == 1 || w >= xp.r) return;
   Job jb;
-  if (!plan_job(offsets, L, NT, K / BK, cpx, smax, tile % kXcds, 0, tile / kXcds, jb)) return;
+  tile_of(offsets, tpre, L, NT, xp.base + xp.F * cpx + w, jb);
+  jb.nparts = xp.s;
+  jb.pslot = xcd * kMaxParts + w * xp.s;
   const int n0 = jb.n0 * ON;
   const size_t pstride = kPartBytes / sizeof(f32x4_t);  // float4s per piece
   const f32x4_t* base = reinterpret_cast<const f32x4_t*>(parts) + size_t(jb.pslot) * pstride;
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
-    const int item = (sub * kPer + it) * kThreads + threadIdx.x;  // consecutive threads: consecutive float4s
-    const int t = item % kThreads, w = item / kThreads;
-    // w -> (i, j, q) of the gate (or plain) float4
-    const int i = NMAT == 2 ? w / 8 : w / 16;
-    const int j = NMAT == 2 ? (w / 4) % 2 : (w / 4) % 4;
-    const int q = w % 4;
+    const int f = sub * kPer + it;  // float4 slot; consecutive threads read consecutive float4s
+    const int t = threadIdx.x;
+    const int i = NMAT == 2 ? f / 8 : f / 16;
+    const int j = NMAT == 2 ? (f / 4) % 2 : (f / 4) % 4;
+    const int q = f % 4;
     const int v = (i * 4 + j) * 4 + q;
     f32x4_t s = base[size_t(v) * kThreads + t];
     f32x4_t su = NMAT == 2 ? base[size_t(v + 8) * kThreads + t] : s;  // up partner: j + 2
@@ -614,7 +753,9 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restri
       if (NMAT == 2) su += base[size_t(p) * pstride + size_t(v + 8) * kThreads + t];
     }
     const int wave = t >> 6, lane = t & 63;
-    const int wm = wave >> 1, wn = wave & 1, fr = lane & 31, g = lane >> 5;
+    const int wm = jb.wide ? Shape<true>::wm(wave) : Shape<false>::wm(wave);
+    const int wn = jb.wide ? Shape<true>::wn(wave) : Shape<false>::wn(wave);
+    const int fr = lane & 31, g = lane >> 5;
     const int rt = wm * 128 + i * 32 + fr;
     const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
     if (rt < jb.rows && n0 + cl < N) {
@@ -648,24 +789,27 @@ bool splits(int K) { return K / BK >= kSplitMinSteps; }
 
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, int64_t max_pairs, float* parts, hipStream_t s) {
+                  bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                  hipStream_t s) {
   auto kern = gemm_kernel<NMAT>;
   constexpr size_t lds = lds_bytes<NMAT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
-  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int cpx = cus_per_xcd();
   const int smax = splits(K) && parts != nullptr ? kMaxSplit : 1;
-  // every XCD's range holds at most ceil(R/8) tiles; splitting adds at most kMaxParts - kMaxTail blocks
+  // every XCD's range holds at most ceil(R/8) tiles (R counts regular tiles, an upper bound on the
+  // mix of regular and wide ones); splitting adds at most kMaxParts - kMaxTail blocks
+  constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int64_t tiles = ((max_pairs + BM - 1) / BM + L) * ((N + ON - 1) / ON);
   const int64_t per_xcd = (tiles + kXcds - 1) / kXcds + (smax > 1 ? kMaxParts - kMaxTail : 0);
-  MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K, cpx,
-             smax, parts);
+  // A holds max_pairs rows (the caller's x_sorted or h)
+  MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K,
+             int(max_pairs), tpre, cpx, smax, parts);
   if (smax > 1) {
     const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
     MOE_LAUNCH(fname, fixup_kernel<NMAT>, dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s, offsets, C,
-               L, N, K, cpx, smax, static_cast<const float*>(parts));
+               L, N, K, tpre, cpx, smax, static_cast<const float*>(parts));
   }
   return MOE_OK;
 }
@@ -837,9 +981,11 @@ moe_status launch_small(const FfnArgs& a) {
 
 }  // namespace
 
-size_t ffn_parts_bytes(const moe_layer_desc* d, int64_t max_pairs) {
-  if (!use_big(d, max_pairs) || !(big::splits(d->hidden) || big::splits(d->intermediate))) return 0;
-  return size_t(big::kXcds) * big::kMaxParts * big::kPartBytes;
+size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs) {
+  if (!use_big(d, max_pairs)) return 0;
+  const size_t plan = align_up(size_t(2) * (d->local_count + 1) * sizeof(int32_t), 256);
+  const bool split = big::splits(d->hidden) || big::splits(d->intermediate);
+  return plan + (split ? size_t(big::kXcds) * big::kMaxParts * big::kPartBytes : 0);
 }
 
 moe_status launch_grouped_ffn(const FfnArgs& a) {
@@ -849,12 +995,20 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
   const bf16_t* x = static_cast<const bf16_t*>(a.x_sorted);
   bf16_t* h = static_cast<bf16_t*>(a.h);
+  // scratch: the tile plan, then (long K) the split pieces
+  int32_t* pre = static_cast<int32_t*>(a.scratch);
+  float* parts = big::splits(H) || big::splits(I)
+                     ? reinterpret_cast<float*>(static_cast<char*>(a.scratch) +
+                                                align_up(size_t(2) * (L + 1) * sizeof(int32_t), 256))
+                     : nullptr;
+  MOE_LAUNCH("ffn_plan", big::plan_kernel, dim3(1), dim3(1024), 0, a.s, a.offsets, L, (I + big::BNE / 2 - 1) / (big::BNE / 2),
+             (H + big::BNE - 1) / big::BNE, pre);
   moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
-                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, a.parts, a.s);
+                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, pre, parts, a.s);
   if (st != MOE_OK) return st;
   return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
                         static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.max_pairs,
-                        a.parts, a.s);
+                        pre + L + 1, parts, a.s);
 }
 
 }  // namespace moe

@@ -87,13 +87,13 @@ struct FfnArgs {
   const void* w_up;
   const void* w_down;
   void* y_sorted;
-  void* h;        // [P_max, I]
-  float* parts;   // split-K pieces (ffn_parts_bytes), or null when that is 0
+  void* h;         // [P_max, I]
+  void* scratch;   // ffn_scratch_bytes: the large-tile path's tile plan and split-K pieces
   int64_t max_pairs;
   hipStream_t s;
 };
-// Scratch for the pieces of split tiles (large-tile path with long K), else 0.
-size_t ffn_parts_bytes(const moe_layer_desc* d, int64_t max_pairs);
+// Scratch of the large-tile path (tile plan; split-K pieces when K is long), else 0.
+size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs);
 moe_status launch_grouped_ffn(const FfnArgs& a);
 
 struct CombineArgs {
