@@ -156,3 +156,30 @@ def test_long_k_split_tiles(H, I):
     # the same call again gives the same bits (the pieces are added in a fixed order)
     y2 = np_of(layer.grouped_ffn(g["x_sorted"], g["offsets"]))[:P]
     np.testing.assert_array_equal(y2, got)
+
+
+def test_segment_tails_on_the_large_tile_path():
+    # hand-made segments whose tails take every tile shape of the large-tile kernel:
+    # 257 rows (full tile + 1-row wide tail), 128 (a wide tile alone), 129 (regular tail),
+    # 0 (empty), 256 (exactly one full tile) and 384 (full + 128-row wide tail); I = 448 and
+    # H = 320 leave the last n-tile of both products partly past N
+    s = synth.spec("mixtral_like", T=600, H=320, I=448, E=6, L=6)
+    inp = synth.make_layer(s)
+    layer, _ = layer_of(inp)
+    counts = np.array([257, 128, 129, 0, 256, 384])
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = int(offs[-1])
+    assert layer.max_pairs >= P and layer.max_pairs >= 128 * s.L
+    rng = np.random.default_rng(7)
+    xs = np.zeros((layer.max_pairs, s.H), dtype=np.float32)
+    xs[:P] = rng.standard_normal((P, s.H)).astype(np.float32)
+    xs_bits = synth.f32_to_bf16_bits(xs)
+    x_dev = torch.from_numpy(xs_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    y = np_of(layer.grouped_ffn(x_dev, torch.from_numpy(offs).cuda()))[:P]
+    view = oracle.moe_oracle._ExpertView
+    x64 = np_of(x_dev)[:P].astype(np.float64)
+    ref = oracle.grouped_ffn(x64, offs.astype(np.int64), view(inp["w_gate"], s.dtype), view(inp["w_up"], s.dtype),
+                             view(inp["w_down"], s.dtype))
+    err = row_error(y, ref, s.dtype)
+    say(f"[parity] segment tails 257/128/129/0/256/384: grouped FFN row error {err:.3g}")
+    assert err <= tol(s.dtype)
