@@ -256,24 +256,32 @@ bool supported(int K) { return K % BK == 0; }
 // Tiles are numbered over (expert, group of kGroupN n-tiles, m-tile, n-tile
 // in group) and dealt to the XCDs in contiguous ranges (block b runs on XCD
 // b % 8).  An XCD with q tiles runs them in rounds of `cpx` (its CU count);
-// when the last round is only partly filled and K is long, its r tiles are
-// cut into s pieces along K (s in {2, 4}, chosen to minimise the rounds the
-// pieces take, ceil(r*s/cpx)/s), so the XCD finishes in F + ceil(r*s/cpx)/s
-// tile times instead of F + 1.  Each piece writes its float32 accumulators;
+// when the last round is only partly filled, its r tiles may be cut into s
+// pieces along K, so the XCD finishes in F + ceil(r*s/cpx)/s tile times
+// instead of F + 1.  Each piece writes its float32 accumulators and
 // fixup_kernel adds the pieces in piece order (so the result does not depend
-// on timing) and runs the usual epilogue.
-constexpr int kSplitMinSteps = 128;  // K/BK from which the last round is split
+// on timing) and runs the usual epilogue.  A cut pays when the tile time it
+// saves, (1 - ceil(r*s/cpx)/s) * nk steps, exceeds the pieces' write and
+// re-read, which cost about kPieceSteps steps each (256 KB out and back per
+// piece against the tile's 64 KB per step from L2 and MALL).
+constexpr int kSplitMinSteps = 32;   // K/BK from which the last round may be cut
 constexpr int kMaxSplit = 4;
-constexpr int kMaxParts = 96;        // pieces per XCD: s = 4 needs r <= 24, s = 2 needs r <= 16
+constexpr int kMaxParts = 96;        // pieces per XCD
 constexpr int kMaxTail = kMaxParts / kMaxSplit;
 constexpr size_t kPartBytes = size_t(kThreads) * 256 * sizeof(float);  // one piece's accumulators
+constexpr float kPieceSteps = 0.4f;
 
 __device__ __forceinline__ int split_of(int r, int cpx, int smax, int nk) {
   int best = 1;
+  float best_net = 0.0f;
   for (int s = 2; s <= smax; s *= 2) {
     if (r == 0 || r > kMaxTail || nk < 16 * s || r * s > kMaxParts) break;
-    // ceil(r*s/cpx)/s < ceil(r*best/cpx)/best
-    if (((r * s + cpx - 1) / cpx) * best < ((r * best + cpx - 1) / cpx) * s) best = s;
+    const float rounds = float((r * s + cpx - 1) / cpx) / float(s);  // tile times the pieces take
+    const float net = (1.0f - rounds) * float(nk) - kPieceSteps * float(r * s);
+    if (net > best_net) {
+      best = s;
+      best_net = net;
+    }
   }
   return best;
 }
@@ -784,7 +792,7 @@ int cus_per_xcd() {
   return cached[dev];
 }
 
-// K long enough for the split of a partly filled last round
+// K long enough to cut a partly filled last round
 bool splits(int K) { return K / BK >= kSplitMinSteps; }
 
 template <int NMAT>

@@ -203,9 +203,9 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
  *   offsets   device [L+1] int32 (from moe_dispatch)
  *   w_gate    device [L, I, H] dtype;  w_up [L, I, H];  w_down [L, H, I]
  *   y_sorted  device [P_max, H] dtype out (rows >= P untouched)
- *   ws        device workspace of MOE_STAGE_FFN bytes: h [P_max, I], and for
- *             K >= 8192 on the large-tile path the float32 K pieces of the
- *             tiles in each XCD's last, partly filled round */
+ *   ws        device workspace of MOE_STAGE_FFN bytes: h [P_max, I], and on
+ *             the large-tile path its tile plan and (K >= 2048) the float32
+ *             K pieces of tiles in each XCD's last, partly filled round */
 moe_status moe_grouped_ffn(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
                            const void* w_gate, const void* w_up, const void* w_down,
                            void* y_sorted, void* ws, size_t ws_bytes, void* stream);
