@@ -251,6 +251,10 @@ constexpr int kXcds = 8;
 #define MOE_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 bool supported(int K) { return K % BK == 0; }
+// word 3 of a buffer descriptor on this family: 32-bit data format, raw byte addressing
+constexpr int kRsrcFlags = 0x00020000;
+// the direct loads address a weight matrix with 32-bit byte offsets
+bool addressable(int64_t rows, int64_t K) { return rows * K * 2 < (int64_t(1) << 32); }
 
 // ---- work plan -------------------------------------------------------------
 // Tiles are numbered over (expert, group of kGroupN n-tiles, m-tile, n-tile
@@ -515,7 +519,9 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   using S = Shape<WIDE>;
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int row0 = jb.row0, rows = jb.rows, n0 = jb.n0 * ON, kb = jb.kb, nks = jb.nks;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keeping it in a scalar register makes every LDS
+  // target of the direct loads scalar arithmetic
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = S::wm(wave), wn = S::wn(wave);
 
   // ---- direct loads: per stage kLdA 1 KB blocks of 8 A rows and kLdB of 8 B
@@ -526,44 +532,47 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
   const int c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
   const int a_lrow = (S::kA / 4) * wave + (lane >> 3);
-  const bf16_t* a_base = A + size_t(row0) * K;
-  const bf16_t* b_base;
+  // buffer resources over the tile's rows of A and over the whole weight matrix
+  // (its extent is under 4 GiB); a read outside either returns zeros
+  const uint32_t a_bytes = uint32_t(min(int64_t(a_rows - row0) * K * 2, int64_t(0xFFFFFFFF)));
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(A + size_t(row0) * K), 0, a_bytes, kRsrcFlags);
   int b_lrow;
-  if (NMAT == 2) {
-    b_base = (wave < 2 ? Bg : Bu) + size_t(n0) * K;  // waves 0-1 load gate rows, 2-3 up rows
-    b_lrow = ((S::kB / 4) * wave + (lane >> 3)) & (S::kB / 2 - 1);
-  } else {
-    b_base = Bg + size_t(n0) * K;
-    b_lrow = (S::kB / 4) * wave + (lane >> 3);
-  }
+  if (NMAT == 2) b_lrow = ((S::kB / 4) * wave + (lane >> 3)) & (S::kB / 2 - 1);  // waves 0-1 load gate rows, 2-3 up
+  else b_lrow = (S::kB / 4) * wave + (lane >> 3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(NMAT == 2 && wave >= 2 ? Bu : Bg), 0, uint32_t(N) * uint32_t(K) * 2u, kRsrcFlags);
   // Rows past the segment (A) or past N (B) feed only outputs that are never
   // stored, so they may read any valid row: A takes the rows that follow (up
   // to the last row of the buffer), B wraps around to the first rows.  Letting
   // them all repeat one row would send every lane of the padding to the same
   // 128 bytes, one L2 channel, on every step.
+  // Each lane's byte offsets are fixed for the whole loop (A from the tile's
+  // first row, B from the matrix); a step only moves the scalar offset by k0,
+  // so a load costs no vector arithmetic.
   const int a_lim = a_rows - 1 - row0;
-  int a_rel[S::kLdA], b_rel[S::kLdB];
+  uint32_t a_vo[S::kLdA], b_vo[S::kLdB];
 #pragma unroll
-  for (int j = 0; j < S::kLdA; ++j) a_rel[j] = min(a_lrow + 8 * j, a_lim);
+  for (int j = 0; j < S::kLdA; ++j) {
+    const int cc = (j & 1) ? c_odd : c_even;
+    a_vo[j] = (uint32_t(min(a_lrow + 8 * j, a_lim)) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
+  }
 #pragma unroll
   for (int j = 0; j < S::kLdB; ++j) {
+    const int cc = (j & 1) ? c_odd : c_even;
     int r = n0 + b_lrow + 8 * j;
     if (r >= N) r %= N;
-    b_rel[j] = r - n0;
+    b_vo[j] = (uint32_t(r) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
   }
 #define MOE_ISSUE(kt_)                                                                                      \
   do {                                                                                                      \
     char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
     char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
-    const int k0_ = (kb + (kt_)) * BK;                                                                      \
+    const uint32_t k0_ = uint32_t(kb + (kt_)) * (BK * 2);                                                   \
     _Pragma("unroll") for (int j = 0; j < S::kLdB; ++j) {                                                   \
-      const int cc_ = (j & 1) ? c_odd : c_even;                                                             \
-      if (j < S::kLdA) {                                                                                    \
-        __builtin_amdgcn_global_load_lds((glb_ptr_t)(a_base + (int64_t(a_rel[j]) * K + cc_ * 8 + k0_)),     \
-                                         (lds_ptr_t)(sa_ + j * 1024), 16, 0, 0);                           \
-      }                                                                                                     \
-      __builtin_amdgcn_global_load_lds((glb_ptr_t)(b_base + (int64_t(b_rel[j]) * K + cc_ * 8 + k0_)),       \
-                                       (lds_ptr_t)(sb_ + j * 1024), 16, 0, 0);                             \
+      if (j < S::kLdA)                                                                                      \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + j * 1024), 16, a_vo[j], k0_, 0, 0); \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(sb_ + j * 1024), 16, b_vo[j], k0_, 0, 0);   \
     }                                                                                                       \
   } while (0)
 
@@ -968,7 +977,7 @@ moe_status launch_t(const FfnArgs& a) {
 // batches (a handful of rows per expert) take the skinny kernel
 bool use_big(const moe_layer_desc* d, int64_t max_pairs) {
   return d->dtype == MOE_BF16 && max_pairs >= int64_t(128) * d->local_count && big::supported(d->hidden) &&
-         big::supported(d->intermediate);
+         big::supported(d->intermediate) && big::addressable(d->intermediate, d->hidden);
 }
 
 moe_status launch_small(const FfnArgs& a) {
