@@ -564,15 +564,19 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     if (r >= N) r %= N;
     b_vo[j] = (uint32_t(r) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
   }
-#define MOE_ISSUE(kt_)                                                                                      \
+// loads q0..q1-1 of stage kt_, in the order A0 B0 A1 B1 ... (then the B rows
+// past the last A block)
+#define MOE_ISSUE(kt_, q0_, q1_)                                                                            \
   do {                                                                                                      \
     char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
     char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
     const uint32_t k0_ = uint32_t(kb + (kt_)) * (BK * 2);                                                   \
-    _Pragma("unroll") for (int j = 0; j < S::kLdB; ++j) {                                                   \
-      if (j < S::kLdA)                                                                                      \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + j * 1024), 16, a_vo[j], k0_, 0, 0); \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(sb_ + j * 1024), 16, b_vo[j], k0_, 0, 0);   \
+    _Pragma("unroll") for (int q = (q0_); q < (q1_); ++q) {                                                 \
+      const int j_ = q < 2 * S::kLdA ? q / 2 : q - S::kLdA;                                                 \
+      if (q < 2 * S::kLdA && q % 2 == 0)                                                                    \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + j_ * 1024), 16, a_vo[j_], k0_, 0, 0); \
+      else                                                                                                  \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(sb_ + j_ * 1024), 16, b_vo[j_], k0_, 0, 0); \
     }                                                                                                       \
   } while (0)
 
@@ -622,10 +626,17 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     }                                                                                                     \
   } while (0)
 
-  MOE_ISSUE(0);
+  // The refill of a stage goes out in two halves: the first right after the
+  // barrier that frees its slot (beside the last chunk of the stage before),
+  // the second beside the first chunk of the stage in between.  Against one
+  // burst of all kLd loads per step this halves the rate at which the 32 CUs
+  // of an XCD hit L2 together, and the second half still has three chunks to
+  // land before the barrier that waits for it.
+  constexpr int kHalf = S::kLd / 2;
+  MOE_ISSUE(0, 0, S::kLd);
   if (nks > 1) {
-    MOE_ISSUE(1);
-    MOE_VMCNT(S::kLd);  // stage 0 landed (kLd loads per stage per wave)
+    MOE_ISSUE(1, 0, kHalf);
+    MOE_VMCNT(kHalf);  // stage 0 landed
   } else {
     MOE_VMCNT(0);
   }
@@ -636,12 +647,20 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   for (int kt = 0; kt + 1 < nks; ++kt) {
     const char* st = lds + (kt % kStages) * S::kStage;
     MOE_LOADF(1, st, 1);
+    MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
     MOE_MMA(0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, kHalf / 8, 0);
+    }
+    if constexpr (kHalf % 8 != 0) __builtin_amdgcn_sched_group_barrier(0x020, kHalf % 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
     MOE_LOADF(0, st, 2);
     MOE_MMA(1);
     MOE_LOADF(1, st, 3);
     MOE_MMA(0);
-    MOE_PIPE_DS();
     MOE_PIPE_DS();
     MOE_PIPE_DS();
     __builtin_amdgcn_sched_barrier(0);
@@ -650,20 +669,15 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
     MOE_LOADF(0, lds + ((kt + 1) % kStages) * S::kStage, 0);
-    MOE_ISSUE(min(kt + 2, nks - 1));
+    MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
     MOE_MMA(1);
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    // the stage's kLd loads between the 16 MFMAs: two after each of the first kLd - 16
 #pragma unroll
-    for (int p = 0; p < S::kLd - 16; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    for (int p = 0; p < 8; ++p) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, kHalf / 8, 0);
     }
-#pragma unroll
-    for (int p = S::kLd - 16; p < 16; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+    if constexpr (kHalf % 8 != 0) __builtin_amdgcn_sched_group_barrier(0x020, kHalf % 8, 0);
   }
   {
     const char* st = lds + ((nks - 1) % kStages) * S::kStage;
