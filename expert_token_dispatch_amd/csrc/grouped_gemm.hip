@@ -56,7 +56,11 @@ template <> struct Gemm<float> {
   }
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU through the hardware reciprocal (1 ulp) rather than an IEEE division:
+// five instructions instead of about fifteen.  Every FFN kernel here uses this
+// one definition, so a token's result does not depend on which kernel ran it.
+// Both ends stay exact: exp(-z) overflowing gives -0, underflowing gives z.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // NMAT = 2: gate and up products with the SwiGLU epilogue; NMAT = 1: plain product.
 template <typename T, int NMAT>
