@@ -21,11 +21,15 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// float32 -> bfloat16, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+// float32 -> bfloat16, round to nearest, ties to even, by the hardware
+// conversion (v_cvt_pk_bf16_f32); a NaN stays a NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+
+// two floats -> two bfloat16 in one word (a in the low half), one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
 }
 
 template <typename T> struct Elem;

@@ -482,8 +482,8 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_
         for (int u = 0; u < 4; ++u)
           v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + 2][4 * q + u] : acc[i][j][4 * q + u];
         uint2 pk;
-        pk.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-        pk.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
         const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
         *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
       }
@@ -798,8 +798,8 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restri
 #pragma unroll
       for (int u = 0; u < 4; ++u) o[u] = NMAT == 2 ? silu(s[u]) * su[u] : s[u];
       uint2 pk;
-      pk.x = uint32_t(f32_to_bf16(o[0])) | (uint32_t(f32_to_bf16(o[1])) << 16);
-      pk.y = uint32_t(f32_to_bf16(o[2])) | (uint32_t(f32_to_bf16(o[3])) << 16);
+      pk.x = pack_bf16x2(o[0], o[1]);
+      pk.y = pack_bf16x2(o[2], o[3]);
       *reinterpret_cast<uint2*>(C + size_t(jb.row0 + rt) * N + n0 + cl) = pk;
     }
   }
