@@ -19,12 +19,11 @@
 //                16x16x32 bf16 (f32: 8 x 16x16x4 per stage).  Each block
 //                writes its partial logits to partial[slice][t][e].
 //  route_topk    sums the slices in slice order (so the logits do not depend
-//                on scheduling) and adds the bias; then four lanes per token
-//                each keep a sorted list of the k best of a contiguous quarter
-//                of the experts (strict compares over ascending ids, so equal
-//                scores keep the lower id first), and one lane merges the four
-//                lists, taking the lower quarter on equal scores, and forms the
-//                softmax over the k chosen.
+//                on scheduling) and adds the bias; then a row of 16 lanes per
+//                token takes the k best in k rounds, each a row-wide maximum and
+//                a row-wide minimum of the expert ids holding it (so equal
+//                scores go to the lower id), both by DPP within the row, and
+//                forms the softmax over the k chosen.
 #include <math.h>
 
 #include "common.h"
@@ -195,58 +194,26 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T* __restrict__ 
 }
 
 constexpr int kTopkTok = 64;      // tokens per top-k block
-constexpr int kTopkThreads = 256; // four lanes per token
-
-// Sorted insertion into a descending list; a strict compare keeps the entry
-// seen first (the lower expert id, as experts are walked in ascending order)
-// ahead of an equal score.
-template <int MAXK>
-__device__ __forceinline__ void topk_insert(float (&v)[MAXK], int (&id)[MAXK], float xv, int e) {
-#pragma unroll
-  for (int j = MAXK - 1; j >= 0; --j) {
-    const bool shift = (j > 0) && (v[j > 0 ? j - 1 : 0] < xv);
-    if (shift) {
-      v[j] = v[j - 1];
-      id[j] = id[j - 1];
-    } else if (v[j] < xv) {
-      v[j] = xv;
-      id[j] = e;
-    }
-  }
-}
 
 static_assert(kTopkTok == kDispatchTokens, "a top-k block is one dispatch chunk");
 
-template <int MAXK>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ partial, int nslice,
-                                                            const float* __restrict__ br, float* __restrict__ logits_out,
-                                                            int32_t* __restrict__ ids, float* __restrict__ tw,
-                                                            float* __restrict__ tl, int32_t* __restrict__ blk_counts,
-                                                            int ntok, int E, int k) {
-  extern __shared__ float sh[];
-  const int ld = E + 1;
-  float* lg = sh;                                          // [64][E + 1]
-  float* mv = sh + kTopkTok * ld;                          // [64][4][MAXK] merge values
-  int* mi = reinterpret_cast<int*>(mv + kTopkTok * 4 * MAXK);  // [64][4][MAXK] merge ids
-  int* hist = mi + kTopkTok * 4 * MAXK;                    // [E] chunk histogram (when blk_counts)
-  const int tid = threadIdx.x;
-  if (blk_counts != nullptr)
-    for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
-  const int t0 = blockIdx.x * kTopkTok;
-  const int rows = min(kTopkTok, ntok - t0);
+// Sum a 64-token tile of partial logits over the slices in slice order, add the
+// bias, optionally store the logits, and keep the tile in LDS with row stride ld.
+template <int NTHR>
+__device__ __forceinline__ void load_logit_tile(const float* __restrict__ partial, int nslice,
+                                                const float* __restrict__ br, float* __restrict__ logits_out,
+                                                int ntok, int E, int t0, int rows, int ld, float* lg, int tid) {
   const int n = rows * E;  // the tile's logits are contiguous in every slice
   const size_t slice_stride = size_t(ntok) * E;
   const float* base = partial + size_t(t0) * E;
-
-  // ---- sum the slices in order, add the bias, keep the tile in LDS
   if ((E & 3) == 0) {
     const int n4 = n >> 2;
     // four float4s per thread per round, their slices' loads issued together and added in slice order
-    for (int i0 = tid; i0 < n4; i0 += 4 * kTopkThreads) {
+    for (int i0 = tid; i0 < n4; i0 += 4 * NTHR) {
       f32x4_t v[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int i = i0 + c * kTopkThreads;
+        const int i = i0 + c * NTHR;
         if (i < n4) v[c] = reinterpret_cast<const f32x4_t*>(base)[i];
       }
       for (int s0 = 1; s0 < nslice; s0 += 4) {
@@ -255,18 +222,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int i = i0 + c * kTopkThreads;
+            const int i = i0 + c * NTHR;
             if (i < n4 && s0 + u < nslice) t[c][u] = reinterpret_cast<const f32x4_t*>(base + (s0 + u) * slice_stride)[i];
           }
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            if (i0 + c * kTopkThreads < n4 && s0 + u < nslice) v[c] += t[c][u];
+            if (i0 + c * NTHR < n4 && s0 + u < nslice) v[c] += t[c][u];
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int i = i0 + c * kTopkThreads;
+        const int i = i0 + c * NTHR;
         if (i >= n4) continue;
         const int m = (4 * i) / E, e = 4 * i - m * E;
         if (br != nullptr) {
@@ -279,7 +246,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       }
     }
   } else {
-    for (int i = tid; i < n; i += kTopkThreads) {
+    for (int i = tid; i < n; i += NTHR) {
       float v = base[i];
       for (int sl = 1; sl < nslice; ++sl) v += base[sl * slice_stride + i];
       const int m = i / E, e = i - m * E;
@@ -288,55 +255,94 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       lg[m * ld + e] = v;
     }
   }
+}
+
+// ---- top-k with one 16-lane row per token (E <= 16 * VPL) ----------------
+// A block of 1024 threads takes the same 64-token tile; each wave's four rows
+// of 16 lanes take one token each, lane r holding experts r*VPL .. r*VPL+VPL-1.
+// Each of the k rounds finds the row's largest remaining logit with four DPP
+// steps, then the lowest expert id holding it with four more (so equal scores
+// go to the lower id, the order the pages' top-k implies), and the lane owning
+// that expert marks it taken.  The weights are a softmax over the k chosen
+// logits, shifted by the largest.
+constexpr int kRowThreads = 1024;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+// maximum / minimum over the 16 lanes of a row, left in every lane of the row
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, __int_as_float(dpp<0xB1>(__float_as_int(x))));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, __int_as_float(dpp<0x4E>(__float_as_int(x))));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, __int_as_float(dpp<0x141>(__float_as_int(x))));  // row_half_mirror
+  x = fmaxf(x, __int_as_float(dpp<0x140>(__float_as_int(x))));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ int row_min(int x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  x = min(x, dpp<0x140>(x));
+  return x;
+}
+
+template <int MAXK, int VPL>
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ partial, int nslice,
+                                                               const float* __restrict__ br, float* __restrict__ logits_out,
+                                                               int32_t* __restrict__ ids, float* __restrict__ tw,
+                                                               float* __restrict__ tl, int32_t* __restrict__ blk_counts,
+                                                               int ntok, int E, int k) {
+  extern __shared__ float sh[];
+  const int ld = 16 * VPL + 4;                 // row stride: a lane's VPL logits are 16-byte aligned
+  float* lg = sh;                              // [64][ld]
+  int* hist = reinterpret_cast<int*>(sh + kTopkTok * ld);  // [E]
+  const int tid = threadIdx.x;
+  if (blk_counts != nullptr)
+    for (int e = tid; e < E; e += kRowThreads) hist[e] = 0;
+  const int t0 = blockIdx.x * kTopkTok;
+  const int rows = min(kTopkTok, ntok - t0);
+  load_logit_tile<kRowThreads>(partial, nslice, br, logits_out, ntok, E, t0, rows, ld, lg, tid);
   __syncthreads();
 
-  // ---- four lanes per token, each over a contiguous quarter of the experts
-  const int m = tid >> 2, q = tid & 3;
-  const int chunk = (E + 3) >> 2;
-  const int e_lo = q * chunk, e_hi = min(E, e_lo + chunk);
-  float v[MAXK];
-  int id[MAXK];
-#pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    v[j] = -INFINITY;
-    id[j] = -1;
-  }
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15;
+  const int m = wave * 4 + (lane >> 4);        // token of this row within the tile
   if (m < rows) {
-    const float* my = lg + m * ld;
-    for (int e = e_lo; e < e_hi; ++e) topk_insert<MAXK>(v, id, my[e], e);
-  }
+    float v[VPL];
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(lg + m * ld + r * VPL);
 #pragma unroll
-  for (int j = 0; j < MAXK; ++j) {
-    mv[(m * 4 + q) * MAXK + j] = v[j];
-    mi[(m * 4 + q) * MAXK + j] = id[j];
-  }
-  __syncthreads();
-
-  // ---- merge the four sorted lists; on equal scores the lower quarter (lower ids) goes first
-  if (q == 0 && m < rows) {
-    const int t = t0 + m;
-    int head[4] = {0, 0, 0, 0};
+    for (int c4 = 0; c4 < VPL / 4; ++c4) {
+      const f32x4_t q = src[c4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[4 * c4 + u] = q[u] == q[u] ? q[u] : -INFINITY;  // a NaN ranks last
+    }
+    unsigned taken = 0;
+#pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      if (r * VPL + c >= E) taken |= 1u << c;  // past the last expert
     float sel_v[MAXK];
     int sel_i[MAXK];
 #pragma unroll
     for (int j = 0; j < MAXK; ++j) {
+      sel_v[j] = 0.0f;
+      sel_i[j] = 0;
       if (j < k) {
-        int best = -1;
+        // this lane's best untaken logit; a strict compare keeps the lower id on ties
         float bv = -INFINITY;
+        int bc = -1;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          if (head[qq] < MAXK) {
-            const int off = (m * 4 + qq) * MAXK + head[qq];
-            if (mi[off] >= 0 && (best < 0 || mv[off] > bv)) {
-              best = qq;
-              bv = mv[off];
-            }
+        for (int c = 0; c < VPL; ++c)
+          if (!((taken >> c) & 1u) && (bc < 0 || v[c] > bv)) {
+            bv = v[c];
+            bc = c;
           }
-        }
-        const int off = (m * 4 + best) * MAXK + head[best];
-        sel_v[j] = bv;
-        sel_i[j] = mi[off];
-        head[best] += 1;
+        const float mx = row_max(bv);
+        const int cand = (bc >= 0 && bv == mx) ? r * VPL + bc : 0x7FFFFFFF;
+        const int win = row_min(cand);
+        if (cand == win) taken |= 1u << bc;
+        sel_v[j] = mx;
+        sel_i[j] = win;
+        if (r == 0 && blk_counts != nullptr) atomicAdd(&hist[win], 1);
       }
     }
     const float top = sel_v[0];
@@ -350,21 +356,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       }
     }
     const float inv = 1.0f / sum;
+    const int t = t0 + m;
+    // lane r of the row writes entries r and r + 16
 #pragma unroll
-    for (int j = 0; j < MAXK; ++j) {
+    for (int h = 0; h < (MAXK + 15) / 16; ++h) {
+      const int j = r + 16 * h;
       if (j < k) {
+        float ov = sel_v[0], oe = ex[0];
+        int oi = sel_i[0];
+#pragma unroll
+        for (int jj = 1; jj < MAXK; ++jj)
+          if (j == jj) {
+            ov = sel_v[jj];
+            oe = ex[jj];
+            oi = sel_i[jj];
+          }
         const size_t o = size_t(t) * k + j;
-        ids[o] = sel_i[j];
-        tw[o] = ex[j] * inv;
-        if (tl != nullptr) tl[o] = sel_v[j];
-        if (blk_counts != nullptr) atomicAdd(&hist[sel_i[j]], 1);
+        ids[o] = oi;
+        tw[o] = oe * inv;
+        if (tl != nullptr) tl[o] = ov;
       }
     }
   }
   // the chunk's expert histogram for dispatch (integer counts: order-free)
   if (blk_counts != nullptr) {
     __syncthreads();
-    for (int e = tid; e < E; e += kTopkThreads) blk_counts[size_t(blockIdx.x) * E + e] = hist[e];
+    for (int e = tid; e < E; e += kRowThreads) blk_counts[size_t(blockIdx.x) * E + e] = hist[e];
   }
 }
 
@@ -409,22 +426,29 @@ moe_status launch_logits(const RouteArgs& a, const Split& sp, float* partial) {
   return MOE_OK;
 }
 
-template <int MAXK>
-moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
+template <int MAXK, int VPL>
+moe_status launch_topk_rows(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
   const moe_layer_desc* d = a.d;
   const int ntok = int(d->num_tokens);
   const int E = d->num_experts;
-  const size_t lds = (size_t(kTopkTok) * (E + 1) + size_t(kTopkTok) * 4 * MAXK * 2 + size_t(E)) * sizeof(float);
-  auto kern = topk_kernel<MAXK>;
+  const size_t lds = (size_t(kTopkTok) * (16 * VPL + 4) + size_t(E)) * sizeof(float);
+  auto kern = topk_row_kernel<MAXK, VPL>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return set_error(MOE_ERR_HIP, "route_topk: LDS attribute: %s", hipGetErrorString(e));
   }
   const dim3 grid(unsigned((ntok + kTopkTok - 1) / kTopkTok));
-  MOE_LAUNCH("route_topk", kern, grid, dim3(kTopkThreads), lds, a.s, partial, nslice, bias, a.logits_out,
+  MOE_LAUNCH("route_topk", kern, grid, dim3(kRowThreads), lds, a.s, partial, nslice, bias, a.logits_out,
              a.topk_ids, a.topk_w, a.topk_logit, a.blk_counts, ntok, E, d->top_k);
   return MOE_OK;
+}
+
+template <int MAXK>
+moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
+  // one 16-lane row per token, 8 or 16 logits per lane (the router takes up to 256 experts)
+  if (a.d->num_experts <= 128) return launch_topk_rows<MAXK, 8>(a, partial, nslice, bias);
+  return launch_topk_rows<MAXK, 16>(a, partial, nslice, bias);
 }
 
 moe_status pick_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {

@@ -65,6 +65,28 @@ def test_all_tokens_to_one_expert_and_empty_experts():
     assert (ref["counts"] == 0).sum() == 14
 
 
+@pytest.mark.parametrize("E,k", [(5, 5), (64, 8), (128, 1), (128, 32), (200, 4), (256, 17), (256, 32)],
+                         ids=lambda v: str(v))
+def test_top_k_on_tied_logits(E, k):
+    # Top-k over given logits with many equal scores (rounded to 0.5): descending order,
+    # equal scores to the lower expert id.  The expert counts cover 8 and 16 logits per
+    # lane of the row kernel (E <= 128, <= 256, the most the router takes), k past 16 (two
+    # entries per lane) and k = E.
+    s = synth.spec("mixtral_like", T=130, H=64, I=64, E=E, k=k, L=E)
+    rng = np.random.default_rng(E * 100 + k)
+    lg = (np.round(rng.standard_normal((s.T, E)) * 2) / 2).astype(np.float32)
+    lg[:3] = 1.5                                   # whole rows tied
+    lg[3, ::7] = 9.0                               # a tie at the top across the row
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    r = layer.route(x, logits_in=torch.from_numpy(lg).cuda(), want_topk_logit=True)
+    ref = oracle.route(None, None, None, k, logits=lg.astype(np.float64))
+    say(f"[edges] top-k on tied logits E={E} k={k}")
+    np.testing.assert_array_equal(np_of(r["topk_ids"]), ref["topk_ids"])
+    np.testing.assert_array_equal(np_of(r["topk_logit"]), ref["topk_logit"].astype(np.float32))
+    np.testing.assert_allclose(np_of(r["topk_w"]), ref["topk_w"], rtol=0, atol=2e-7)
+
+
 def test_capacity_with_tied_scores():
     # expert 0 is everyone's first choice with the same score: the lower tokens win
     s = synth.spec("skewed_capacity", T=2000, H=64, I=64, E=8, k=2, L=8, capacity_factor=1.0)
