@@ -477,12 +477,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__
 }
 
 // ---- place (scatter + gather in one pass, no capacity cut) -------------------
-// kPlaceSplit blocks share one chunk of kDispatchTokens tokens: each ranks all
-// of the chunk's pairs exactly like the scatter kernel (so the rows are the
-// same), the first also writes sorted_pairs/pair_row, and each copies the
-// rows of its quarter of the chunk's tokens, token-major (one read of x[t],
-// one write per kept local pair).
-constexpr int kPlaceSplit = 4;
+// `split` blocks share one chunk of kDispatchTokens tokens: each ranks all of
+// the chunk's pairs exactly like the scatter kernel (so the rows are the same),
+// the first also writes sorted_pairs/pair_row, and each copies the rows of its
+// share of the chunk's tokens, token-major (one read of x[t], one write per
+// kept local pair).  The split is at least 4 and large enough that a small
+// batch still spreads its row copies over ~256 CUs (a decode batch of one
+// chunk: 64 blocks of one token each).
+constexpr int kMinPlaceSplit = 4, kMaxPlaceSplit = kDispatchTokens;
+int place_split(int nblk) {  // power of two, kDispatchTokens divisible by it
+  int s = kMinPlaceSplit;
+  while (s < kMaxPlaceSplit && int64_t(nblk) * s < 256) s *= 2;
+  return s;
+}
 // With few chunks and experts the place blocks find their own bases: every
 // block sums the chunk histograms it needs (no separate scan launch).
 constexpr int kFuseEntries = 16384;  // chunks x experts up to which the scan is folded in
@@ -499,14 +506,14 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
                                                                  int32_t* __restrict__ sorted_pairs,
                                                                  int32_t* __restrict__ pair_row,
                                                                  const u32x4_t* __restrict__ x, int vec_per_row,
-                                                                 u32x4_t* __restrict__ xs) {
+                                                                 u32x4_t* __restrict__ xs, int split) {
   extern __shared__ int32_t sh[];
   constexpr int kWaves = kDispatchThreads / 64;
   int32_t* run = sh;                      // [L]
   int32_t* cnt = sh + L;                  // [kWaves][L]
   int32_t* pos = sh + L * (1 + kWaves);   // [kDispatchTokens * k] row of each of the chunk's pairs, -1 if none
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int chunk = blockIdx.x / kPlaceSplit, part = blockIdx.x % kPlaceSplit;
+  const int chunk = blockIdx.x / split, part = blockIdx.x % split;
   const int64_t t0 = int64_t(chunk) * kDispatchTokens;
   const int ntk = int(min<int64_t>(kDispatchTokens, ntok - t0));
   const int np = ntk * k;
@@ -618,21 +625,26 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
     __syncthreads();
   }
 
-  // copy this part's tokens: wave w takes tokens part*16 + 4w .. +3 of the chunk
-  constexpr int kTokPerPart = kDispatchTokens / kPlaceSplit;
+  // copy this part's tokens (tpp of the chunk): with at least one token per wave each
+  // wave takes whole tokens, else the waves on a token split its columns
+  const int tpp = kDispatchTokens / split;
+  const int wpt = tpp >= kWaves ? 1 : kWaves / tpp;  // waves per token
+  const int tpw = tpp >= kWaves ? tpp / kWaves : 1;  // tokens per wave
+  const int tw0 = part * tpp + (tpp >= kWaves ? wave * tpw : wave / wpt);
+  const int cper = (vec_per_row + wpt - 1) / wpt;
+  const int c_lo = (wave % wpt) * cper, c_hi = min(vec_per_row, c_lo + cper);
   constexpr int kUnroll = 4;
-  for (int tt = part * kTokPerPart + wave * (kTokPerPart / kWaves);
-       tt < part * kTokPerPart + (wave + 1) * (kTokPerPart / kWaves) && tt < ntk; ++tt) {
+  for (int tt = tw0; tt < tw0 + tpw && tt < ntk; ++tt) {
     const int my_row = lane < k ? pos[tt * k + lane] : -1;
     const uint64_t kept = __ballot(my_row >= 0);
     if (kept == 0) continue;
     const u32x4_t* src = x + size_t(t0 + tt) * vec_per_row;
-    for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kUnroll) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 64 * kUnroll) {
       u32x4_t v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < vec_per_row) v[u] = src[c];
+        if (c < c_hi) v[u] = src[c];
       }
       for (uint64_t mk = kept; mk != 0; mk &= mk - 1) {
         const int j = __ffsll((unsigned long long)mk) - 1;
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int c = c0 + u * 64 + lane;
-          if (c < vec_per_row) dst[c] = v[u];
+          if (c < c_hi) dst[c] = v[u];
         }
       }
     }
@@ -686,10 +698,11 @@ moe_status launch_dispatch(const DispatchArgs& a) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
       if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_place: LDS attribute: %s", hipGetErrorString(e));
     }
-    MOE_LAUNCH("dispatch_place", kern, dim3(unsigned(nblk) * kPlaceSplit), dim3(kDispatchThreads), lds, a.s,
+    const int split = place_split(nblk);
+    MOE_LAUNCH("dispatch_place", kern, dim3(unsigned(nblk) * split), dim3(kDispatchThreads), lds, a.s,
                a.topk_ids, d->num_tokens, d->top_k, begin, L, a.scr.blk_base, a.scr.blk_all, nblk, E, a.counts,
                a.offsets, a.num_dropped, a.sorted_pairs, a.pair_row, static_cast<const u32x4_t*>(a.x), vec_per_row,
-               static_cast<u32x4_t*>(a.x_sorted));
+               static_cast<u32x4_t*>(a.x_sorted), split);
   }
   return MOE_OK;
 }
