@@ -144,7 +144,8 @@ def moe_workspace_size(d: LayerDesc, stage: int) -> int:
 
 
 def moe_profile_events(handles) -> None:
-    """handles: list of hipEvent_t values (ints), or None/[] to switch timing off."""
+    """handles: list of hipEvent_t values (ints; None for both of a kernel's pair skips it),
+    or None/[] to switch timing off."""
     if not handles:
         _check(lib().moe_profile_events(None, 0))
         return

@@ -38,12 +38,14 @@ moe_status set_error(moe_status st, const char* fmt, ...) {
 
 void prof_before(const char* name, hipStream_t s) {
   if (g_kernel_idx < 64) g_kernel_names[g_kernel_idx] = name;
-  if (2 * g_kernel_idx + 1 < g_prof_count) (void)hipEventRecord(g_prof_events[2 * g_kernel_idx], s);
+  if (2 * g_kernel_idx + 1 < g_prof_count && g_prof_events[2 * g_kernel_idx] != nullptr)
+    (void)hipEventRecord(g_prof_events[2 * g_kernel_idx], s);
 }
 
 moe_status prof_after(const char* name, hipStream_t s) {
   const hipError_t e = hipGetLastError();
-  if (2 * g_kernel_idx + 1 < g_prof_count) (void)hipEventRecord(g_prof_events[2 * g_kernel_idx + 1], s);
+  if (2 * g_kernel_idx + 1 < g_prof_count && g_prof_events[2 * g_kernel_idx + 1] != nullptr)
+    (void)hipEventRecord(g_prof_events[2 * g_kernel_idx + 1], s);
   ++g_kernel_idx;
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
   return MOE_OK;
@@ -292,9 +294,11 @@ moe_status moe_profile_events(void* const* events, int32_t count) {
     g_prof_count = 0;
     return MOE_OK;
   }
-  if (count > 64) return set_error(MOE_ERR_INVALID_ARG, "at most 64 profiling events");
+  if (count > 64 || count % 2 != 0)
+    return set_error(MOE_ERR_INVALID_ARG, "profiling events: an even count of at most 64 (got %d)", count);
   for (int i = 0; i < count; ++i) {
-    if (events[i] == nullptr) return set_error(MOE_ERR_INVALID_ARG, "profiling event %d is NULL", i);
+    if ((events[i] == nullptr) != (events[i ^ 1] == nullptr))
+      return set_error(MOE_ERR_INVALID_ARG, "profiling events %d and %d: give both or neither", i & ~1, i | 1);
     g_prof_events[i] = static_cast<hipEvent_t>(events[i]);
   }
   g_prof_count = count;

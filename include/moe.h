@@ -129,8 +129,9 @@ moe_status moe_workspace_size(const moe_layer_desc* d, int32_t stage, size_t* by
 /* Optional kernel timing, for benchmarks.  While set (events != NULL), every
  * library call on this thread records events[2i] on its stream just before
  * its i-th kernel launch and events[2i+1] just after it, for i < count/2.
- * events are hipEvent_t handles created by the caller.  count == 0 or
- * events == NULL switches timing off. */
+ * events are hipEvent_t handles created by the caller; a NULL pair skips
+ * kernel i (give both of a pair or neither).  count must be even and at most
+ * 64.  count == 0 or events == NULL switches timing off. */
 moe_status moe_profile_events(void* const* events, int32_t count);
 
 /* Name of the i-th kernel launched by the last library call on this thread,
