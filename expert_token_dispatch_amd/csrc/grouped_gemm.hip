@@ -865,14 +865,15 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
 // expert that received no rows returns before touching its weights.
 namespace skinny {
 
-constexpr int kThreads = 256, kUnroll = 8, kMaxRowBlocks = 4;
+constexpr int kThreads = 256, kMaxRowBlocks = 4;
 
 bool supported(int K) { return K % 32 == 0; }
 
 // Each wave streams two sets of 16 weight rows: for gate/up the gate and the
 // up rows of the same 16 output columns, for down two adjacent groups of 16
 // output columns.  So a block (four waves) covers 64 gate/up columns or 128
-// down columns, and every lane keeps two weight loads per k step in flight.
+// down columns.  The k loop is double-buffered in registers: the loads of the
+// next two 32-k steps are in flight while the MFMAs of the current two run.
 template <int NMAT>
 constexpr int cols_per_block() { return NMAT == 2 ? 64 : 128; }
 
@@ -909,27 +910,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 #pragma unroll
       for (int rb = 0; rb < kMaxRowBlocks; ++rb) acc[m][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    int k0 = 0;
-    for (; k0 + 32 * kUnroll <= K; k0 += 32 * kUnroll) {
-      bf16x8_t w0[kUnroll], w1[kUnroll], a0[kUnroll];
+    // two register sets of kPipe k steps: the loads of the next set are in flight
+    // while the MFMAs of the current one run
+    constexpr int kPipe = 2;
+    bf16x8_t w0[2][kPipe], w1[2][kPipe], a0[2][kPipe];
+    const int nset = K / (32 * kPipe);
+    auto load_set = [&](int b, int k0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        w0[u] = *reinterpret_cast<const bf16x8_t*>(bs0 + k0 + 32 * u);
-        w1[u] = *reinterpret_cast<const bf16x8_t*>(bs1 + k0 + 32 * u);
-        a0[u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);  // first row block: loaded with the weights
+      for (int u = 0; u < kPipe; ++u) {
+        w0[b][u] = *reinterpret_cast<const bf16x8_t*>(bs0 + k0 + 32 * u);
+        w1[b][u] = *reinterpret_cast<const bf16x8_t*>(bs1 + k0 + 32 * u);
+        a0[b][u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);
       }
+    };
+    auto mma_set = [&](int b, int k0) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kPipe; ++u) {
 #pragma unroll
         for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
           if (rb < nrb) {
-            const bf16x8_t a = rb == 0 ? a0[u] : *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0 + 32 * u);
-            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0[u], acc[0][rb], 0, 0, 0);
-            acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1[u], acc[1][rb], 0, 0, 0);
+            const bf16x8_t a = rb == 0 ? a0[b][u] : *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0 + 32 * u);
+            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0[b][u], acc[0][rb], 0, 0, 0);
+            acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1[b][u], acc[1][rb], 0, 0, 0);
           }
         }
       }
+    };
+    if (nset > 0) load_set(0, 0);
+    int set = 0;
+    for (; set + 2 <= nset; set += 2) {
+      load_set(1, (set + 1) * 32 * kPipe);
+      mma_set(0, set * 32 * kPipe);
+      if (set + 2 < nset) load_set(0, (set + 2) * 32 * kPipe);
+      mma_set(1, (set + 1) * 32 * kPipe);
     }
+    if (set < nset) mma_set(0, set * 32 * kPipe);
+    int k0 = nset * 32 * kPipe;
     for (; k0 < K; k0 += 32) {
       const bf16x8_t w0 = *reinterpret_cast<const bf16x8_t*>(bs0 + k0);
       const bf16x8_t w1 = *reinterpret_cast<const bf16x8_t*>(bs1 + k0);
