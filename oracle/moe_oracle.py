@@ -22,6 +22,11 @@ Sources (cited by page title and section):
         - "Load balancing and capacity": each expert takes at most a fixed
           number of tokens per batch (e.g. 1.25x the even share); overflow
           tokens skip that expert and pass through the residual unchanged.
+          Bias-based balancing: a per-expert bias is added to the router
+          scores for choosing experts only, and after every step it goes down
+          for overloaded experts and up for idle ones.  The same section:
+          each token's experts lie on at most a few of the nodes that hold
+          them (node-limited routing).
 
 Readings where the pages are silent (each is listed in the design notes):
   * top-k ties go to the lower expert id; slot j holds the j-th best score;
@@ -36,7 +41,18 @@ Readings where the pages are silent (each is listed in the design notes):
   * within an expert's segment, pairs appear in ascending pair index
     p = t*k + j (a token picks an expert at most once, so this is ascending
     token order);
-  * the layer output excludes the residual branch.
+  * the layer output excludes the residual branch;
+  * routing with a selection bias: experts are chosen by logit + bias, added
+    in float32 (the precision the kernel decides in); the order, the weights
+    (softmax over the k chosen) and the capacity ranking use the router
+    logits without the bias;
+  * the bias step: b_e -= gamma for experts with more than the mean load
+    (c_e * E > sum c), b_e += gamma for those with less, unchanged at the
+    mean; float32 state, one rounding per step;
+  * group-limited routing: the E experts form G contiguous groups of E/G
+    (the nodes); a group scores its best expert's selection score; each
+    token keeps the M best groups (equal scores to the lower group) and
+    takes its k experts from those groups only.
 
 All floating-point work is float64 on the exact input values.  A top-k or
 capacity decision made on given float32 logits compares those float32 values
@@ -65,6 +81,10 @@ __all__ = [
     "grouped_ffn",
     "combine",
     "route",
+    "selection_scores",
+    "group_allowed",
+    "route_with_options",
+    "selection_bias_update",
     "dispatch",
     "layer_forward",
     "ep_local_range",
@@ -131,6 +151,83 @@ def route(x, w_router, b_router, k: int, logits: Optional[np.ndarray] = None) ->
     ids = topk_select(logits, k)
     chosen = np.take_along_axis(logits, ids, axis=1)
     return {"logits": logits, "topk_ids": ids, "topk_logit": chosen, "topk_w": softmax_over_k(chosen)}
+
+
+# --------------------------------------------------------------------------- #
+# step 1 variants  ([UL] "Load balancing and capacity": bias-based balancing,
+#                   node-limited routing)
+# --------------------------------------------------------------------------- #
+def selection_scores(logits: np.ndarray, selection_bias: Optional[np.ndarray]) -> np.ndarray:
+    """Scores the experts are chosen by: logit + per-expert bias, in float32.
+
+    The bias only steers the choice.  The sum is formed in float32 because a
+    float32 kernel takes the same integer decisions from the same sums; the
+    float64 result holds those float32 values exactly.
+    """
+    if selection_bias is None:
+        return logits
+    s32 = logits.astype(np.float32) + selection_bias.astype(np.float32)[None, :]
+    return s32.astype(np.float64)
+
+
+def group_allowed(scores: np.ndarray, num_groups: int, max_groups: int) -> np.ndarray:
+    """[T, E] bool: experts in the max_groups best of num_groups contiguous groups.
+
+    A group's score is the largest score among its experts; groups are
+    ranked by it, equal scores to the lower group index.
+    """
+    T, E = scores.shape
+    if num_groups <= 1 or max_groups >= num_groups:
+        return np.ones((T, E), dtype=bool)
+    if E % num_groups != 0:
+        raise ValueError("the experts must split evenly into the groups")
+    gsize = E // num_groups
+    gscore = scores.reshape(T, num_groups, gsize).max(axis=2)
+    best = np.argsort(-gscore, axis=1, kind="stable")[:, :max_groups]
+    keep = np.zeros((T, num_groups), dtype=bool)
+    np.put_along_axis(keep, best, True, axis=1)
+    return np.repeat(keep, gsize, axis=1)
+
+
+def route_with_options(logits: np.ndarray, k: int, selection_bias: Optional[np.ndarray] = None,
+                       num_groups: int = 0, max_groups: int = 0) -> dict:
+    """Top-k by the selection scores among the allowed experts; weights from the logits.
+
+    Allowed experts come first; among them the larger selection score, then
+    the lower expert id.  topk_logit and the softmax use the chosen experts'
+    logits without the bias.
+    """
+    T, E = logits.shape
+    scores = selection_scores(logits, selection_bias)
+    allowed = group_allowed(scores, num_groups, max_groups)
+    if np.any(allowed.sum(axis=1) < k):
+        raise ValueError("fewer allowed experts than k")
+    ids = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        # lexsort: last key first -> allowed before not, then higher score, then (stable) lower id
+        order = np.lexsort((-scores[t], ~allowed[t]))
+        ids[t] = order[:k]
+    chosen = np.take_along_axis(logits, ids, axis=1)
+    return {"logits": logits, "topk_ids": ids, "topk_logit": chosen, "topk_w": softmax_over_k(chosen)}
+
+
+def selection_bias_update(bias: np.ndarray, counts: np.ndarray, gamma: float) -> np.ndarray:
+    """One balancing step on the float32 bias from the expert loads of a batch.
+
+    Overloaded experts (load above the mean, tested as c_e * E > sum c on
+    integers) lose gamma, idle ones (below the mean) gain gamma, one float32
+    rounding each.
+    """
+    c = np.asarray(counts, dtype=np.int64)
+    E = c.shape[0]
+    total = int(c.sum())
+    b = np.asarray(bias, dtype=np.float32).copy()
+    g = np.float32(gamma)
+    over = c * E > total
+    under = c * E < total
+    b[over] = b[over] - g
+    b[under] = b[under] + g
+    return b
 
 
 # --------------------------------------------------------------------------- #

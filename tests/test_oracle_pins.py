@@ -412,6 +412,96 @@ def test_layer_forward_token_subset_matches_full():
 
 
 # --------------------------------------------------------------------------- #
+# 6b. routing variants (Ultralytics glossary "Expert Parallelism", section "Load
+#     balancing and capacity": bias-based balancing, node-limited routing)
+# --------------------------------------------------------------------------- #
+def test_variants_reduce_to_plain_routing():
+    rng = np.random.default_rng(11)
+    lg = rng.standard_normal((64, 16)).astype(np.float32).astype(np.float64)
+    plain = oracle.route(None, None, None, 4, logits=lg)
+    for kw in (dict(), dict(selection_bias=np.zeros(16, np.float32)), dict(num_groups=4, max_groups=4),
+               dict(num_groups=1, max_groups=1)):
+        r = oracle.route_with_options(lg, 4, **kw)
+        np.testing.assert_array_equal(r["topk_ids"], plain["topk_ids"])
+        np.testing.assert_array_equal(r["topk_w"], plain["topk_w"])
+
+
+def test_selection_bias_worked_example():
+    # logits 1.0 0.9 0.5 0.1, bias +0.6 on expert 2: choice by 1.0 0.9 1.1 0.1 -> experts 2, 0;
+    # the weights are a softmax over their unbiased logits 0.5 and 1.0
+    r = oracle.route_with_options(np.array([[1.0, 0.9, 0.5, 0.1]]), 2, np.array([0, 0, 0.6, 0], np.float32))
+    assert r["topk_ids"].tolist() == [[2, 0]]
+    assert r["topk_logit"].tolist() == [[0.5, 1.0]]
+    w2 = 1.0 / (1.0 + math.exp(0.5))
+    assert abs(r["topk_w"][0, 0] - w2) < 1e-15 and abs(r["topk_w"][0, 1] - (1.0 - w2)) < 1e-15
+
+
+def test_group_limit_worked_example():
+    # four groups of two: maxima 0.2 0.9 0.8 0.4.  One group: group 1 only, so 0.9 then
+    # 0.0 although 0.8 and 0.7 score higher elsewhere; two groups: groups 1 and 2.
+    lg = np.array([[0.1, 0.2, 0.9, 0.0, 0.8, 0.7, 0.3, 0.4]])
+    assert oracle.route_with_options(lg, 2, None, 4, 1)["topk_ids"].tolist() == [[2, 3]]
+    assert oracle.route_with_options(lg, 2, None, 4, 2)["topk_ids"].tolist() == [[2, 4]]
+    # equal group maxima: the lower group wins
+    lg = np.array([[0.5, 0.0, 0.0, 0.5, 0.1, 0.2]])
+    assert oracle.route_with_options(lg, 2, None, 3, 1)["topk_ids"].tolist() == [[0, 1]]
+
+
+@pytest.mark.parametrize("G,M", [(4, 1), (4, 2), (8, 3)])
+def test_group_limit_invariants(G, M):
+    rng = np.random.default_rng(G * 10 + M)
+    T, E, k = 200, 32, 4
+    lg = rng.standard_normal((T, E))
+    bias = (rng.standard_normal(E) * 0.5).astype(np.float32)
+    r = oracle.route_with_options(lg, k, bias, G, M)
+    sc = lg.astype(np.float32) + bias
+    for t in range(T):
+        ids = [int(e) for e in r["topk_ids"][t]]
+        assert len(set(ids)) == k
+        # the best expert overall is always taken first (its group has the best score)
+        assert ids[0] == bf_topk(sc[t].astype(np.float64), 1)[0]
+        assert len({e // (E // G) for e in ids}) <= M
+        # chosen scores never increase
+        assert all(sc[t][ids[j]] >= sc[t][ids[j + 1]] for j in range(k - 1))
+        # weights: a softmax over the chosen unbiased logits
+        ex = [math.exp(lg[t, e] - max(lg[t, i] for i in ids)) for e in ids]
+        assert np.allclose(r["topk_w"][t], [v / sum(ex) for v in ex], rtol=0, atol=1e-14)
+
+
+def test_bias_step_closed_forms():
+    # mean load 3.25: expert 3 is over, the others under; equal loads leave the bias alone
+    g = 2.0 ** -10
+    b = oracle.selection_bias_update(np.zeros(4, np.float32), np.array([3, 3, 3, 4]), g)
+    assert b.dtype == np.float32 and b.tolist() == [g, g, g, -g]
+    b0 = np.array([0.25, -1.5, 3.0], np.float32)
+    assert oracle.selection_bias_update(b0, np.array([7, 7, 7]), g).tolist() == b0.tolist()
+    # n steps at constant loads from zero: exactly -n*gamma*sign (multiples of 2^-10 are exact)
+    c = np.array([10, 0, 5, 5, 20])
+    b = np.zeros(5, np.float32)
+    for _ in range(37):
+        b = oracle.selection_bias_update(b, c, g)
+    assert b.tolist() == [-37 * g, 37 * g, 37 * g, 37 * g, -37 * g]
+
+
+def test_bias_steps_even_out_a_skewed_load():
+    # the section's claim: the bias balances the load.  A router that favours expert 0
+    # by one unit, 400 steps of choose-count-adjust; the largest load falls toward T*k/E.
+    rng = np.random.default_rng(3)
+    T, E, k = 256, 8, 2
+    lg = rng.standard_normal((T, E))
+    lg[:, 0] += 1.0
+    b = np.zeros(E, np.float32)
+    first = None
+    for _ in range(400):
+        ids = oracle.route_with_options(lg, k, b)["topk_ids"]
+        c = np.bincount(ids.ravel(), minlength=E)
+        first = c if first is None else first
+        b = oracle.selection_bias_update(b, c, 0.01)
+    assert first.max() > 1.8 * T * k / E
+    assert c.max() < 1.25 * T * k / E
+    assert b[0] < 0
+
+
 # 7. planted mistakes must be caught by the pins above
 # --------------------------------------------------------------------------- #
 def _pins_pass():
@@ -425,6 +515,10 @@ def _pins_pass():
         lambda: test_dispatch_invariants("skewed_capacity", {"T": 1024, "H": 64}),
         test_single_expert_is_dense_swiglu_mlp,
         test_k_equals_e_is_dense_soft_moe,
+        test_selection_bias_worked_example,
+        test_group_limit_worked_example,
+        lambda: test_group_limit_invariants(4, 2),
+        test_bias_step_closed_forms,
     ]
     for c in checks:
         try:
@@ -468,7 +562,34 @@ def _mut_capacity_highest(topk_ids, topk_logit, begin, L, C):
     return _ORIG["capacity_keep"](topk_ids, -topk_logit, begin, L, C)
 
 
-_ORIG = {n: getattr(oracle.moe_oracle, n) for n in ("counting_sort", "capacity_keep")}
+def _mut_weights_from_biased(logits, k, selection_bias=None, num_groups=0, max_groups=0):
+    r = _ORIG["route_with_options"](logits, k, selection_bias, num_groups, max_groups)
+    sc = oracle.selection_scores(logits, selection_bias)
+    r["topk_w"] = oracle.softmax_over_k(np.take_along_axis(sc, r["topk_ids"], axis=1))
+    return r
+
+
+def _mut_bias_sign(bias, counts, gamma):
+    return _ORIG["selection_bias_update"](bias, counts, -gamma)
+
+
+def _mut_group_sum(scores, num_groups, max_groups):
+    T, E = scores.shape
+    if num_groups <= 1 or max_groups >= num_groups:
+        return np.ones((T, E), dtype=bool)
+    gs = E // num_groups
+    best = np.argsort(-scores.reshape(T, num_groups, gs).sum(axis=2), axis=1, kind="stable")[:, :max_groups]
+    keep = np.zeros((T, num_groups), dtype=bool)
+    np.put_along_axis(keep, best, True, axis=1)
+    return np.repeat(keep, gs, axis=1)
+
+
+def _mut_group_ties_high(scores, num_groups, max_groups):
+    return _ORIG["group_allowed"](scores[:, ::-1], num_groups, max_groups)[:, ::-1]
+
+
+_ORIG = {n: getattr(oracle.moe_oracle, n) for n in ("counting_sort", "capacity_keep", "route_with_options",
+                                                     "selection_bias_update", "group_allowed")}
 
 
 @pytest.mark.parametrize("target,mutant", [
@@ -479,6 +600,10 @@ _ORIG = {n: getattr(oracle.moe_oracle, n) for n in ("counting_sort", "capacity_k
     ("expert_ffn", _mut_ffn_swap),
     ("counting_sort", _mut_unstable_sort),
     ("capacity_keep", _mut_capacity_highest),
+    ("route_with_options", _mut_weights_from_biased),
+    ("selection_bias_update", _mut_bias_sign),
+    ("group_allowed", _mut_group_sum),
+    ("group_allowed", _mut_group_ties_high),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, mutant):
     monkeypatch.setattr(oracle.moe_oracle, target, mutant)
