@@ -16,10 +16,12 @@ from ._lib import (  # noqa: F401
     MOE_STAGE_LAYER,
     MOE_STAGE_ROUTE,
     LayerDesc,
+    RouteOpts,
     MoeError,
     lib,
     lib_path,
     make_desc,
+    make_route_opts,
     moe_capacity,
     moe_combine,
     moe_dispatch,
@@ -27,11 +29,14 @@ from ._lib import (  # noqa: F401
     moe_grouped_ffn,
     moe_last_error,
     moe_layer_forward,
+    moe_layer_forward_ex,
     moe_max_pairs,
     moe_profile_events,
     moe_profile_kernel_count,
     moe_profile_kernel_name,
     moe_route,
+    moe_route_ex,
+    moe_selection_bias_update,
     moe_version,
     moe_workspace_size,
 )

@@ -37,6 +37,23 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
+class RouteOpts(ctypes.Structure):
+    """moe_route_opts: selection-only expert bias and groups per token (include/moe.h)."""
+    _fields_ = [
+        ("selection_bias", ctypes.c_void_p),
+        ("num_groups", ctypes.c_int32),
+        ("max_groups", ctypes.c_int32),
+    ]
+
+
+def make_route_opts(selection_bias=None, num_groups: int = 0, max_groups: int = 0) -> RouteOpts:
+    """selection_bias: float32 [E] device tensor or None.  The options keep a
+    reference to it, so the pointer stays valid while they are alive."""
+    o = RouteOpts(_p(selection_bias), int(num_groups), int(max_groups))
+    o._bias = selection_bias
+    return o
+
+
 def make_desc(num_tokens: int, hidden: int, intermediate: int, num_experts: int, top_k: int,
               local_begin: int = 0, local_count: Optional[int] = None, capacity_factor: float = 0.0,
               dtype="bf16") -> LayerDesc:
@@ -49,6 +66,7 @@ def make_desc(num_tokens: int, hidden: int, intermediate: int, num_experts: int,
 _LIB = None
 _VP = ctypes.c_void_p
 _DP = ctypes.POINTER(LayerDesc)
+_OP = ctypes.c_void_p  # moe_route_opts*, NULL allowed
 
 
 def lib() -> ctypes.CDLL:
@@ -78,6 +96,10 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (st, [_DP, _VP, _VP, _VP, _VP, _VP]),
             "moe_layer_forward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                        ctypes.c_size_t, _VP]),
+            "moe_route_ex": (st, [_DP, _OP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+            "moe_layer_forward_ex": (st, [_DP, _OP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          ctypes.c_size_t, _VP]),
+            "moe_selection_bias_update": (st, [_DP, _VP, _VP, ctypes.c_float, _VP]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -194,3 +216,27 @@ def moe_layer_forward(d, x, w_router, b_router, w_gate, w_up, w_down, y, ws, top
     _check(lib().moe_layer_forward(ctypes.byref(d), _p(x), _p(w_router), _p(b_router), _p(w_gate), _p(w_up),
                                    _p(w_down), _p(y), _p(topk_ids_out), _p(topk_w_out), _p(counts_out),
                                    _p(num_dropped_out), wp, wn, _s(stream)))
+
+
+# ---- routing options (glossary "Load balancing and capacity") --------------------
+def _opts(opts) -> Optional[int]:
+    return None if opts is None else ctypes.addressof(opts)
+
+
+def moe_route_ex(d, opts, x, w_router, b_router, topk_ids, topk_w, topk_logit=None, logits_in=None, logits_out=None,
+                 ws=None, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_route_ex(ctypes.byref(d), _opts(opts), _p(x), _p(w_router), _p(b_router), _p(logits_in),
+                              _p(logits_out), _p(topk_ids), _p(topk_w), _p(topk_logit), wp, wn, _s(stream)))
+
+
+def moe_layer_forward_ex(d, opts, x, w_router, b_router, w_gate, w_up, w_down, y, ws, topk_ids_out=None,
+                         topk_w_out=None, counts_out=None, num_dropped_out=None, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_forward_ex(ctypes.byref(d), _opts(opts), _p(x), _p(w_router), _p(b_router), _p(w_gate),
+                                      _p(w_up), _p(w_down), _p(y), _p(topk_ids_out), _p(topk_w_out),
+                                      _p(counts_out), _p(num_dropped_out), wp, wn, _s(stream)))
+
+
+def moe_selection_bias_update(d, counts, bias, gamma: float, stream=None) -> None:
+    _check(lib().moe_selection_bias_update(ctypes.byref(d), _p(counts), _p(bias), float(gamma), _s(stream)))

@@ -2,6 +2,7 @@
 // The operations are defined in moe.h; every check below runs before any
 // work is enqueued, following the Transformers "Expert parallelism" page's
 // convention of rejecting a bad configuration before anything is sharded.
+#include <cmath>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -252,6 +253,33 @@ moe_status combine_checks(const void* y_sorted, const int32_t* pair_row, const f
 
 using namespace moe;
 
+namespace moe {
+namespace {
+// Routing options: glossary "Load balancing and capacity" (selection bias, groups per token).
+moe_status opts_checks(const moe_layer_desc* d, const moe_route_opts* o) {
+  if (o == nullptr || o->num_groups <= 1) return MOE_OK;
+  const int E = d->num_experts, G = o->num_groups;
+  if (G > 16) return set_error(MOE_ERR_UNSUPPORTED, "route options: num_groups above 16 is not supported (got %d)", G);
+  if (E % G != 0) return set_error(MOE_ERR_INVALID_ARG, "route options: num_groups %d does not divide E=%d", G, E);
+  if (o->max_groups < 1 || o->max_groups > G)
+    return set_error(MOE_ERR_INVALID_ARG, "route options: max_groups must be in [1, %d] (got %d)", G, o->max_groups);
+  if (int64_t(o->max_groups) * (E / G) < d->top_k)
+    return set_error(MOE_ERR_INVALID_ARG, "route options: %d groups of %d experts hold fewer than k=%d", o->max_groups,
+                     E / G, d->top_k);
+  return MOE_OK;
+}
+
+void apply_opts(RouteArgs& a, const moe_layer_desc* d, const moe_route_opts* o) {
+  if (o == nullptr) return;
+  a.sel_bias = o->selection_bias;
+  if (o->num_groups > 1 && o->max_groups < o->num_groups) {
+    a.group_size = d->num_experts / o->num_groups;
+    a.max_groups = o->max_groups;
+  }
+}
+}  // namespace
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
@@ -312,17 +340,36 @@ const char* moe_profile_kernel_name(int32_t i) {
 
 int32_t moe_profile_kernel_count(void) { return g_last_kernel_count; }
 
-moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_router, const float* b_router,
-                     const float* logits_in, float* logits_out, int32_t* topk_ids, float* topk_w, float* topk_logit,
-                     void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_route_ex(const moe_layer_desc* d, const moe_route_opts* opts, const void* x, const void* w_router,
+                        const float* b_router, const float* logits_in, float* logits_out, int32_t* topk_ids,
+                        float* topk_w, float* topk_logit, void* ws, size_t ws_bytes, void* stream) {
   CallScope scope;
   TRY(check_desc(d));
   if (d->num_tokens == 0) return MOE_OK;
   TRY(route_checks(d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit));
+  TRY(opts_checks(d, opts));
   if (logits_in == nullptr) TRY(check_ws(d, MOE_STAGE_ROUTE, ws, ws_bytes));
   RouteArgs a{d, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit,
               static_cast<float*>(ws), nullptr, static_cast<hipStream_t>(stream)};
+  apply_opts(a, d, opts);
   return launch_route(a);
+}
+
+moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_router, const float* b_router,
+                     const float* logits_in, float* logits_out, int32_t* topk_ids, float* topk_w, float* topk_logit,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return moe_route_ex(d, nullptr, x, w_router, b_router, logits_in, logits_out, topk_ids, topk_w, topk_logit, ws,
+                      ws_bytes, stream);
+}
+
+moe_status moe_selection_bias_update(const moe_layer_desc* d, const int32_t* counts, float* bias, float gamma,
+                                     void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (counts == nullptr || bias == nullptr)
+    return set_error(MOE_ERR_INVALID_ARG, "selection bias update: counts and bias are required");
+  if (!std::isfinite(gamma)) return set_error(MOE_ERR_INVALID_ARG, "selection bias update: gamma must be finite");
+  return launch_selection_bias_update(d, counts, bias, gamma, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* topk_ids, const float* topk_logit,
@@ -366,6 +413,15 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
                              const void* w_gate, const void* w_up, const void* w_down, void* y, int32_t* topk_ids_out,
                              float* topk_w_out, int32_t* counts_out, int64_t* num_dropped_out, void* ws,
                              size_t ws_bytes, void* stream) {
+  return moe_layer_forward_ex(d, nullptr, x, w_router, b_router, w_gate, w_up, w_down, y, topk_ids_out, topk_w_out,
+                              counts_out, num_dropped_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_route_opts* opts, const void* x,
+                                const void* w_router, const float* b_router, const void* w_gate, const void* w_up,
+                                const void* w_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                                int32_t* counts_out, int64_t* num_dropped_out, void* ws, size_t ws_bytes,
+                                void* stream) {
   CallScope scope;
   TRY(check_desc(d));
   if (d->num_tokens == 0) return MOE_OK;
@@ -380,12 +436,14 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
   TRY(dispatch_checks(d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped));
   TRY(ffn_checks(w.x_sorted, w.offsets, w_gate, w_up, w_down, w.y_sorted));
   TRY(combine_checks(w.y_sorted, w.pair_row, tw, y));
+  TRY(opts_checks(d, opts));
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   const DispatchScratch scr = carve_dispatch_scratch(d, w.dispatch);
   // the router's top-k kernel also writes the per-chunk expert histograms
   RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, ids, tw, cap ? w.topk_logit : nullptr,
                static_cast<float*>(w.route), scr.blk_all, s};
+  apply_opts(ra, d, opts);
   TRY(launch_route(ra));
   DispatchArgs da{d, x, ids, w.topk_logit, counts, w.offsets, w.sorted_pairs, w.pair_row, w.x_sorted, dropped,
                   scr, capacity_of(d), true, s};

@@ -47,9 +47,14 @@ struct RouteArgs {
   float* partial;       // route scratch: per-slice partial logits
   int32_t* blk_counts;  // optional [dispatch_blocks(T), E]: per-chunk expert histogram for dispatch
   hipStream_t s;
+  const float* sel_bias = nullptr;  // optional [E]: added to the logits for choosing experts only
+  int group_size = 0;               // experts per group when the groups per token are limited, else 0
+  int max_groups = 0;               // groups a token may use (with group_size)
 };
 size_t route_scratch_bytes(const moe_layer_desc* d);
 moe_status launch_route(const RouteArgs& a);
+moe_status launch_selection_bias_update(const moe_layer_desc* d, const int32_t* counts, float* bias, float gamma,
+                                        hipStream_t s);
 
 // Dispatch scratch, carved from the caller's workspace.
 struct DispatchScratch {

@@ -292,7 +292,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
                                                                const float* __restrict__ br, float* __restrict__ logits_out,
                                                                int32_t* __restrict__ ids, float* __restrict__ tw,
                                                                float* __restrict__ tl, int32_t* __restrict__ blk_counts,
-                                                               int ntok, int E, int k) {
+                                                               int ntok, int E, int k, const float* __restrict__ sel_bias,
+                                                               int gsize, int max_groups) {
   extern __shared__ float sh[];
   const int ld = 16 * VPL + 4;                 // row stride: a lane's VPL logits are 16-byte aligned
   float* lg = sh;                              // [64][ld]
@@ -320,6 +321,47 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
 #pragma unroll
     for (int c = 0; c < VPL; ++c)
       if (r * VPL + c >= E) taken |= 1u << c;  // past the last expert
+    // selection scores: the logits plus the selection bias (a float32 sum), if any
+    float sc[VPL];
+#pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      sc[c] = v[c];
+      if (sel_bias != nullptr && r * VPL + c < E) {
+        const float t = v[c] + sel_bias[r * VPL + c];
+        sc[c] = t == t ? t : -INFINITY;
+      }
+    }
+    if (gsize > 0) {
+      // group-limited routing: lane g < G scores group g (its best selection score), then
+      // max_groups rounds of row max / lowest group keep the best groups; experts of
+      // the other groups count as taken
+      const int G = E / gsize;
+      float gs = -INFINITY;
+      if (r < G) {
+        const float* row = lg + m * ld + r * gsize;
+        for (int i = 0; i < gsize; ++i) {
+          float t = row[i];
+          t = t == t ? t : -INFINITY;
+          if (sel_bias != nullptr) {
+            t += sel_bias[r * gsize + i];
+            t = t == t ? t : -INFINITY;
+          }
+          gs = fmaxf(gs, t);
+        }
+      }
+      bool avail = r < G;
+      unsigned chosen = 0;
+      for (int q = 0; q < max_groups; ++q) {
+        const float mx = row_max(avail ? gs : -INFINITY);
+        const int cand = (avail && gs == mx) ? r : 0x7FFFFFFF;
+        const int win = row_min(cand);
+        chosen |= 1u << win;
+        if (r == win) avail = false;
+      }
+#pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        if (!((chosen >> ((r * VPL + c) / gsize)) & 1u)) taken |= 1u << c;
+    }
     float sel_v[MAXK];
     int sel_i[MAXK];
 #pragma unroll
@@ -328,24 +370,30 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       sel_i[j] = 0;
       if (j < k) {
         // this lane's best untaken logit; a strict compare keeps the lower id on ties
-        float bv = -INFINITY;
+        float bv = -INFINITY, bl = -INFINITY;
         int bc = -1;
 #pragma unroll
         for (int c = 0; c < VPL; ++c)
-          if (!((taken >> c) & 1u) && (bc < 0 || v[c] > bv)) {
-            bv = v[c];
+          if (!((taken >> c) & 1u) && (bc < 0 || sc[c] > bv)) {
+            bv = sc[c];
+            bl = v[c];
             bc = c;
           }
         const float mx = row_max(bv);
         const int cand = (bc >= 0 && bv == mx) ? r * VPL + bc : 0x7FFFFFFF;
         const int win = row_min(cand);
         if (cand == win) taken |= 1u << bc;
-        sel_v[j] = mx;
+        // the chosen expert's logit without the bias (the winner lane's)
+        sel_v[j] = sel_bias != nullptr ? row_max(cand == win ? bl : -INFINITY) : mx;
         sel_i[j] = win;
         if (r == 0 && blk_counts != nullptr) atomicAdd(&hist[win], 1);
       }
     }
-    const float top = sel_v[0];
+    // the largest chosen logit (the first one, unless a selection bias reordered them)
+    float top = sel_v[0];
+#pragma unroll
+    for (int j = 1; j < MAXK; ++j)
+      if (j < k) top = fmaxf(top, sel_v[j]);
     float ex[MAXK];
     float sum = 0.0f;
 #pragma unroll
@@ -382,6 +430,28 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   if (blk_counts != nullptr) {
     __syncthreads();
     for (int e = tid; e < E; e += kRowThreads) blk_counts[size_t(blockIdx.x) * E + e] = hist[e];
+  }
+}
+
+// ---- one balancing step on the selection bias --------------------------------
+// Ultralytics glossary "Expert Parallelism", section "Load balancing and
+// capacity": after each step the bias goes down for overloaded experts and up
+// for idle ones.  Overloaded means more than the mean load, tested on integers
+// (counts[e] * E > total); at the mean the bias stays.
+__global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __restrict__ counts, float* __restrict__ bias,
+                                                           int E, float gamma) {
+  __shared__ long long part[16];
+  long long t = 0;
+  for (int e = threadIdx.x; e < E; e += 1024) t += counts[e];
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = t;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) total += part[w];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const long long c = (long long)counts[e] * E;
+    if (c > total) bias[e] = bias[e] - gamma;
+    else if (c < total) bias[e] = bias[e] + gamma;
   }
 }
 
@@ -440,7 +510,8 @@ moe_status launch_topk_rows(const RouteArgs& a, const float* partial, int nslice
   }
   const dim3 grid(unsigned((ntok + kTopkTok - 1) / kTopkTok));
   MOE_LAUNCH("route_topk", kern, grid, dim3(kRowThreads), lds, a.s, partial, nslice, bias, a.logits_out,
-             a.topk_ids, a.topk_w, a.topk_logit, a.blk_counts, ntok, E, d->top_k);
+             a.topk_ids, a.topk_w, a.topk_logit, a.blk_counts, ntok, E, d->top_k, a.sel_bias, a.group_size,
+             a.max_groups);
   return MOE_OK;
 }
 
@@ -479,6 +550,12 @@ moe_status route_t(const RouteArgs& a) {
 size_t route_scratch_bytes(const moe_layer_desc* d) {
   const Split sp = d->dtype == MOE_BF16 ? plan<bf16_t>(d) : plan<float>(d);
   return align_up(size_t(sp.slices) * size_t(d->num_tokens) * d->num_experts * sizeof(float), 256);
+}
+
+moe_status launch_selection_bias_update(const moe_layer_desc* d, const int32_t* counts, float* bias, float gamma,
+                                        hipStream_t s) {
+  MOE_LAUNCH("route_bias_update", bias_update_kernel, dim3(1), dim3(1024), 0, s, counts, bias, d->num_experts, gamma);
+  return MOE_OK;
 }
 
 moe_status launch_route(const RouteArgs& a) {

@@ -57,7 +57,7 @@ class MoELayer:
         return torch.empty(shape, dtype=dtype, device=self.device)
 
     # ---- stages ------------------------------------------------------------
-    def route(self, x, logits_in=None, want_logits=False, want_topk_logit=None):
+    def route(self, x, logits_in=None, want_logits=False, want_topk_logit=None, opts=None):
         d = self.desc
         T, k, E = d.num_tokens, d.top_k, d.num_experts
         out = {"topk_ids": self._empty((T, k), torch.int32), "topk_w": self._empty((T, k), torch.float32)}
@@ -65,8 +65,8 @@ class MoELayer:
             want_topk_logit = d.capacity_factor > 0
         out["topk_logit"] = self._empty((T, k), torch.float32) if want_topk_logit else None
         out["logits"] = self._empty((T, E), torch.float32) if want_logits else None
-        L.moe_route(d, x, self.w_router, self.b_router, out["topk_ids"], out["topk_w"], out["topk_logit"],
-                    logits_in=logits_in, logits_out=out["logits"], ws=self.workspace(L.MOE_STAGE_ROUTE))
+        L.moe_route_ex(d, opts, x, self.w_router, self.b_router, out["topk_ids"], out["topk_w"], out["topk_logit"],
+                       logits_in=logits_in, logits_out=out["logits"], ws=self.workspace(L.MOE_STAGE_ROUTE))
         return out
 
     def dispatch(self, x, topk_ids, topk_logit=None):
@@ -98,18 +98,25 @@ class MoELayer:
         L.moe_combine(d, y_sorted, pair_row, topk_w, y)
         return y
 
-    def forward(self, x, y=None, topk_ids_out=None, topk_w_out=None, counts_out=None, num_dropped_out=None):
+    def forward(self, x, y=None, topk_ids_out=None, topk_w_out=None, counts_out=None, num_dropped_out=None,
+                opts=None):
+        """opts: an L.RouteOpts (selection bias, groups per token) or None."""
         d = self.desc
         if y is None:
             y = self._empty((d.num_tokens, d.hidden), x.dtype)
-        L.moe_layer_forward(d, x, self.w_router, self.b_router, self.w_gate, self.w_up, self.w_down, y,
-                            self.workspace(L.MOE_STAGE_LAYER), topk_ids_out, topk_w_out, counts_out,
-                            num_dropped_out)
+        L.moe_layer_forward_ex(d, opts, x, self.w_router, self.b_router, self.w_gate, self.w_up, self.w_down, y,
+                               self.workspace(L.MOE_STAGE_LAYER), topk_ids_out, topk_w_out, counts_out,
+                               num_dropped_out)
         return y
 
-    def staged(self, x, logits_in=None):
+    def update_selection_bias(self, counts, bias, gamma):
+        """One balancing step on the float32 [E] bias from a batch's [E] int32 expert loads."""
+        L.moe_selection_bias_update(self.desc, counts, bias, gamma)
+        return bias
+
+    def staged(self, x, logits_in=None, opts=None):
         """The four stage calls one after another; returns every intermediate."""
-        r = self.route(x, logits_in=logits_in, want_logits=True, want_topk_logit=True)
+        r = self.route(x, logits_in=logits_in, want_logits=True, want_topk_logit=True, opts=opts)
         dd = self.dispatch(x, r["topk_ids"], r["topk_logit"])
         ys = self.grouped_ffn(dd["x_sorted"], dd["offsets"])
         y = self.combine(ys, dd["pair_row"], r["topk_w"])

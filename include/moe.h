@@ -165,6 +165,44 @@ moe_status moe_route(const moe_layer_desc* d, const void* x, const void* w_route
                      int32_t* topk_ids, float* topk_w, float* topk_logit,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Routing options.  Ultralytics glossary "Expert Parallelism", section "Load
+ * balancing and capacity":
+ *  - bias-based balancing: a per-expert bias is added to the router scores
+ *    for choosing experts only.  Here experts are chosen by logit + bias (a
+ *    float32 sum), in that order, ties to the lower id; topk_logit, the
+ *    weights (softmax over the k chosen) and the capacity ranking use the
+ *    logits without the bias.
+ *  - node-limited routing: each token's experts lie on at most a few nodes.
+ *    Here the E experts form num_groups contiguous groups of E/num_groups;
+ *    a group scores its best expert's selection score, a token keeps the
+ *    max_groups best groups (equal scores to the lower group) and takes its
+ *    k experts from them.
+ * selection_bias: [E] float32 on the device, or NULL for none.
+ * num_groups: 0 or 1 for no limit, else 2..16 dividing E; max_groups: 1..num_groups,
+ * with max_groups * (E / num_groups) >= top_k.  Options are read at the call. */
+typedef struct moe_route_opts {
+  const float* selection_bias;
+  int32_t num_groups;
+  int32_t max_groups;
+} moe_route_opts;
+
+/* moe_route with options (NULL opts: same as moe_route).  Errors as moe_route,
+ * plus MOE_ERR_INVALID_ARG for group settings outside the ranges above. */
+moe_status moe_route_ex(const moe_layer_desc* d, const moe_route_opts* opts, const void* x, const void* w_router,
+                        const float* b_router, const float* logits_in, float* logits_out,
+                        int32_t* topk_ids, float* topk_w, float* topk_logit,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* One balancing step on the selection bias from a batch's expert loads (same
+ * section: after each step the bias goes down for overloaded experts and up
+ * for idle ones).  counts: [E] int32 device (moe_dispatch's counts, or
+ * moe_layer_forward's counts_out); bias: [E] float32 device, updated in
+ * place: bias[e] -= gamma where counts[e] * E > sum(counts), += gamma where
+ * counts[e] * E < sum(counts), unchanged at the mean.  One kernel on stream,
+ * no workspace.  MOE_ERR_INVALID_ARG for NULL pointers or a non-finite gamma. */
+moe_status moe_selection_bias_update(const moe_layer_desc* d, const int32_t* counts, float* bias, float gamma,
+                                     void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Stage 2: dispatch.  Transformers, "Token dispatch": every (token, expert) */
 /* pair goes to the owner of its expert.  On one GPU this is a histogram of  */
@@ -234,6 +272,14 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const void* x, const void*
                              const void* w_down, void* y, int32_t* topk_ids_out,
                              float* topk_w_out, int32_t* counts_out, int64_t* num_dropped_out,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward with routing options (see moe_route_opts); NULL opts is
+ * moe_layer_forward.  The same workspace. */
+moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_route_opts* opts, const void* x,
+                                const void* w_router, const float* b_router, const void* w_gate, const void* w_up,
+                                const void* w_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
+                                int32_t* counts_out, int64_t* num_dropped_out, void* ws, size_t ws_bytes,
+                                void* stream);
 
 #ifdef __cplusplus
 }

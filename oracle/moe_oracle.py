@@ -399,13 +399,15 @@ def combine(y_sorted: np.ndarray, pair_row: np.ndarray, topk_w: np.ndarray,
 # the whole layer
 # --------------------------------------------------------------------------- #
 def layer_forward(inp: dict, *, logits: Optional[np.ndarray] = None,
-                  tokens: Optional[np.ndarray] = None) -> dict:
+                  tokens: Optional[np.ndarray] = None, route_opts: Optional[dict] = None) -> dict:
     """All four steps on one layer's inputs (the dict the input generator returns).
 
     logits: optional [T,E] float32/float64 scores to route on instead of
             computing them (used to compare decisions on identical scores).
     tokens: optional token subset; routing and dispatch cover every token, the
             expert FFN and combine only the pairs of these tokens.
+    route_opts: optional {"selection_bias", "num_groups", "max_groups"} for
+            route_with_options (bias-based balancing, group-limited routing).
     """
     s = inp["spec"]
     dt = s.dtype
@@ -413,6 +415,9 @@ def layer_forward(inp: dict, *, logits: Optional[np.ndarray] = None,
     wr = decode(inp["w_router"], dt)
     br = None if inp.get("b_router") is None else np.asarray(inp["b_router"], dtype=np.float32).astype(np.float64)
     r = route(x, wr, br, s.k, logits=None if logits is None else np.asarray(logits, dtype=np.float64))
+    if route_opts is not None:
+        r = route_with_options(r["logits"], s.k, route_opts.get("selection_bias"), route_opts.get("num_groups", 0),
+                               route_opts.get("max_groups", 0))
     d = dispatch(r["topk_ids"], r["topk_logit"], s.E, s.local_begin, s.L, s.capacity_factor, x=x)
     out = {**r, **d}
     rows = None

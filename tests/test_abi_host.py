@@ -144,3 +144,28 @@ def test_zero_tokens_is_a_noop():
     assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None) == L.MOE_OK
     assert lib.moe_layer_forward(ctypes.byref(d), *([None] * 12), 0, None) == L.MOE_OK
     assert lib.moe_profile_kernel_count() == 0
+
+
+@pytest.mark.parametrize("G,M,code", [(3, 1, "INVALID_ARG"), (32, 1, "UNSUPPORTED"), (4, 0, "INVALID_ARG"),
+                                      (4, 5, "INVALID_ARG"), (8, 1, "INVALID_ARG")])
+def test_route_options_rejected_before_launch(G, M, code):
+    # groups must divide E (8 here), at most 16 of them, 1 <= max_groups <= num_groups, and
+    # the groups a token may use must hold at least k experts (8 groups of one, k = 2)
+    lib = L.lib()
+    d = etd.make_desc(16, 64, 64, 8, 2)
+    opts = L.make_route_opts(None, G, M)
+    st = lib.moe_route_ex(ctypes.byref(d), ctypes.addressof(opts), 256, 256, None, None, None, 256, 256, None, None,
+                          0, None)
+    assert st == getattr(L, "MOE_ERR_" + code), L.moe_last_error()
+    assert "route options" in L.moe_last_error()
+    st = lib.moe_layer_forward_ex(ctypes.byref(d), ctypes.addressof(opts), 256, 256, None, 256, 256, 256, 256, None,
+                                  None, None, None, 256, 1 << 30, None)
+    assert st == getattr(L, "MOE_ERR_" + code), L.moe_last_error()
+
+
+def test_selection_bias_update_arguments_checked():
+    lib = L.lib()
+    d = etd.make_desc(16, 64, 64, 8, 2)
+    assert lib.moe_selection_bias_update(ctypes.byref(d), None, 256, 0.001, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_selection_bias_update(ctypes.byref(d), 256, None, 0.001, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_selection_bias_update(ctypes.byref(d), 256, 256, float("nan"), None) == L.MOE_ERR_INVALID_ARG
