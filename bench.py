@@ -142,6 +142,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--route-groups", type=int, nargs=2, default=None, metavar=("G", "M"),
+                    help="group-limited routing: E experts in G contiguous groups, at most M per token")
+    ap.add_argument("--balance-gamma", type=float, default=None, metavar="GAMMA",
+                    help="route with a selection bias (zero at the start) and take one balancing step on it "
+                         "per layer step, from that step's expert loads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES bytes (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -169,6 +174,28 @@ def main():
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     dropped = torch.zeros((1,), dtype=torch.int64, device="cuda")
 
+    # routing options (glossary "Load balancing and capacity"): a step is then the layer
+    # forward with the options plus, with a bias, one balancing step on it
+    opts, sel_bias, step_counts = None, None, None
+    if args.route_groups is not None or args.balance_gamma is not None:
+        if args.balance_gamma is not None:
+            sel_bias = torch.zeros((s.E,), dtype=torch.float32, device="cuda")
+            step_counts = torch.zeros((s.E,), dtype=torch.int32, device="cuda")
+        G, M = args.route_groups if args.route_groups is not None else (0, 0)
+        opts = etd.make_route_opts(sel_bias, G, M)
+
+    fw_names = []
+
+    def step(capture_names=False, **kw):
+        if step_counts is not None and "counts_out" not in kw:
+            kw["counts_out"] = step_counts
+        layer.forward(x, y=y, opts=opts, **kw)
+        if capture_names:  # the forward's kernels, before the balancing call
+            fw_names[:] = [etd.moe_profile_kernel_name(i) for i in range(etd.moe_profile_kernel_count())]
+        if sel_bias is not None:
+            etd.moe_profile_events(None)  # the balancing step is a call of its own
+            layer.update_selection_bias(kw["counts_out"], sel_bias, args.balance_gamma)
+
     if args.copy_calibration > 0:
         n = args.copy_calibration
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -180,9 +207,9 @@ def main():
         log(f"[bench] calibration copy of {n} bytes done")
 
     # one run to learn the routing (pairs kept, experts touched) for the work model
-    layer.forward(x, y=y, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
+    step(capture_names=True, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
     torch.cuda.synchronize()
-    names = [etd.moe_profile_kernel_name(i) for i in range(etd.moe_profile_kernel_count())]
+    names = list(fw_names)
     ids_h = ids.cpu().numpy()
     cnt_h = counts.cpu().numpy()
     C = etd.moe_capacity(desc)
@@ -196,7 +223,7 @@ def main():
     log(f"[bench] kernels {names}; P={P}, experts touched {touched_experts}, dropped {int(dropped.item())}")
 
     for _ in range(args.warmup):
-        layer.forward(x, y=y)
+        step()
     torch.cuda.synchronize()
 
     hip = HipEvents()
@@ -217,7 +244,7 @@ def main():
     evs = [hip.create(2 * nk) for _ in range(nbd)]
     for i in range(nbd):
         etd.moe_profile_events(evs[i])
-        layer.forward(x, y=y)
+        step()
     torch.cuda.synchronize()
     etd.moe_profile_events(None)
     per_kernel = {}
@@ -243,7 +270,7 @@ def main():
     start.record()
     for i in range(args.steps):
         etd.moe_profile_events(tev[i])
-        layer.forward(x, y=y)
+        step()
     stop.record()
     torch.cuda.synchronize()
     etd.moe_profile_events(None)
@@ -288,7 +315,9 @@ def main():
         "data": "synthetic (seeded numpy draws; random-init router and experts)",
         "config": {"workload": s.name, "tokens": s.T, "hidden": s.H, "intermediate": s.I, "experts": s.E,
                    "top_k": s.k, "local_experts": [s.local_begin, s.local_begin + s.L],
-                   "capacity_factor": s.capacity_factor, "pairs_kept": P, "seed": s.seed},
+                   "capacity_factor": s.capacity_factor, "pairs_kept": P, "seed": s.seed,
+                   **({"route_groups": args.route_groups} if args.route_groups else {}),
+                   **({"balance_gamma": args.balance_gamma} if args.balance_gamma is not None else {})},
         "grouped_gemm_mfma_frac": round(gemm_frac, 4) if gemm_frac else None,
         "stages_us": {"route": stage("route"), "dispatch": stage("dispatch"), "grouped_ffn": stage("ffn"),
                       "combine": stage("combine")},

@@ -298,9 +298,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   const int ld = 16 * VPL + 4;                 // row stride: a lane's VPL logits are 16-byte aligned
   float* lg = sh;                              // [64][ld]
   int* hist = reinterpret_cast<int*>(sh + kTopkTok * ld);  // [E]
+  float* sb = sh + kTopkTok * ld + E;          // [E] selection bias, staged once per block
   const int tid = threadIdx.x;
   if (blk_counts != nullptr)
     for (int e = tid; e < E; e += kRowThreads) hist[e] = 0;
+  if (sel_bias != nullptr)
+    for (int e = tid; e < E; e += kRowThreads) sb[e] = sel_bias[e];
   const int t0 = blockIdx.x * kTopkTok;
   const int rows = min(kTopkTok, ntok - t0);
   load_logit_tile<kRowThreads>(partial, nslice, br, logits_out, ntok, E, t0, rows, ld, lg, tid);
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     for (int c = 0; c < VPL; ++c) {
       sc[c] = v[c];
       if (sel_bias != nullptr && r * VPL + c < E) {
-        const float t = v[c] + sel_bias[r * VPL + c];
+        const float t = v[c] + sb[r * VPL + c];
         sc[c] = t == t ? t : -INFINITY;
       }
     }
@@ -343,7 +346,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
           float t = row[i];
           t = t == t ? t : -INFINITY;
           if (sel_bias != nullptr) {
-            t += sel_bias[r * gsize + i];
+            t += sb[r * gsize + i];
             t = t == t ? t : -INFINITY;
           }
           gs = fmaxf(gs, t);
@@ -501,7 +504,7 @@ moe_status launch_topk_rows(const RouteArgs& a, const float* partial, int nslice
   const moe_layer_desc* d = a.d;
   const int ntok = int(d->num_tokens);
   const int E = d->num_experts;
-  const size_t lds = (size_t(kTopkTok) * (16 * VPL + 4) + size_t(E)) * sizeof(float);
+  const size_t lds = (size_t(kTopkTok) * (16 * VPL + 4) + 2 * size_t(E)) * sizeof(float);
   auto kern = topk_row_kernel<MAXK, VPL>;
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
