@@ -245,7 +245,7 @@ namespace big {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
-constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2, kThreads = 256;
+constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2;
 constexpr int kRowBytes = BK * 2;              // 128
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
@@ -276,7 +276,7 @@ constexpr int kSplitMinSteps = 32;   // K/BK from which the last round may be cu
 constexpr int kMaxSplit = 4;
 constexpr int kMaxParts = 96;        // pieces per XCD
 constexpr int kMaxTail = kMaxParts / kMaxSplit;
-constexpr size_t kPartBytes = size_t(kThreads) * 256 * sizeof(float);  // one piece's accumulators
+constexpr size_t kPartBytes = size_t(65536) * sizeof(float);  // one piece's accumulators (a 256 x 256 tile)
 constexpr float kPieceSteps = 0.4f;
 
 __device__ __forceinline__ int split_of(int r, int cpx, int smax, int nk) {
@@ -438,21 +438,25 @@ __device__ __forceinline__ void unit_job(const int32_t* __restrict__ offsets, co
   jb.nks = ((jb.part + 1) * nk) / jb.nparts - jb.kb;
 }
 
-// Tile shapes: regular 256 A rows x 256 B rows, waves 2 (M) x 2 (N); wide 128 A rows
-// x 512 B rows, waves side by side along N.  Either way a wave owns 128 A rows x
-// 128 B rows (4 x 4 MFMA 32x32 accumulators).
-template <bool WIDE>
+// Tile shapes: regular 256 A rows x 256 B rows, wide 128 A rows x 512 B rows.  With
+// NW = 4 waves (one per SIMD) a wave owns 128 A rows x 128 B rows (4 x 4 MFMA 32x32
+// accumulators, waves 2 x 2, or 1 x 4 for the wide tile); with NW = 8 (two per SIMD)
+// 128 A rows x 64 B rows (4 x 2 accumulators, waves 2 x 4, or 1 x 8).  NB = 16 / NW
+// B fragments per wave.
+template <bool WIDE, int NW>
 struct Shape {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int NB = 16 / NW;
   static constexpr int kA = WIDE ? BM / 2 : BM;          // A rows
   static constexpr int kB = WIDE ? 2 * BNE : BNE;        // B rows
   static constexpr int kStageA = kA * kRowBytes;
   static constexpr int kStage = (kA + kB) * kRowBytes;   // 64 KB regular, 80 KB wide
-  static constexpr int kLdA = kA / 32, kLdB = kB / 32;   // 1 KB direct loads per wave per stage
+  static constexpr int kLdA = kA / (8 * NW), kLdB = kB / (8 * NW);  // 1 KB direct loads per wave per stage
   static constexpr int kLd = kLdA + kLdB;
-  __device__ static int wm(int wave) { return WIDE ? 0 : wave >> 1; }
-  __device__ static int wn(int wave) { return WIDE ? wave : wave & 1; }
+  __device__ static int wm(int wave) { return WIDE ? 0 : wave / (NW / 2); }
+  __device__ static int wn(int wave) { return WIDE ? wave : wave % (NW / 2); }
 };
-constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true>::kStage;  // 160 KB
+constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true, 4>::kStage;  // 160 KB
 
 // ---- epilogue.  The products were formed as (weight rows) x (token rows), so
 // in the 32x32 accumulator layout lane l holds token row l & 31 and register
@@ -461,13 +465,14 @@ constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true>::kStage;  // 160 KB
 // and parks it in LDS, rows padded by 16 bytes; then every thread copies
 // 16-byte row chunks out, so each store instruction writes whole row pieces.
 // The caller has made sure no wave still reads the loop's LDS stages.
-template <int NMAT, bool WIDE>
-__device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_t* __restrict__ C, int row0, int rows,
-                                         int n0, int N) {
-  using S = Shape<WIDE>;
+template <int NMAT, bool WIDE, int NW>
+__device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds, bf16_t* __restrict__ C, int row0,
+                                         int rows, int n0, int N) {
+  using S = Shape<WIDE, NW>;
+  constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
   constexpr int RS = TC * 2 + 16;
-  constexpr int NJ = NMAT == 2 ? 2 : 4;
+  constexpr int NJ = NMAT == 2 ? NB / 2 : NB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = S::wm(wave), wn = S::wn(wave), fr = lane & 31, g = lane >> 5;
 #pragma unroll
@@ -480,11 +485,11 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_
         float v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + 2][4 * q + u] : acc[i][j][4 * q + u];
+          v[u] = NMAT == 2 ? silu(acc[i][j][4 * q + u]) * acc[i][j + NB / 2][4 * q + u] : acc[i][j][4 * q + u];
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
-        const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
+        const int cl = (NMAT == 2 ? wn * NB * 16 : wn * NB * 32) + j * 32 + 8 * q + 4 * g;
         *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
       }
     }
@@ -504,8 +509,8 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][4], char* lds, bf16_
 
 template <int NMAT>
 constexpr size_t lds_bytes() {
-  constexpr size_t reg = size_t(Shape<false>::kA) * ((NMAT == 2 ? BNE / 2 : BNE) * 2 + 16);
-  constexpr size_t wide = size_t(Shape<true>::kA) * ((NMAT == 2 ? BNE : 2 * BNE) * 2 + 16);
+  constexpr size_t reg = size_t(Shape<false, 4>::kA) * ((NMAT == 2 ? BNE / 2 : BNE) * 2 + 16);
+  constexpr size_t wide = size_t(Shape<true, 4>::kA) * ((NMAT == 2 ? BNE : 2 * BNE) * 2 + 16);
   constexpr size_t st = reg > wide ? reg : wide;
   return kLoopLdsMax > st ? kLoopLdsMax : st;
 }
@@ -516,11 +521,12 @@ __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslo
 }
 
 // One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
-template <int NMAT, bool WIDE>
+template <int NMAT, bool WIDE, int NW>
 __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
                                           const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
                                           const Job& jb, float* __restrict__ parts, char* lds) {
-  using S = Shape<WIDE>;
+  using S = Shape<WIDE, NW>;
+  constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   const int row0 = jb.row0, rows = jb.rows, n0 = jb.n0 * ON, kb = jb.kb, nks = jb.nks;
   // the wave index is uniform: keeping it in a scalar register makes every LDS
@@ -535,17 +541,17 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   // is a multiple of 16, that depends on i and the parity of j only.
   const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
   const int c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
-  const int a_lrow = (S::kA / 4) * wave + (lane >> 3);
+  const int a_lrow = (S::kA / NW) * wave + (lane >> 3);
   // buffer resources over the tile's rows of A and over the whole weight matrix
   // (its extent is under 4 GiB); a read outside either returns zeros
   const uint32_t a_bytes = uint32_t(min(int64_t(a_rows - row0) * K * 2, int64_t(0xFFFFFFFF)));
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(A + size_t(row0) * K), 0, a_bytes, kRsrcFlags);
   int b_lrow;
-  if (NMAT == 2) b_lrow = ((S::kB / 4) * wave + (lane >> 3)) & (S::kB / 2 - 1);  // waves 0-1 load gate rows, 2-3 up
-  else b_lrow = (S::kB / 4) * wave + (lane >> 3);
+  if (NMAT == 2) b_lrow = ((S::kB / NW) * wave + (lane >> 3)) & (S::kB / 2 - 1);  // first half of the waves: gate rows
+  else b_lrow = (S::kB / NW) * wave + (lane >> 3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(NMAT == 2 && wave >= 2 ? Bu : Bg), 0, uint32_t(N) * uint32_t(K) * 2u, kRsrcFlags);
+      const_cast<bf16_t*>(NMAT == 2 && wave >= NW / 2 ? Bu : Bg), 0, uint32_t(N) * uint32_t(K) * 2u, kRsrcFlags);
   // Rows past the segment (A) or past N (B) feed only outputs that are never
   // stored, so they may read any valid row: A takes the rows that follow (up
   // to the last row of the buffer), B wraps around to the first rows.  Letting
@@ -584,11 +590,11 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     }                                                                                                       \
   } while (0)
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -598,35 +604,44 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   const int fr = lane & 31;
   const int sw = (fr >> 1) & 7;
   const int g = lane >> 5;
-  int boffs[4];
+  int boffs[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int br = NMAT == 2 ? (j < 2 ? wn * 64 + j * 32 : S::kB / 2 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
+  for (int j = 0; j < NB; ++j) {
+    const int br = NMAT == 2 ? (j < NB / 2 ? wn * NB * 16 + j * 32 : S::kB / 2 + wn * NB * 16 + (j - NB / 2) * 32)
+                             : wn * NB * 32 + j * 32;
     boffs[j] = S::kStageA + (br + fr) * kRowBytes;
   }
   const int a_off = (wm * 128 + fr) * kRowBytes;
-  bf16x8_t fa[2][4], fb[2][4];
+  bf16x8_t fa[2][4], fb[2][NB];
 #define MOE_LOADF(buf_, st_, kc_)                                                                         \
   do {                                                                                                    \
     const int co_ = ((2 * (kc_) + g) ^ sw) * 16;                                                          \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
       fa[buf_][i] = *reinterpret_cast<const bf16x8_t*>((st_) + a_off + i * 32 * kRowBytes + co_);          \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                         \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                        \
       fb[buf_][j] = *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                            \
   } while (0)
 #define MOE_MMA(buf_)                                                                                     \
   do {                                                                                                    \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                       \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                      \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][i], acc[i][j], 0, 0, 0); \
   } while (0)
   // 8 x {MFMA, LDS read, MFMA}: the next chunk's fragment reads spread over the whole group
 #define MOE_PIPE_DS()                                                                                     \
   do {                                                                                                    \
-    _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                    \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                  \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                  \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                  \
+    if constexpr (NB == 4) {                                                                              \
+      _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                  \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+      }                                                                                                   \
+    } else {                                                                                              \
+      _Pragma("unroll") for (int p_ = 0; p_ < 4 + NB; ++p_) {                                             \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
+      }                                                                                                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - (4 + NB), 0);                                  \
     }                                                                                                     \
   } while (0)
 
@@ -637,6 +652,24 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   // of an XCD hit L2 together, and the second half still has three chunks to
   // land before the barrier that waits for it.
   constexpr int kHalf = S::kLd / 2;
+  // a chunk that also issues half a refill: its fragment reads first, then the loads
+  // spread over its 4 * NB MFMAs
+#define MOE_CHUNK_LOADS()                                                                                 \
+  do {                                                                                                    \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NB, 0);                                               \
+    if constexpr (NB == 4) {                                                                              \
+      _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                  \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                \
+        __builtin_amdgcn_sched_group_barrier(0x020, kHalf / 8, 0);                                        \
+      }                                                                                                   \
+      if constexpr (kHalf % 8 != 0) __builtin_amdgcn_sched_group_barrier(0x020, kHalf % 8, 0);           \
+    } else {                                                                                              \
+      _Pragma("unroll") for (int p_ = 0; p_ < kHalf; ++p_) {                                              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB / kHalf, 0);                                   \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                                \
+      }                                                                                                   \
+    }                                                                                                     \
+  } while (0)
   MOE_ISSUE(0, 0, S::kLd);
   if (nks > 1) {
     MOE_ISSUE(1, 0, kHalf);
@@ -653,13 +686,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     MOE_LOADF(1, st, 1);
     MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
     MOE_MMA(0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, kHalf / 8, 0);
-    }
-    if constexpr (kHalf % 8 != 0) __builtin_amdgcn_sched_group_barrier(0x020, kHalf % 8, 0);
+    MOE_CHUNK_LOADS();
     __builtin_amdgcn_sched_barrier(0);
     MOE_LOADF(0, st, 2);
     MOE_MMA(1);
@@ -675,13 +702,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     MOE_LOADF(0, lds + ((kt + 1) % kStages) * S::kStage, 0);
     MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
     MOE_MMA(1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, kHalf / 8, 0);
-    }
-    if constexpr (kHalf % 8 != 0) __builtin_amdgcn_sched_group_barrier(0x020, kHalf % 8, 0);
+    MOE_CHUNK_LOADS();
   }
   {
     const char* st = lds + ((nks - 1) % kStages) * S::kStage;
@@ -698,6 +719,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
 #undef MOE_LOADF
 #undef MOE_MMA
 #undef MOE_PIPE_DS
+#undef MOE_CHUNK_LOADS
 
   if (jb.nparts > 1) {
     // one piece of a split tile: park the accumulators for fixup_kernel
@@ -705,22 +727,22 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          dst[((i * 4 + j) * 4 + c) * kThreads + tid] =
+          dst[((i * NB + j) * 4 + c) * kThreads + tid] =
               f32x4_t{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
     return;
   }
   MOE_LGKMCNT0();
   block_barrier();  // every wave is done reading the last stage
-  epilogue<NMAT, WIDE>(acc, lds, C, row0, rows, n0, N);
+  epilogue<NMAT, WIDE, NW>(acc, lds, C, row0, rows, n0, N);
 }
 
-template <int NMAT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
+template <int NMAT, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                       const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+                                                       bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
                                                         const int32_t* __restrict__ tpre, int cpx, int smax,
                                                         float* __restrict__ parts) {
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
@@ -733,7 +755,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   // the tile prefix into LDS for the search (the loop's stages overwrite it later)
   int32_t* spre = reinterpret_cast<int32_t*>(lds);
-  for (int i = threadIdx.x; i <= L; i += kThreads) spre[i] = tpre[i];
+  for (int i = threadIdx.x; i <= L; i += NW * 64) spre[i] = tpre[i];
   __syncthreads();
   Job jb;
   unit_job(offsets, spre, L, NT, nk, cpx, xcd, xp, loc, jb);
@@ -742,24 +764,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   const bf16_t* Bg = B0 + boff;
   const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
   if (jb.wide)
-    tile_body<NMAT, true>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
+    tile_body<NMAT, true, NW>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
   else
-    tile_body<NMAT, false>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
+    tile_body<NMAT, false, NW>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
 }
 
 // Adds the pieces of each split tile in piece order and writes the tile.
 // kFixSub blocks share a tile; an item is one float4 of the accumulator
-// layout (thread t, float4 v: i = v/16, j = v/4 % 4, q = v % 4), that is four
-// adjacent output columns of one token row (for gate/up: the gate float4 and
-// its up partner j + 2).
+// layout of the NW-wave kernel (thread t, float4 v: i = v / (4 NB), j = v/4 % NB,
+// q = v % 4), that is four adjacent output columns of one token row (for
+// gate/up: the gate float4 and its up partner j + NB/2).
 constexpr int kFixSub = 8;
 
-template <int NMAT>
-__global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
+template <int NMAT, int NW>
+__global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
                                                          int L, int N, int K, const int32_t* __restrict__ tpre, int cpx,
                                                          int smax, const float* __restrict__ parts) {
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
-  constexpr int NV = NMAT == 2 ? 32 : 64;       // output float4s per thread of the tile
+  constexpr int kThreads = NW * 64, NB = 16 / NW;
+  constexpr int NJ = NMAT == 2 ? NB / 2 : NB;   // output column blocks per wave
+  constexpr int NV = 16 * NJ;                   // output float4s per thread of the tile
   constexpr int kPer = NV / kFixSub;            // items per thread of this block
   const int NT = (N + ON - 1) / ON;
   const int sub = blockIdx.x % kFixSub, tile = blockIdx.x / kFixSub;
@@ -777,22 +801,23 @@ __global__ __launch_bounds__(kThreads) void fixup_kernel(const int32_t* __restri
   for (int it = 0; it < kPer; ++it) {
     const int f = sub * kPer + it;  // float4 slot; consecutive threads read consecutive float4s
     const int t = threadIdx.x;
-    const int i = NMAT == 2 ? f / 8 : f / 16;
-    const int j = NMAT == 2 ? (f / 4) % 2 : (f / 4) % 4;
+    const int i = f / (4 * NJ);
+    const int j = (f / 4) % NJ;
     const int q = f % 4;
-    const int v = (i * 4 + j) * 4 + q;
+    const int v = (i * NB + j) * 4 + q;
+    constexpr int UP = (NB / 2) * 4;  // up partner: j + NB/2
     f32x4_t s = base[size_t(v) * kThreads + t];
-    f32x4_t su = NMAT == 2 ? base[size_t(v + 8) * kThreads + t] : s;  // up partner: j + 2
+    f32x4_t su = NMAT == 2 ? base[size_t(v + UP) * kThreads + t] : s;
     for (int p = 1; p < jb.nparts; ++p) {
       s += base[size_t(p) * pstride + size_t(v) * kThreads + t];
-      if (NMAT == 2) su += base[size_t(p) * pstride + size_t(v + 8) * kThreads + t];
+      if (NMAT == 2) su += base[size_t(p) * pstride + size_t(v + UP) * kThreads + t];
     }
     const int wave = t >> 6, lane = t & 63;
-    const int wm = jb.wide ? Shape<true>::wm(wave) : Shape<false>::wm(wave);
-    const int wn = jb.wide ? Shape<true>::wn(wave) : Shape<false>::wn(wave);
+    const int wm = jb.wide ? Shape<true, NW>::wm(wave) : Shape<false, NW>::wm(wave);
+    const int wn = jb.wide ? Shape<true, NW>::wn(wave) : Shape<false, NW>::wn(wave);
     const int fr = lane & 31, g = lane >> 5;
     const int rt = wm * 128 + i * 32 + fr;
-    const int cl = (NMAT == 2 ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * g;
+    const int cl = (NMAT == 2 ? wn * NB * 16 : wn * NB * 32) + j * 32 + 8 * q + 4 * g;
     if (rt < jb.rows && n0 + cl < N) {
       float o[4];
 #pragma unroll
@@ -822,11 +847,17 @@ int cus_per_xcd() {
 // K long enough to cut a partly filled last round
 bool splits(int K) { return K / BK >= kSplitMinSteps; }
 
-template <int NMAT>
-moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                  hipStream_t s) {
-  auto kern = gemm_kernel<NMAT>;
+// Eight waves (two per SIMD) for products shorter than kEightWaveSteps k steps, where
+// the per-tile fixed costs weigh most (same-box A/B: gpt-oss-like layer -4.5%,
+// skewed layer -1.5%); four for longer ones (mixtral-like layer: eight are 1% slower).
+constexpr int kEightWaveSteps = 64;
+
+template <int NMAT, int NW>
+moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
+                     bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                     hipStream_t s) {
+  constexpr int kThreads = NW * 64;
+  auto kern = gemm_kernel<NMAT, NW>;
   constexpr size_t lds = lds_bytes<NMAT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
@@ -843,10 +874,18 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
              int(max_pairs), tpre, cpx, smax, parts);
   if (smax > 1) {
     const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
-    MOE_LAUNCH(fname, fixup_kernel<NMAT>, dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s, offsets, C,
-               L, N, K, tpre, cpx, smax, static_cast<const float*>(parts));
+    MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
+               offsets, C, L, N, K, tpre, cpx, smax, static_cast<const float*>(parts));
   }
   return MOE_OK;
+}
+
+template <int NMAT>
+moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
+                  bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                  hipStream_t s) {
+  if (K / BK < kEightWaveSteps) return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s);
+  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s);
 }
 
 }  // namespace big
