@@ -23,6 +23,8 @@
 // fall in distinct banks.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -63,7 +65,9 @@ template <> struct Gemm<float> {
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // NMAT = 2: gate and up products with the SwiGLU epilogue; NMAT = 1: plain product.
-template <typename T, int NMAT>
+// Tiles of BMT (128 or 64) token rows x BN weight rows; the waves split them 2 x 2,
+// so a wave holds BMT/64 x 2 MFMA 32x32 blocks per matrix.
+template <typename T, int NMAT, int BMT>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restrict__ A,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const T* __restrict__ B0, const T* __restrict__ B1,
@@ -72,8 +76,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
   constexpr int BK = G::BK, kLd = G::kLd, FV = G::kFragVec;
   constexpr int EPV = 16 / int(sizeof(T));     // elements per 16-byte vector
   constexpr int CPR = BK / EPV;                // 16-byte chunks per tile row (4)
-  constexpr int CPT = BM * CPR / kThreads;     // chunks per thread per matrix (2)
-  static_assert(BM == BN, "one chunk map serves A and B");
+  constexpr int CPTA = BMT * CPR / kThreads;   // A chunks per thread (2 or 1)
+  constexpr int CPTB = BN * CPR / kThreads;    // B chunks per thread per matrix (2)
+  constexpr int MI = BMT / 64;                 // 32-row blocks per wave
 
   // ---- which expert and rows this block owns --------------------------------
   int g = blockIdx.x;
@@ -82,11 +87,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
     int prev = offsets[0];
     for (int i = 0; i < L; ++i) {
       const int nxt = offsets[i + 1];
-      const int tiles = (nxt - prev + BM - 1) / BM;
+      const int tiles = (nxt - prev + BMT - 1) / BMT;
       if (g < tiles) {
         expert = i;
-        row0 = prev + g * BM;
-        rows = min(BM, nxt - row0);
+        row0 = prev + g * BMT;
+        rows = min(BMT, nxt - row0);
         break;
       }
       g -= tiles;
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
   const size_t boff = size_t(expert) * N * K;
   const T* Bm[2] = {B0 + boff, NMAT > 1 ? B1 + boff : B0 + boff};
 
-  __shared__ __attribute__((aligned(16))) T As[2][BM * kLd];
+  __shared__ __attribute__((aligned(16))) T As[2][BMT * kLd];
   __shared__ __attribute__((aligned(16))) T Bs[2][NMAT][BN * kLd];
 
   const int tid = threadIdx.x;
@@ -106,39 +111,49 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
   const int wm = wave >> 1, wn = wave & 1;
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
-  uint4 ra[CPT], rb[NMAT][CPT];
+  uint4 ra[CPTA], rb[NMAT][CPTB];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
+    for (int j = 0; j < CPTA; ++j) {
       const int c = tid + j * kThreads;
       const int r = c / CPR, col = c % CPR;
       const int kk = k0 + col * EPV;
-      const bool kok = kk < K;
       const int ar = min(r, rows - 1);  // rows past the segment repeat its last row; never stored
-      ra[j] = kok ? *reinterpret_cast<const uint4*>(A + size_t(row0 + ar) * K + kk) : zero;
+      ra[j] = kk < K ? *reinterpret_cast<const uint4*>(A + size_t(row0 + ar) * K + kk) : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < CPTB; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / CPR, col = c % CPR;
+      const int kk = k0 + col * EPV;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const int nr = n0 + r;
-        rb[m][j] = (kok && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
+        rb[m][j] = (kk < K && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
       }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
+    for (int j = 0; j < CPTA; ++j) {
       const int c = tid + j * kThreads;
       const int r = c / CPR, col = c % CPR;
       *reinterpret_cast<uint4*>(&As[buf][r * kLd + col * EPV]) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < CPTB; ++j) {
+      const int c = tid + j * kThreads;
+      const int r = c / CPR, col = c % CPR;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) *reinterpret_cast<uint4*>(&Bs[buf][m][r * kLd + col * EPV]) = rb[m][j];
     }
   };
 
-  f32x16_t acc[NMAT][2][2];
+  f32x16_t acc[NMAT][MI][2];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -155,10 +170,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
     if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
     for (int kc = 0; kc < BK / 16; ++kc) {
-      uint4 af[2][FV], bfr[NMAT][2][FV];
+      uint4 af[MI][FV], bfr[NMAT][2][FV];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4* p = reinterpret_cast<const uint4*>(&As[buf][(wm * 64 + i * 32 + frow) * kLd + kc * 16 + fk]);
+      for (int i = 0; i < MI; ++i) {
+        const uint4* p =
+            reinterpret_cast<const uint4*>(&As[buf][(wm * (BMT / 2) + i * 32 + frow) * kLd + kc * 16 + fk]);
 #pragma unroll
         for (int v = 0; v < FV; ++v) af[i][v] = p[v];
       }
@@ -174,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) G::mma(af[i], bfr[m][j], acc[m][i][j]);
     }
@@ -185,13 +201,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
   // ---- epilogue: 32x32 accumulator layout, lane -> column (lane & 31),
   // register r -> row 8*(r/4) + 4*(lane/32) + r%4 ------------------------------
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rt = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int rt = wm * (BMT / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (rt < rows && col < N) {
           float v;
           if constexpr (NMAT == 2) {
@@ -1032,18 +1048,28 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
 
 }  // namespace skinny
 
-template <typename T>
-moe_status launch_t(const FfnArgs& a) {
+template <typename T, int BMT>
+moe_status launch_bm(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
-  const unsigned mslots = unsigned((a.max_pairs + BM - 1) / BM + L);
-  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0, a.s,
-             static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
+  const unsigned mslots = unsigned((a.max_pairs + BMT - 1) / BMT + L);
+  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2, BMT>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
+             a.s, static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
              static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H);
-  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0, a.s,
+  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1, BMT>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0, a.s,
              static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down), static_cast<const T*>(a.w_down),
              static_cast<T*>(a.y_sorted), L, H, I);
   return MOE_OK;
+}
+
+// 64-row tiles when 128-row tiles would leave fewer than two blocks per CU (the
+// fp32 layer's 8 experts x ~1024 rows x 256 columns: 144 blocks of 128 rows)
+template <typename T>
+moe_status launch_t(const FfnArgs& a) {
+  const moe_layer_desc* d = a.d;
+  const int64_t nb = std::min((d->intermediate + BN - 1) / BN, (d->hidden + BN - 1) / BN);
+  if (((a.max_pairs + BM - 1) / BM + d->local_count) * nb < 512) return launch_bm<T, 64>(a);
+  return launch_bm<T, 128>(a);
 }
 
 // large tiles pay off once segments hold a few hundred rows; decode-sized
