@@ -100,6 +100,8 @@ def decode(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
     dtype "bf16": `a` holds uint16 bfloat16 bit patterns (sign, 8-bit
     exponent, 7-bit mantissa: the top half of an IEEE float32).
     dtype "f32": `a` holds float32 values.
+    dtype "f64": `a` holds float64 values, taken as they are (small exact
+    layers for finite-difference checks of the backward).
     """
     if a is None:
         return None
@@ -108,6 +110,8 @@ def decode(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
         return bits.view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -413,7 +417,9 @@ def layer_forward(inp: dict, *, logits: Optional[np.ndarray] = None,
     dt = s.dtype
     x = decode(inp["x"], dt)
     wr = decode(inp["w_router"], dt)
-    br = None if inp.get("b_router") is None else np.asarray(inp["b_router"], dtype=np.float32).astype(np.float64)
+    br = inp.get("b_router")
+    if br is not None:
+        br = np.asarray(br, dtype=np.float64) if dt == "f64" else np.asarray(br, dtype=np.float32).astype(np.float64)
     r = route(x, wr, br, s.k, logits=None if logits is None else np.asarray(logits, dtype=np.float64))
     if route_opts is not None:
         r = route_with_options(r["logits"], s.k, route_opts.get("selection_bias"), route_opts.get("num_groups", 0),

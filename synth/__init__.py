@@ -167,3 +167,13 @@ def make_layer(s: LayerSpec, with_experts: bool = True) -> dict:
             _normal_into(wd[e], kids[3 * e + 2], 1.0 / math.sqrt(s.I), s.dtype)
         out["w_gate"], out["w_up"], out["w_down"] = wg, wu, wd
     return out
+
+
+def make_upstream_grad(s: LayerSpec) -> np.ndarray:
+    """Seeded upstream gradient dy [T,H] of the layer output, N(0,1), in the layer's storage type.
+
+    Drawn from its own child of the layer seed (spawn key 4), so the other
+    draws of `make_layer` are unchanged.
+    """
+    seq = np.random.SeedSequence(s.seed, spawn_key=(4,))
+    return _normal(seq, (s.T, s.H), 1.0, s.dtype)
