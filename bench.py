@@ -1,10 +1,11 @@
 """Benchmark: one MoE layer forward (route -> dispatch -> grouped SwiGLU FFN ->
 combine) on one MI355X through the libmoe C ABI.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--backward]
 
 A step is one moe_layer_forward over one batch of seeded synthetic input that
-is already resident in HBM.  W untimed steps, then exactly K timed steps
+is already resident in HBM (with --backward: one training step of the layer,
+moe_layer_forward_train then moe_layer_backward on a seeded upstream gradient).  W untimed steps, then exactly K timed steps
 between two device synchronisations.  Every kernel of every timed step is
 also bracketed by HIP events on the launch stream (the library records them),
 which gives each kernel's average duration; the roofline entry uses the
@@ -25,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "routed tokens/s per MoE layer (1 GPU, bf16) + grouped-GEMM % MFMA peak"
+METRIC_TRAIN = "routed tokens/s per MoE layer training step (forward keeping activations + backward; 1 GPU)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
@@ -63,8 +65,10 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int, nblk: int) -> tuple[float, float]:
-    """Algorithmic (bytes, flops) of one launch of a libmoe kernel."""
+def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int, nblk: int,
+                train: bool = False) -> tuple[float, float]:
+    """Algorithmic (bytes, flops) of one launch of a libmoe kernel (train: the
+    training forward, whose gate/up kernel also writes the pre-activations)."""
     dt = 2 if s.dtype == "bf16" else 4
     T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
     cap = s.capacity_factor > 0
@@ -86,11 +90,32 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
         # ranks from the pair ids and chunk bases, both permutation arrays, and the row copy
         return T * k * 4 * 2 + nblk * E * 4 + P * 4 + (touched_tokens + P) * H * dt, 0.0
     if name == "ffn_gate_up":
-        return P * H * dt + 2 * touched_experts * I * H * dt + P * I * dt, 4.0 * P * H * I
+        return P * H * dt + 2 * touched_experts * I * H * dt + (3 if train else 1) * P * I * dt, 4.0 * P * H * I
     if name == "ffn_down":
         return P * I * dt + touched_experts * H * I * dt + P * H * dt, 2.0 * P * H * I
     if name == "combine":
         return P * H * dt + T * k * 8 + T * H * dt, 0.0
+    # backward (training): dy_sorted, dl; dh -> dg, du; dW; dx_sorted; router; dx
+    Ep = (E + 7) // 8 * 8
+    Lc = s.L
+    if name == "combine_bwd":
+        return (T * H + 2 * P * H) * dt + T * k * 12, 0.0
+    if name == "ffn_down_dgrad":
+        return (P * H + touched_experts * H * I + 4 * P * I) * dt, 2.0 * P * H * I
+    if name == "ffn_down_wgrad":
+        return (P * H + P * I + Lc * H * I) * dt, 2.0 * P * H * I
+    if name == "ffn_gate_up_dgrad":
+        return (2 * P * I + 2 * touched_experts * I * H + P * H) * dt, 4.0 * P * H * I
+    if name == "ffn_gate_up_wgrad":
+        return (2 * P * I + P * H + 2 * Lc * I * H) * dt, 4.0 * P * H * I
+    if name == "route_bwd_dlogits":
+        return T * k * 8 + T * Ep * (dt + 4), 0.0
+    if name == "route_bwd_wgrad":
+        return (T * H + T * Ep + E * H) * dt, 2.0 * T * k * H
+    if name == "route_bwd_bias":
+        return T * Ep * 4, 0.0
+    if name == "dispatch_bwd":
+        return (P * H + T * H + E * H) * dt + T * k * 12, 0.0
     return 0.0, 0.0
 
 
@@ -115,22 +140,30 @@ def traffic_for(kernel: str, workload: str):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(inp, tokens: int) -> dict:
-    """The oracle as it stands, on the first `tokens` tokens of the same layer."""
+def cpu_baseline(inp, tokens: int, backward: bool = False) -> dict:
+    """The oracle as it stands, on the first `tokens` tokens of the same layer
+    (with backward: its forward and backward, a training step)."""
     import numpy as np
     import oracle
+    import oracle.moe_backward as ob
+    import synth
     from threadpoolctl import threadpool_info
     s = inp["spec"]
     sub = dict(inp)
     sub["spec"] = s.replace(T=tokens)
     sub["x"] = np.ascontiguousarray(inp["x"][:tokens])
+    dy = oracle.decode(synth.make_upstream_grad(s)[:tokens], s.dtype) if backward else None
     t0 = time.perf_counter()
-    oracle.layer_forward(sub)
+    if backward:
+        ob.layer_backward(sub, dy)
+    else:
+        oracle.layer_forward(sub)
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1), "kind": "oracle",
             "sample": f"first {tokens} of {s.T} tokens of the same layer, all {s.L} experts' weights; "
-                      f"whole oracle path (float64) in {dt:.1f} s; host has {os.cpu_count()} CPUs"}
+                      f"whole oracle {'forward + backward' if backward else 'path'} (float64) in {dt:.1f} s; "
+                      f"host has {os.cpu_count()} CPUs"}
 
 
 def main():
@@ -147,6 +180,9 @@ def main():
     ap.add_argument("--balance-gamma", type=float, default=None, metavar="GAMMA",
                     help="route with a selection bias (zero at the start) and take one balancing step on it "
                          "per layer step, from that step's expert loads")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step of the layer: the forward that keeps its activations, "
+                         "then the backward on a seeded upstream gradient")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES bytes (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -184,17 +220,35 @@ def main():
         G, M = args.route_groups if args.route_groups is not None else (0, 0)
         opts = etd.make_route_opts(sel_bias, G, M)
 
-    fw_names = []
+    # a step is a list of library calls; each call gets its own profiling event array
+    if args.backward:
+        dy = to_device(synth.make_upstream_grad(s), s.dtype)
+        saved = etd.make_saved(layer.saved_buffers(x.dtype))
+        grads = layer.grad_buffers(x.dtype)
 
-    def step(capture_names=False, **kw):
+    def calls(**kw):
         if step_counts is not None and "counts_out" not in kw:
             kw["counts_out"] = step_counts
-        layer.forward(x, y=y, opts=opts, **kw)
-        if capture_names:  # the forward's kernels, before the balancing call
-            fw_names[:] = [etd.moe_profile_kernel_name(i) for i in range(etd.moe_profile_kernel_count())]
-        if sel_bias is not None:
-            etd.moe_profile_events(None)  # the balancing step is a call of its own
-            layer.update_selection_bias(kw["counts_out"], sel_bias, args.balance_gamma)
+        if args.backward:
+            out = [lambda: layer.forward_train(x, opts=opts, saved=saved, y=y, **kw),
+                   lambda: layer.backward(x, saved, dy, grads=grads)]
+        else:
+            out = [lambda: layer.forward(x, y=y, opts=opts, **kw)]
+        if sel_bias is not None:  # the balancing step, never timed on its own
+            out.append(lambda: layer.update_selection_bias(kw["counts_out"], sel_bias, args.balance_gamma))
+        return out
+
+    ncalls = len(calls()) - (1 if sel_bias is not None else 0)  # calls whose kernels are profiled
+    names = []  # names[c]: the kernels of call c, in launch order
+
+    def step(ev=None, capture_names=False, **kw):
+        """ev: per profiled call, a list of hipEvent_t (or None)."""
+        for c, fn in enumerate(calls(**kw)):
+            etd.moe_profile_events(ev[c] if ev is not None and c < ncalls else None)
+            fn()
+            if capture_names and c < ncalls:
+                names.append([etd.moe_profile_kernel_name(i) for i in range(etd.moe_profile_kernel_count())])
+        etd.moe_profile_events(None)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration
@@ -207,10 +261,14 @@ def main():
         log(f"[bench] calibration copy of {n} bytes done")
 
     # one run to learn the routing (pairs kept, experts touched) for the work model
-    step(capture_names=True, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
-    torch.cuda.synchronize()
-    names = list(fw_names)
-    ids_h = ids.cpu().numpy()
+    if args.backward:
+        step(capture_names=True, counts_out=counts, num_dropped_out=dropped)
+        torch.cuda.synchronize()
+        ids_h = saved._tensors["topk_ids"].cpu().numpy()
+    else:
+        step(capture_names=True, topk_ids_out=ids, counts_out=counts, num_dropped_out=dropped)
+        torch.cuda.synchronize()
+        ids_h = ids.cpu().numpy()
     cnt_h = counts.cpu().numpy()
     C = etd.moe_capacity(desc)
     local = cnt_h[s.local_begin:s.local_begin + s.L]
@@ -227,10 +285,9 @@ def main():
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    nk = len(names)
 
     def kernel_entry(n, us, count):
-        b, f = kernel_work(n, s, P, touched_tokens, touched_experts, nblk)
+        b, f = kernel_work(n, s, P, touched_tokens, touched_experts, nblk, args.backward)
         b, f = b * count, f * count
         gbs = b / (us * 1e-6) / 1e9 if us > 0 else 0.0
         tfl = f / (us * 1e-6) / 1e12 if us > 0 else 0.0
@@ -241,46 +298,45 @@ def main():
     # breakdown: a few more steps with every kernel between HIP events (each event pair
     # costs the stream a little time, so the timed steps below carry only one kernel's)
     nbd = max(3, min(args.steps, 10))
-    evs = [hip.create(2 * nk) for _ in range(nbd)]
+    evs = [[hip.create(2 * len(nc)) for nc in names] for _ in range(nbd)]
     for i in range(nbd):
-        etd.moe_profile_events(evs[i])
-        step()
+        step(evs[i])
     torch.cuda.synchronize()
-    etd.moe_profile_events(None)
     per_kernel = {}
-    for j, n in enumerate(names):
-        ts = [hip.elapsed_ms(evs[i][2 * j], evs[i][2 * j + 1]) for i in range(nbd)]
-        per_kernel.setdefault(n, []).append(sum(ts) / len(ts))
+    for c, nc in enumerate(names):
+        for j, n in enumerate(nc):
+            ts = [hip.elapsed_ms(evs[i][c][2 * j], evs[i][c][2 * j + 1]) for i in range(nbd)]
+            per_kernel.setdefault(n, []).append(sum(ts) / len(ts))
     for e in evs:
-        hip.destroy(e)
+        for ec in e:
+            hip.destroy(ec)
     # a name launched twice in a step adds up
     kern = {n: kernel_entry(n, sum(ts) * 1e3, len(ts)) for n, ts in per_kernel.items()}
     dom = max(kern, key=lambda n: kern[n]["us"])
 
     # timed steps: HIP events around the dominant kernel's launches only
-    dj = [j for j, n in enumerate(names) if n == dom]
+    where = [(c, j) for c, nc in enumerate(names) for j, n in enumerate(nc) if n == dom]
     tev = []
     for _ in range(args.steps):
-        h = [None] * (2 * (max(dj) + 1))
-        for j in dj:
-            h[2 * j], h[2 * j + 1] = hip.create(2)
+        h = [[None] * (2 * len(nc)) for nc in names]
+        for c, j in where:
+            h[c][2 * j], h[c][2 * j + 1] = hip.create(2)
         tev.append(h)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        etd.moe_profile_events(tev[i])
-        step()
+        step(tev[i])
     stop.record()
     torch.cuda.synchronize()
-    etd.moe_profile_events(None)
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    dom_ms = sum(hip.elapsed_ms(h[2 * j], h[2 * j + 1]) for h in tev for j in dj) / args.steps
+    dom_ms = sum(hip.elapsed_ms(h[c][2 * j], h[c][2 * j + 1]) for h in tev for c, j in where) / args.steps
     for h in tev:
-        hip.destroy([e for e in h if e is not None])
-    kern[dom] = kernel_entry(dom, dom_ms * 1e3, len(dj))
-    b, f = kernel_work(dom, s, P, touched_tokens, touched_experts, nblk)
+        for hc in h:
+            hip.destroy([e for e in hc if e is not None])
+    kern[dom] = kernel_entry(dom, dom_ms * 1e3, len(where))
+    b, f = kernel_work(dom, s, P, touched_tokens, touched_experts, nblk, args.backward)
     us = kern[dom]["us"]
     gemm_bound_hbm = dom.startswith("ffn") and (f / (MFMA_PEAK_TFLOPS[s.dtype] * 1e12) < b / (HBM_PEAK_GBS * 1e9))
     if f > 0 and not gemm_bound_hbm:
@@ -296,12 +352,15 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = f if roof["bound"] == "mfma" else b
 
+    # grouped GEMM: all ffn kernels (plan and fixups included) against their flops
     gemm_us = sum(kern[n]["us"] for n in kern if n.startswith("ffn"))
-    gemm_frac = 6.0 * P * s.H * s.I / (gemm_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[s.dtype] if gemm_us else None
+    gemm_fl = sum(kernel_work(n, s, P, touched_tokens, touched_experts, nblk, args.backward)[1] * len(per_kernel[n])
+                  for n in kern if n.startswith("ffn"))
+    gemm_frac = gemm_fl / (gemm_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[s.dtype] if gemm_us else None
     stage = lambda pre: round(sum(kern[n]["us"] for n in kern if n.startswith(pre)), 2)  # noqa: E731
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_TRAIN if args.backward else METRIC,
         "value": round(s.T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -321,12 +380,13 @@ def main():
         "grouped_gemm_mfma_frac": round(gemm_frac, 4) if gemm_frac else None,
         "stages_us": {"route": stage("route"), "dispatch": stage("dispatch"), "grouped_ffn": stage("ffn"),
                       "combine": stage("combine")},
+        **({"mode": "training step (forward keeping activations + backward)"} if args.backward else {}),
         "kernels": kern,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, s.T))
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, s.T), backward=args.backward)
     print(json.dumps(out), flush=True)
 
 

@@ -1,4 +1,4 @@
-"""MI355X-native forward pass of one MoE layer on one GPU's share of experts.
+"""MI355X-native forward and backward passes of one MoE layer on one GPU's share of experts.
 
 The computation lives in libmoe.so (hand-written HIP kernels for gfx950 behind
 the C ABI in include/moe.h).  This package is a thin ctypes binding with the
@@ -15,7 +15,12 @@ from ._lib import (  # noqa: F401
     MOE_STAGE_FFN,
     MOE_STAGE_LAYER,
     MOE_STAGE_ROUTE,
+    MOE_STAGE_FFN_BACKWARD,
+    MOE_STAGE_ROUTE_BACKWARD,
+    MOE_STAGE_LAYER_BACKWARD,
     LayerDesc,
+    Saved,
+    make_saved,
     RouteOpts,
     MoeError,
     lib,
@@ -38,6 +43,13 @@ from ._lib import (  # noqa: F401
     moe_route_ex,
     moe_selection_bias_update,
     moe_version,
+    moe_grouped_ffn_train,
+    moe_layer_forward_train,
+    moe_combine_backward,
+    moe_grouped_ffn_backward,
+    moe_route_backward,
+    moe_dispatch_backward,
+    moe_layer_backward,
     moe_workspace_size,
 )
 from .layer import MoELayer  # noqa: F401

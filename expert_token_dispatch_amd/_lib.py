@@ -12,6 +12,7 @@ lib_path = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_FFN, MOE_STAGE_COMBINE, MOE_STAGE_LAYER = 0, 1, 2, 3, 4
+MOE_STAGE_FFN_BACKWARD, MOE_STAGE_ROUTE_BACKWARD, MOE_STAGE_LAYER_BACKWARD = 5, 6, 7
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
            -4: "MOE_ERR_HIP"}
@@ -44,6 +45,20 @@ class RouteOpts(ctypes.Structure):
         ("num_groups", ctypes.c_int32),
         ("max_groups", ctypes.c_int32),
     ]
+
+
+class Saved(ctypes.Structure):
+    """moe_saved: what the training forward keeps for the backward (include/moe.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_ids", "topk_w", "offsets", "pair_row", "x_sorted", "gate", "up", "h", "y_sorted")]
+
+
+def make_saved(t: dict) -> Saved:
+    """t: a dict of device tensors under the moe_saved field names.  The struct
+    keeps a reference to the dict, so the pointers stay valid while it lives."""
+    v = Saved(*[_p(t[n]) for n, _ in Saved._fields_])
+    v._tensors = t
+    return v
 
 
 def make_route_opts(selection_bias=None, num_groups: int = 0, max_groups: int = 0) -> RouteOpts:
@@ -100,6 +115,17 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward_ex": (st, [_DP, _OP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           ctypes.c_size_t, _VP]),
             "moe_selection_bias_update": (st, [_DP, _VP, _VP, ctypes.c_float, _VP]),
+            "moe_grouped_ffn_train": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                           _VP]),
+            "moe_layer_forward_train": (st, [_DP, _OP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                             ctypes.c_size_t, _VP]),
+            "moe_combine_backward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+            "moe_grouped_ffn_backward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                              _VP, ctypes.c_size_t, _VP]),
+            "moe_route_backward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+            "moe_dispatch_backward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+            "moe_layer_backward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        ctypes.c_size_t, _VP]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -240,3 +266,55 @@ def moe_layer_forward_ex(d, opts, x, w_router, b_router, w_gate, w_up, w_down, y
 
 def moe_selection_bias_update(d, counts, bias, gamma: float, stream=None) -> None:
     _check(lib().moe_selection_bias_update(ctypes.byref(d), _p(counts), _p(bias), float(gamma), _s(stream)))
+
+
+# ---- training: the backward pass (Transformers "Expert parallelism", "Token dispatch") ----
+def _saved(v) -> Optional[int]:
+    return None if v is None else ctypes.addressof(v)
+
+
+def moe_grouped_ffn_train(d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, h, gate, up, ws=None,
+                          stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_grouped_ffn_train(ctypes.byref(d), _p(x_sorted), _p(offsets), _p(w_gate), _p(w_up), _p(w_down),
+                                       _p(y_sorted), _p(h), _p(gate), _p(up), wp, wn, _s(stream)))
+
+
+def moe_layer_forward_train(d, opts, x, w_router, b_router, w_gate, w_up, w_down, y, saved, ws, counts_out=None,
+                            num_dropped_out=None, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_forward_train(ctypes.byref(d), _opts(opts), _p(x), _p(w_router), _p(b_router), _p(w_gate),
+                                         _p(w_up), _p(w_down), _p(y), _saved(saved), _p(counts_out),
+                                         _p(num_dropped_out), wp, wn, _s(stream)))
+
+
+def moe_combine_backward(d, dy, y_sorted, pair_row, topk_w, dy_sorted, dl, stream=None) -> None:
+    _check(lib().moe_combine_backward(ctypes.byref(d), _p(dy), _p(y_sorted), _p(pair_row), _p(topk_w),
+                                      _p(dy_sorted), _p(dl), _s(stream)))
+
+
+def moe_grouped_ffn_backward(d, x_sorted, offsets, w_gate, w_up, w_down, gate, up, h, dy_sorted, dx_sorted, dw_gate,
+                             dw_up, dw_down, ws=None, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_grouped_ffn_backward(ctypes.byref(d), _p(x_sorted), _p(offsets), _p(w_gate), _p(w_up),
+                                          _p(w_down), _p(gate), _p(up), _p(h), _p(dy_sorted), _p(dx_sorted),
+                                          _p(dw_gate), _p(dw_up), _p(dw_down), wp, wn, _s(stream)))
+
+
+def moe_route_backward(d, x, topk_ids, dl, dw_router, db_router=None, ws=None, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_route_backward(ctypes.byref(d), _p(x), _p(topk_ids), _p(dl), _p(dw_router), _p(db_router),
+                                    wp, wn, _s(stream)))
+
+
+def moe_dispatch_backward(d, dx_sorted, pair_row, topk_ids, dl, w_router, dx, stream=None) -> None:
+    _check(lib().moe_dispatch_backward(ctypes.byref(d), _p(dx_sorted), _p(pair_row), _p(topk_ids), _p(dl),
+                                       _p(w_router), _p(dx), _s(stream)))
+
+
+def moe_layer_backward(d, x, w_router, w_gate, w_up, w_down, saved, dy, dx, dw_router, db_router, dw_gate, dw_up,
+                       dw_down, ws, stream=None) -> None:
+    wp, wn = _ws(ws)
+    _check(lib().moe_layer_backward(ctypes.byref(d), _p(x), _p(w_router), _p(w_gate), _p(w_up), _p(w_down),
+                                    _saved(saved), _p(dy), _p(dx), _p(dw_router), _p(db_router), _p(dw_gate),
+                                    _p(dw_up), _p(dw_down), wp, wn, _s(stream)))

@@ -146,6 +146,39 @@ LayerWs layer_layout(const moe_layer_desc* d, void* base) {
   return w;
 }
 
+// moe_grouped_ffn_backward's workspace: dg and du [P_max, I]
+size_t ffn_bwd_bytes(const moe_layer_desc* d) { return 2 * ffn_h_bytes(d); }
+
+// Layout of the moe_layer_backward workspace.
+struct LayerBwdWs {
+  void* dy_sorted;
+  float* dl;
+  void* dx_sorted;
+  void* ffn;    // dg, du
+  void* route;  // logit gradients
+  size_t bytes;
+};
+
+LayerBwdWs layer_bwd_layout(const moe_layer_desc* d, void* base) {
+  const int64_t pm = max_pairs_of(d);
+  const size_t dt = dtype_bytes(d->dtype);
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  LayerBwdWs w{};
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + o : nullptr;
+    o += align_up(bytes, 256);
+    return r;
+  };
+  w.dy_sorted = take(size_t(pm) * d->hidden * dt);
+  w.dl = static_cast<float*>(take(size_t(d->num_tokens) * d->top_k * 4));
+  w.dx_sorted = take(size_t(pm) * d->hidden * dt);
+  w.ffn = take(ffn_bwd_bytes(d));
+  w.route = take(route_bwd_scratch_bytes(d));
+  w.bytes = o;
+  return w;
+}
+
 size_t stage_bytes(const moe_layer_desc* d, int32_t stage) {
   switch (stage) {
     case MOE_STAGE_ROUTE:
@@ -158,10 +191,22 @@ size_t stage_bytes(const moe_layer_desc* d, int32_t stage) {
       return ffn_h_bytes(d) + align_up(ffn_scratch_bytes(d, max_pairs_of(d)), 256);
     case MOE_STAGE_LAYER:
       return layer_layout(d, nullptr).bytes;
+    case MOE_STAGE_FFN_BACKWARD:
+      return ffn_bwd_bytes(d);
+    case MOE_STAGE_ROUTE_BACKWARD:
+      return route_bwd_scratch_bytes(d);
+    case MOE_STAGE_LAYER_BACKWARD:
+      return layer_bwd_layout(d, nullptr).bytes;
     default:
       return 0;
   }
 }
+
+#define TRY_ZERO(expr)                 \
+  do {                                 \
+    const moe_status _z = (expr);      \
+    if (_z != MOE_OK) return _z;       \
+  } while (0)
 
 #define REQUIRE_PTR(p, a)                                                                                  \
   do {                                                                                                     \
@@ -242,6 +287,84 @@ moe_status combine_checks(const void* y_sorted, const int32_t* pair_row, const f
   return MOE_OK;
 }
 
+moe_status saved_checks(const moe_saved* v) {
+  if (v == nullptr) return set_error(MOE_ERR_INVALID_ARG, "saved is NULL");
+  REQUIRE_PTR(v->topk_ids, 4);
+  REQUIRE_PTR(v->topk_w, 4);
+  REQUIRE_PTR(v->offsets, 4);
+  REQUIRE_PTR(v->pair_row, 4);
+  REQUIRE_PTR(v->x_sorted, 16);
+  REQUIRE_PTR(v->gate, 16);
+  REQUIRE_PTR(v->up, 16);
+  REQUIRE_PTR(v->h, 16);
+  REQUIRE_PTR(v->y_sorted, 16);
+  return MOE_OK;
+}
+
+moe_status combine_bwd_checks(const void* dy, const void* y_sorted, const int32_t* pair_row, const float* topk_w,
+                              const void* dy_sorted, const float* dl) {
+  REQUIRE_PTR(dy, 16);
+  REQUIRE_PTR(y_sorted, 16);
+  REQUIRE_PTR(pair_row, 4);
+  REQUIRE_PTR(topk_w, 4);
+  REQUIRE_PTR(dy_sorted, 16);
+  REQUIRE_PTR(dl, 4);
+  return MOE_OK;
+}
+
+moe_status ffn_bwd_checks(const void* x_sorted, const int32_t* offsets, const void* w_gate, const void* w_up,
+                          const void* w_down, const void* gate, const void* up, const void* h, const void* dy_sorted,
+                          const void* dx_sorted, const void* dw_gate, const void* dw_up, const void* dw_down) {
+  REQUIRE_PTR(x_sorted, 16);
+  REQUIRE_PTR(offsets, 4);
+  REQUIRE_PTR(w_gate, 16);
+  REQUIRE_PTR(w_up, 16);
+  REQUIRE_PTR(w_down, 16);
+  REQUIRE_PTR(gate, 16);
+  REQUIRE_PTR(up, 16);
+  REQUIRE_PTR(h, 16);
+  REQUIRE_PTR(dy_sorted, 16);
+  REQUIRE_PTR(dx_sorted, 16);
+  REQUIRE_PTR(dw_gate, 16);
+  REQUIRE_PTR(dw_up, 16);
+  REQUIRE_PTR(dw_down, 16);
+  return MOE_OK;
+}
+
+moe_status route_bwd_checks(const void* x, const int32_t* topk_ids, const float* dl, const void* dw_router,
+                            const float* db_router) {
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(topk_ids, 4);
+  REQUIRE_PTR(dl, 4);
+  REQUIRE_PTR(dw_router, 16);
+  OPTIONAL_PTR(db_router, 16);
+  return MOE_OK;
+}
+
+moe_status dispatch_bwd_checks(const void* dx_sorted, const int32_t* pair_row, const int32_t* topk_ids,
+                               const float* dl, const void* w_router, const void* dx) {
+  REQUIRE_PTR(dx_sorted, 16);
+  REQUIRE_PTR(pair_row, 4);
+  REQUIRE_PTR(topk_ids, 4);
+  REQUIRE_PTR(dl, 4);
+  REQUIRE_PTR(w_router, 16);
+  REQUIRE_PTR(dx, 16);
+  return MOE_OK;
+}
+
+// Zero weight gradients of a layer that saw no tokens (no expert received any).
+moe_status zero_ffn_grads(const moe_layer_desc* d, void* dw_gate, void* dw_up, void* dw_down, hipStream_t s) {
+  const size_t n = size_t(d->local_count) * d->intermediate * d->hidden * dtype_bytes(d->dtype);
+  TRY_ZERO(launch_zero("ffn_bwd_zero", dw_gate, n, s));
+  TRY_ZERO(launch_zero("ffn_bwd_zero", dw_up, n, s));
+  return launch_zero("ffn_bwd_zero", dw_down, n, s);
+}
+
+moe_status zero_route_grads(const moe_layer_desc* d, void* dw_router, float* db_router, hipStream_t s) {
+  TRY_ZERO(launch_zero("route_bwd_zero", dw_router, size_t(d->num_experts) * d->hidden * dtype_bytes(d->dtype), s));
+  return launch_zero("route_bwd_zero", db_router, size_t(d->num_experts) * 4, s);
+}
+
 #define TRY(expr)                          \
   do {                                     \
     const moe_status _s = (expr);          \
@@ -312,7 +435,8 @@ int64_t moe_max_pairs(const moe_layer_desc* d) {
 moe_status moe_workspace_size(const moe_layer_desc* d, int32_t stage, size_t* bytes) {
   TRY(check_desc(d));
   if (bytes == nullptr) return set_error(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_LAYER) return set_error(MOE_ERR_INVALID_ARG, "unknown stage %d", stage);
+  if (stage < MOE_STAGE_ROUTE || stage > MOE_STAGE_LAYER_BACKWARD)
+    return set_error(MOE_ERR_INVALID_ARG, "unknown stage %d", stage);
   *bytes = stage_bytes(d, stage);
   return MOE_OK;
 }
@@ -452,6 +576,156 @@ moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_route_opts* o
   TRY(launch_grouped_ffn(fa));
   CombineArgs ca{d, w.y_sorted, w.pair_row, tw, y, s};
   return launch_combine(ca);
+}
+
+moe_status moe_grouped_ffn_train(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
+                                 const void* w_gate, const void* w_up, const void* w_down, void* y_sorted, void* h,
+                                 void* gate, void* up, void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(ffn_checks(x_sorted, offsets, w_gate, w_up, w_down, y_sorted));
+  REQUIRE_PTR(h, 16);
+  REQUIRE_PTR(gate, 16);
+  REQUIRE_PTR(up, 16);
+  TRY(check_ws(d, MOE_STAGE_FFN, ws, ws_bytes));
+  void* scratch = ffn_scratch_bytes(d, max_pairs_of(d)) ? static_cast<char*>(ws) + ffn_h_bytes(d) : nullptr;
+  FfnArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, h, scratch, max_pairs_of(d),
+            static_cast<hipStream_t>(stream), gate, up};
+  return launch_grouped_ffn(a);
+}
+
+moe_status moe_layer_forward_train(const moe_layer_desc* d, const moe_route_opts* opts, const void* x,
+                                   const void* w_router, const float* b_router, const void* w_gate, const void* w_up,
+                                   const void* w_down, void* y, const moe_saved* saved, int32_t* counts_out,
+                                   int64_t* num_dropped_out, void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(saved_checks(saved));
+  TRY(check_ws(d, MOE_STAGE_LAYER, ws, ws_bytes));
+  LayerWs w = layer_layout(d, ws);
+  const moe_saved& v = *saved;
+  int32_t* counts = counts_out ? counts_out : w.counts;
+  int64_t* dropped = num_dropped_out ? num_dropped_out : w.num_dropped;
+  const bool cap = capacity_of(d) >= 0;
+  TRY(route_checks(d, x, w_router, b_router, nullptr, nullptr, v.topk_ids, v.topk_w, w.topk_logit));
+  TRY(dispatch_checks(d, x, v.topk_ids, w.topk_logit, counts, v.offsets, w.sorted_pairs, v.pair_row, v.x_sorted,
+                      dropped));
+  TRY(ffn_checks(v.x_sorted, v.offsets, w_gate, w_up, w_down, v.y_sorted));
+  TRY(combine_checks(v.y_sorted, v.pair_row, v.topk_w, y));
+  TRY(opts_checks(d, opts));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const DispatchScratch scr = carve_dispatch_scratch(d, w.dispatch);
+  RouteArgs ra{d, x, w_router, b_router, nullptr, nullptr, v.topk_ids, v.topk_w, cap ? w.topk_logit : nullptr,
+               static_cast<float*>(w.route), scr.blk_all, s};
+  apply_opts(ra, d, opts);
+  TRY(launch_route(ra));
+  DispatchArgs da{d, x, v.topk_ids, w.topk_logit, counts, v.offsets, w.sorted_pairs, v.pair_row, v.x_sorted,
+                  dropped, scr, capacity_of(d), true, s};
+  TRY(launch_dispatch(da));
+  FfnArgs fa{d, v.x_sorted, v.offsets, w_gate, w_up, w_down, v.y_sorted, v.h, w.ffn_scratch, max_pairs_of(d), s,
+             v.gate, v.up};
+  TRY(launch_grouped_ffn(fa));
+  CombineArgs ca{d, v.y_sorted, v.pair_row, v.topk_w, y, s};
+  return launch_combine(ca);
+}
+
+moe_status moe_combine_backward(const moe_layer_desc* d, const void* dy, const void* y_sorted,
+                                const int32_t* pair_row, const float* topk_w, void* dy_sorted, float* dl,
+                                void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(combine_bwd_checks(dy, y_sorted, pair_row, topk_w, dy_sorted, dl));
+  CombineBwdArgs a{d, dy, y_sorted, pair_row, topk_w, dy_sorted, dl, static_cast<hipStream_t>(stream)};
+  return launch_combine_backward(a);
+}
+
+moe_status moe_grouped_ffn_backward(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
+                                    const void* w_gate, const void* w_up, const void* w_down, const void* gate,
+                                    const void* up, const void* h, const void* dy_sorted, void* dx_sorted,
+                                    void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->num_tokens == 0) {
+    REQUIRE_PTR(dw_gate, 16);
+    REQUIRE_PTR(dw_up, 16);
+    REQUIRE_PTR(dw_down, 16);
+    return zero_ffn_grads(d, dw_gate, dw_up, dw_down, s);
+  }
+  TRY(ffn_bwd_checks(x_sorted, offsets, w_gate, w_up, w_down, gate, up, h, dy_sorted, dx_sorted, dw_gate, dw_up,
+                     dw_down));
+  TRY(check_ws(d, MOE_STAGE_FFN_BACKWARD, ws, ws_bytes));
+  FfnBwdArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, gate, up, h, dy_sorted, dx_sorted, dw_gate, dw_up,
+               dw_down, ws, static_cast<char*>(ws) + ffn_h_bytes(d), max_pairs_of(d), s};
+  return launch_grouped_ffn_backward(a);
+}
+
+moe_status moe_route_backward(const moe_layer_desc* d, const void* x, const int32_t* topk_ids, const float* dl,
+                              void* dw_router, float* db_router, void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->num_tokens == 0) {
+    REQUIRE_PTR(dw_router, 16);
+    OPTIONAL_PTR(db_router, 16);
+    return zero_route_grads(d, dw_router, db_router, s);
+  }
+  TRY(route_bwd_checks(x, topk_ids, dl, dw_router, db_router));
+  TRY(check_ws(d, MOE_STAGE_ROUTE_BACKWARD, ws, ws_bytes));
+  RouteBwdArgs a{d, x, topk_ids, dl, dw_router, db_router, ws, s};
+  return launch_route_backward(a);
+}
+
+moe_status moe_dispatch_backward(const moe_layer_desc* d, const void* dx_sorted, const int32_t* pair_row,
+                                 const int32_t* topk_ids, const float* dl, const void* w_router, void* dx,
+                                 void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(dispatch_bwd_checks(dx_sorted, pair_row, topk_ids, dl, w_router, dx));
+  DispatchBwdArgs a{d, dx_sorted, pair_row, topk_ids, dl, w_router, dx, static_cast<hipStream_t>(stream)};
+  return launch_dispatch_backward(a);
+}
+
+moe_status moe_layer_backward(const moe_layer_desc* d, const void* x, const void* w_router, const void* w_gate,
+                              const void* w_up, const void* w_down, const moe_saved* saved, const void* dy,
+                              void* dx, void* dw_router, float* db_router, void* dw_gate, void* dw_up,
+                              void* dw_down, void* ws, size_t ws_bytes, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->num_tokens == 0) {
+    REQUIRE_PTR(dw_router, 16);
+    OPTIONAL_PTR(db_router, 16);
+    REQUIRE_PTR(dw_gate, 16);
+    REQUIRE_PTR(dw_up, 16);
+    REQUIRE_PTR(dw_down, 16);
+    TRY(zero_route_grads(d, dw_router, db_router, s));
+    return zero_ffn_grads(d, dw_gate, dw_up, dw_down, s);
+  }
+  TRY(saved_checks(saved));
+  TRY(check_ws(d, MOE_STAGE_LAYER_BACKWARD, ws, ws_bytes));
+  const moe_saved& v = *saved;
+  LayerBwdWs w = layer_bwd_layout(d, ws);
+  TRY(combine_bwd_checks(dy, v.y_sorted, v.pair_row, v.topk_w, w.dy_sorted, w.dl));
+  TRY(ffn_bwd_checks(v.x_sorted, v.offsets, w_gate, w_up, w_down, v.gate, v.up, v.h, w.dy_sorted, w.dx_sorted,
+                     dw_gate, dw_up, dw_down));
+  TRY(route_bwd_checks(x, v.topk_ids, w.dl, dw_router, db_router));
+  TRY(dispatch_bwd_checks(w.dx_sorted, v.pair_row, v.topk_ids, w.dl, w_router, dx));
+  CombineBwdArgs ca{d, dy, v.y_sorted, v.pair_row, v.topk_w, w.dy_sorted, w.dl, s};
+  TRY(launch_combine_backward(ca));
+  char* ffn = static_cast<char*>(w.ffn);
+  FfnBwdArgs fa{d, v.x_sorted, v.offsets, w_gate, w_up, w_down, v.gate, v.up, v.h, w.dy_sorted, w.dx_sorted,
+                dw_gate, dw_up, dw_down, ffn, ffn + ffn_h_bytes(d), max_pairs_of(d), s};
+  TRY(launch_grouped_ffn_backward(fa));
+  RouteBwdArgs ra{d, x, v.topk_ids, w.dl, dw_router, db_router, w.route, s};
+  TRY(launch_route_backward(ra));
+  DispatchBwdArgs da{d, w.dx_sorted, v.pair_row, v.topk_ids, w.dl, w_router, dx, s};
+  return launch_dispatch_backward(da);
 }
 
 }  // extern "C"

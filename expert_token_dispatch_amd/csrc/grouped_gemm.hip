@@ -71,7 +71,8 @@ template <typename T, int NMAT, int BMT>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restrict__ A,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const T* __restrict__ B0, const T* __restrict__ B1,
-                                                                T* __restrict__ C, int L, int N, int K) {
+                                                                T* __restrict__ C, int L, int N, int K,
+                                                                T* __restrict__ Gs, T* __restrict__ Us) {
   using G = Gemm<T>;
   constexpr int BK = G::BK, kLd = G::kLd, FV = G::kFragVec;
   constexpr int EPV = 16 / int(sizeof(T));     // elements per 16-byte vector
@@ -212,6 +213,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
           float v;
           if constexpr (NMAT == 2) {
             v = silu(acc[0][i][j][r]) * acc[1][i][j][r];
+            if (Gs != nullptr) {  // training: keep the pre-activations for the backward
+              Gs[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(acc[0][i][j][r]);
+              Us[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(acc[1][i][j][r]);
+            }
           } else {
             v = acc[0][i][j][r];
           }
@@ -481,9 +486,10 @@ constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true, 4>::kStage;  // 160
 // and parks it in LDS, rows padded by 16 bytes; then every thread copies
 // 16-byte row chunks out, so each store instruction writes whole row pieces.
 // The caller has made sure no wave still reads the loop's LDS stages.
-template <int NMAT, bool WIDE, int NW>
+template <int NMAT, bool WIDE, int NW, bool SAVE>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds, bf16_t* __restrict__ C, int row0,
-                                         int rows, int n0, int N) {
+                                         int rows, int n0, int N, bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
+  if constexpr (!SAVE) {
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
@@ -521,6 +527,69 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds,
     // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
     if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(C + size_t(row0 + r) * N + n0 + c * 8) = val;
   }
+  } else {
+  using S = Shape<WIDE, NW>;
+  constexpr int NB = S::NB, kThreads = S::kThreads;
+  constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
+  constexpr int RS = TC * 2 + 16;
+  constexpr int NJ = NMAT == 2 ? NB / 2 : NB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = S::wm(wave), wn = S::wn(wave), fr = lane & 31, g = lane >> 5;
+  // sel 0: the output (SwiGLU for gate/up); sel 1, 2: the gate, up pre-activations
+  auto park = [&](int sel) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rt = wm * 128 + i * 32 + fr;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (NMAT == 1) {
+              v[u] = acc[i][j][4 * q + u];
+            } else {
+              const float gv = acc[i][j][4 * q + u], uv = acc[i][j + NB / 2][4 * q + u];
+              v[u] = sel == 0 ? silu(gv) * uv : (sel == 1 ? gv : uv);
+            }
+          }
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          const int cl = (NMAT == 2 ? wn * NB * 16 : wn * NB * 32) + j * 32 + 8 * q + 4 * g;
+          *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    block_barrier();
+  };
+  constexpr int CPR = TC / 8;  // 16-byte chunks per row
+  auto copy_out = [&](bf16_t* __restrict__ dst) {
+#pragma unroll
+    for (int u = 0; u < S::kA * CPR / kThreads; ++u) {
+      const int id = tid + kThreads * u;
+      const int r = id / CPR, c = id % CPR;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
+      // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
+      if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(dst + size_t(row0 + r) * N + n0 + c * 8) = val;
+    }
+  };
+  park(0);
+  copy_out(C);
+  if (NMAT == 2) {
+    // training: the pre-activations too, through the same LDS tile once every
+    // wave has read the previous one out
+#pragma unroll 1
+    for (int sel = 1; sel <= 2; ++sel) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      block_barrier();
+      park(sel);
+      copy_out(sel == 1 ? Gs : Us);
+    }
+  }
+  }
 }
 
 template <int NMAT>
@@ -537,10 +606,11 @@ __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslo
 }
 
 // One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
-template <int NMAT, bool WIDE, int NW>
+template <int NMAT, bool WIDE, int NW, bool SAVE>
 __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
                                           const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
-                                          const Job& jb, float* __restrict__ parts, char* lds) {
+                                          const Job& jb, float* __restrict__ parts, char* lds,
+                                          bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
@@ -752,15 +822,16 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   }
   MOE_LGKMCNT0();
   block_barrier();  // every wave is done reading the last stage
-  epilogue<NMAT, WIDE, NW>(acc, lds, C, row0, rows, n0, N);
+  epilogue<NMAT, WIDE, NW, SAVE>(acc, lds, C, row0, rows, n0, N, Gs, Us);
 }
 
-template <int NMAT, int NW>
+template <int NMAT, int NW, bool SAVE>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                        bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
                                                         const int32_t* __restrict__ tpre, int cpx, int smax,
-                                                        float* __restrict__ parts) {
+                                                        float* __restrict__ parts, bf16_t* __restrict__ Gs,
+                                                        bf16_t* __restrict__ Us) {
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
   const int NT = (N + ON - 1) / ON;
   const int nk = K / BK;
@@ -780,9 +851,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
   const bf16_t* Bg = B0 + boff;
   const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
   if (jb.wide)
-    tile_body<NMAT, true, NW>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
+    tile_body<NMAT, true, NW, SAVE>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
   else
-    tile_body<NMAT, false, NW>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds);
+    tile_body<NMAT, false, NW, SAVE>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
 }
 
 // Adds the pieces of each split tile in piece order and writes the tile.
@@ -792,10 +863,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
 // gate/up: the gate float4 and its up partner j + NB/2).
 constexpr int kFixSub = 8;
 
-template <int NMAT, int NW>
+template <int NMAT, int NW, bool SAVE>
 __global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
                                                          int L, int N, int K, const int32_t* __restrict__ tpre, int cpx,
-                                                         int smax, const float* __restrict__ parts) {
+                                                         int smax, const float* __restrict__ parts,
+                                                         bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
   constexpr int kThreads = NW * 64, NB = 16 / NW;
   constexpr int NJ = NMAT == 2 ? NB / 2 : NB;   // output column blocks per wave
@@ -842,6 +914,11 @@ __global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restric
       pk.x = pack_bf16x2(o[0], o[1]);
       pk.y = pack_bf16x2(o[2], o[3]);
       *reinterpret_cast<uint2*>(C + size_t(jb.row0 + rt) * N + n0 + cl) = pk;
+      if constexpr (NMAT == 2 && SAVE) {  // training: the pre-activations too
+        const size_t at = size_t(jb.row0 + rt) * N + n0 + cl;
+        *reinterpret_cast<uint2*>(Gs + at) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+        *reinterpret_cast<uint2*>(Us + at) = make_uint2(pack_bf16x2(su[0], su[1]), pack_bf16x2(su[2], su[3]));
+      }
     }
   }
 }
@@ -868,12 +945,26 @@ bool splits(int K) { return K / BK >= kSplitMinSteps; }
 // skewed layer -1.5%); four for longer ones (mixtral-like layer: eight are 1% slower).
 constexpr int kEightWaveSteps = 64;
 
+template <int NMAT, int NW, bool SAVE>
+moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
+                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                      hipStream_t s, bf16_t* Gs, bf16_t* Us);
+
 template <int NMAT, int NW>
 moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                     hipStream_t s) {
+                     hipStream_t s, bf16_t* Gs, bf16_t* Us) {
+  if (NMAT == 2 && Gs != nullptr) return launch_nws<NMAT, NW, true>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+  return launch_nws<NMAT, NW, false>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+}
+
+// SAVE: the training forward's variant, which also writes the gate and up pre-activations
+template <int NMAT, int NW, bool SAVE>
+moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
+                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                      hipStream_t s, bf16_t* Gs, bf16_t* Us) {
   constexpr int kThreads = NW * 64;
-  auto kern = gemm_kernel<NMAT, NW>;
+  auto kern = gemm_kernel<NMAT, NW, SAVE>;
   constexpr size_t lds = lds_bytes<NMAT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
@@ -887,11 +978,11 @@ moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, 
   const int64_t per_xcd = (tiles + kXcds - 1) / kXcds + (smax > 1 ? kMaxParts - kMaxTail : 0);
   // A holds max_pairs rows (the caller's x_sorted or h)
   MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K,
-             int(max_pairs), tpre, cpx, smax, parts);
+             int(max_pairs), tpre, cpx, smax, parts, Gs, Us);
   if (smax > 1) {
     const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
-    MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
-               offsets, C, L, N, K, tpre, cpx, smax, static_cast<const float*>(parts));
+    MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW, SAVE>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
+               offsets, C, L, N, K, tpre, cpx, smax, static_cast<const float*>(parts), Gs, Us);
   }
   return MOE_OK;
 }
@@ -899,9 +990,10 @@ moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, 
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                   bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                  hipStream_t s) {
-  if (K / BK < kEightWaveSteps) return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s);
-  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s);
+                  hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
+  if (K / BK < kEightWaveSteps)
+    return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
 }
 
 }  // namespace big
@@ -1055,10 +1147,11 @@ moe_status launch_bm(const FfnArgs& a) {
   const unsigned mslots = unsigned((a.max_pairs + BMT - 1) / BMT + L);
   MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2, BMT>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
              a.s, static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
-             static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H);
+             static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H, static_cast<T*>(a.g_out),
+             static_cast<T*>(a.u_out));
   MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1, BMT>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0, a.s,
              static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down), static_cast<const T*>(a.w_down),
-             static_cast<T*>(a.y_sorted), L, H, I);
+             static_cast<T*>(a.y_sorted), L, H, I, static_cast<T*>(nullptr), static_cast<T*>(nullptr));
   return MOE_OK;
 }
 
@@ -1083,7 +1176,8 @@ moe_status launch_small(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
   // decode-sized batches: a few rows per expert, bound by streaming the weights
-  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I)) {
+  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I) &&
+      a.g_out == nullptr) {
     bf16_t* h = static_cast<bf16_t*>(a.h);
     moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
                                       static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
@@ -1120,7 +1214,8 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
   MOE_LAUNCH("ffn_plan", big::plan_kernel, dim3(1), dim3(1024), 0, a.s, a.offsets, L, (I + big::BNE / 2 - 1) / (big::BNE / 2),
              (H + big::BNE - 1) / big::BNE, pre);
   moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
-                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, pre, parts, a.s);
+                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, pre, parts, a.s,
+                                 static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
   if (st != MOE_OK) return st;
   return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
                         static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.max_pairs,

@@ -96,6 +96,8 @@ struct FfnArgs {
   void* scratch;   // ffn_scratch_bytes: the large-tile path's tile plan and split-K pieces
   int64_t max_pairs;
   hipStream_t s;
+  void* g_out = nullptr;  // optional [P_max, I] each: the gate and up pre-activations (training forward)
+  void* u_out = nullptr;
 };
 // Scratch of the large-tile path (tile plan; split-K pieces when K is long), else 0.
 size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs);
@@ -110,5 +112,74 @@ struct CombineArgs {
   hipStream_t s;
 };
 moe_status launch_combine(const CombineArgs& a);
+
+// ---- backward ----------------------------------------------------------------
+struct CombineBwdArgs {
+  const moe_layer_desc* d;
+  const void* dy;        // [T, H]
+  const void* y_sorted;  // [P_max, H]
+  const int32_t* pair_row;
+  const float* topk_w;
+  void* dy_sorted;       // [P_max, H]
+  float* dl;             // [T, k]: gradient of the chosen logits
+  hipStream_t s;
+};
+moe_status launch_combine_backward(const CombineBwdArgs& a);
+
+struct FfnBwdArgs {
+  const moe_layer_desc* d;
+  const void* x_sorted;
+  const int32_t* offsets;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* gate;      // [P_max, I] saved pre-activations
+  const void* up;
+  const void* h;         // [P_max, I] saved silu(gate) * up
+  const void* dy_sorted; // [P_max, H]
+  void* dx_sorted;       // [P_max, H]
+  void* dw_gate;         // [L, I, H]
+  void* dw_up;
+  void* dw_down;         // [L, H, I]
+  void* dg;              // scratch [P_max, I] each
+  void* du;
+  int64_t max_pairs;
+  hipStream_t s;
+};
+moe_status launch_grouped_ffn_backward(const FfnBwdArgs& a);
+
+struct RouteBwdScratch {
+  void* dlogits;     // [T, Ep] in the layer's type (Ep = E rounded up to 8)
+  float* dlogits32;  // [T, Ep] float32 (bias gradient)
+  float* part;       // column sums per token chunk
+};
+size_t route_bwd_scratch_bytes(const moe_layer_desc* d);
+RouteBwdScratch carve_route_bwd_scratch(const moe_layer_desc* d, void* ws);
+
+struct RouteBwdArgs {
+  const moe_layer_desc* d;
+  const void* x;
+  const int32_t* topk_ids;
+  const float* dl;
+  void* dw_router;   // [E, H]
+  float* db_router;  // [E] or NULL
+  void* ws;          // route_bwd_scratch_bytes
+  hipStream_t s;
+};
+moe_status launch_route_backward(const RouteBwdArgs& a);
+
+struct DispatchBwdArgs {
+  const moe_layer_desc* d;
+  const void* dx_sorted;
+  const int32_t* pair_row;
+  const int32_t* topk_ids;
+  const float* dl;
+  const void* w_router;
+  void* dx;          // [T, H]
+  hipStream_t s;
+};
+moe_status launch_dispatch_backward(const DispatchBwdArgs& a);
+// Zero `bytes` (a multiple of 4) at a 16-byte aligned device pointer, by a kernel.
+moe_status launch_zero(const char* name, void* p, size_t bytes, hipStream_t s);
 
 }  // namespace moe

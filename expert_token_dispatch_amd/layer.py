@@ -121,3 +121,72 @@ class MoELayer:
         ys = self.grouped_ffn(dd["x_sorted"], dd["offsets"])
         y = self.combine(ys, dd["pair_row"], r["topk_w"])
         return {**r, **dd, "y_sorted": ys, "y": y}
+
+    # ---- training (Transformers "Expert parallelism", "Token dispatch") ----------
+    def saved_buffers(self, x_dtype) -> dict:
+        """Device buffers for the intermediates the training forward keeps."""
+        d = self.desc
+        T, k, Lc, H, I = d.num_tokens, d.top_k, d.local_count, d.hidden, d.intermediate
+        pm = max(self.max_pairs, 1)
+        return {
+            "topk_ids": self._empty((max(T, 1), k), torch.int32),
+            "topk_w": self._empty((max(T, 1), k), torch.float32),
+            "offsets": self._empty((Lc + 1,), torch.int32),
+            "pair_row": self._empty((max(T * k, 1),), torch.int32),
+            "x_sorted": self._empty((pm, H), x_dtype),
+            "gate": self._empty((pm, I), x_dtype),
+            "up": self._empty((pm, I), x_dtype),
+            "h": self._empty((pm, I), x_dtype),
+            "y_sorted": self._empty((pm, H), x_dtype),
+        }
+
+    def forward_train(self, x, opts=None, saved=None, y=None, counts_out=None, num_dropped_out=None):
+        """The layer forward that keeps what the backward needs; returns (y, saved)."""
+        d = self.desc
+        if y is None:
+            y = self._empty((d.num_tokens, d.hidden), x.dtype)
+        if saved is None:
+            saved = L.make_saved(self.saved_buffers(x.dtype))
+        L.moe_layer_forward_train(d, opts, x, self.w_router, self.b_router, self.w_gate, self.w_up, self.w_down, y,
+                                  saved, self.workspace(L.MOE_STAGE_LAYER), counts_out, num_dropped_out)
+        return y, saved
+
+    def grad_buffers(self, x_dtype) -> dict:
+        d = self.desc
+        T, E, Lc, H, I = d.num_tokens, d.num_experts, d.local_count, d.hidden, d.intermediate
+        return {
+            "dx": self._empty((max(T, 1), H), x_dtype),
+            "dw_router": self._empty((E, H), x_dtype),
+            "db_router": self._empty((E,), torch.float32) if self.b_router is not None else None,
+            "dw_gate": self._empty((Lc, I, H), x_dtype),
+            "dw_up": self._empty((Lc, I, H), x_dtype),
+            "dw_down": self._empty((Lc, H, I), x_dtype),
+        }
+
+    def backward(self, x, saved, dy, grads=None) -> dict:
+        """Gradients of the layer given dy, from forward_train's saved intermediates."""
+        if grads is None:
+            grads = self.grad_buffers(dy.dtype)
+        L.moe_layer_backward(self.desc, x, self.w_router, self.w_gate, self.w_up, self.w_down, saved, dy,
+                             grads["dx"], grads["dw_router"], grads["db_router"], grads["dw_gate"], grads["dw_up"],
+                             grads["dw_down"], self.workspace(L.MOE_STAGE_LAYER_BACKWARD))
+        return grads
+
+    def staged_backward(self, x, saved, dy) -> dict:
+        """The four backward stage calls one after another; returns every intermediate."""
+        d = self.desc
+        T, k, H = d.num_tokens, d.top_k, d.hidden
+        pm = max(self.max_pairs, 1)
+        t = saved._tensors
+        g = self.grad_buffers(dy.dtype)
+        dys = self._empty((pm, H), dy.dtype)
+        dl = self._empty((max(T, 1), k), torch.float32)
+        L.moe_combine_backward(d, dy, t["y_sorted"], t["pair_row"], t["topk_w"], dys, dl)
+        dxs = self._empty((pm, H), dy.dtype)
+        L.moe_grouped_ffn_backward(d, t["x_sorted"], t["offsets"], self.w_gate, self.w_up, self.w_down, t["gate"],
+                                   t["up"], t["h"], dys, dxs, g["dw_gate"], g["dw_up"], g["dw_down"],
+                                   ws=self.workspace(L.MOE_STAGE_FFN_BACKWARD))
+        L.moe_route_backward(d, x, t["topk_ids"], dl, g["dw_router"], g["db_router"],
+                             ws=self.workspace(L.MOE_STAGE_ROUTE_BACKWARD))
+        L.moe_dispatch_backward(d, dxs, t["pair_row"], t["topk_ids"], dl, self.w_router, g["dx"])
+        return {**g, "dy_sorted": dys, "dl": dl, "dx_sorted": dxs}

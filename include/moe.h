@@ -93,7 +93,10 @@ typedef enum {
   MOE_STAGE_DISPATCH = 1,
   MOE_STAGE_FFN = 2,
   MOE_STAGE_COMBINE = 3,
-  MOE_STAGE_LAYER = 4 /* moe_layer_forward: all intermediates of the layer */
+  MOE_STAGE_LAYER = 4, /* moe_layer_forward: all intermediates of the layer */
+  MOE_STAGE_FFN_BACKWARD = 5,   /* moe_grouped_ffn_backward: dg, du [P_max, I] each */
+  MOE_STAGE_ROUTE_BACKWARD = 6, /* moe_route_backward: the logit gradients [T, E] */
+  MOE_STAGE_LAYER_BACKWARD = 7  /* moe_layer_backward: all backward intermediates */
 } moe_stage;
 
 /* ------------------------------------------------------------------------ */
@@ -280,6 +283,114 @@ moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_route_opts* o
                                 const void* w_down, void* y, int32_t* topk_ids_out, float* topk_w_out,
                                 int32_t* counts_out, int64_t* num_dropped_out, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/* ======================================================================== */
+/* Training: the backward pass.                                              */
+/*                                                                           */
+/* Transformers "Expert parallelism", section "Token dispatch": every rank   */
+/* trains on its own share of the batch, and an expert's weight gradient is  */
+/* the sum over the pairs that reached it; an expert that received no       */
+/* tokens still takes part (its gradient is zero).  The gradients are the   */
+/* chain rule through the forward above, given dy = dLoss/dy for the layer   */
+/* output y (no residual).  Which experts a token uses (top-k, selection     */
+/* bias, group limit, capacity) is a discrete choice and carries no          */
+/* gradient; the router receives it through the softmax over the k chosen   */
+/* logits (all k slots take part; a slot with no kept local pair has a zero  */
+/* weight gradient).  Rounding: every stored gradient is accumulated in      */
+/* float32 and rounded to dtype once; dl and db are float32.                 */
+/* ======================================================================== */
+
+/* What the training forward keeps for the backward (all device, caller-owned).
+ * The index arrays and rows are the forward's own (see moe_route,
+ * moe_dispatch, moe_grouped_ffn). */
+typedef struct moe_saved {
+  int32_t* topk_ids;  /* [T, k] int32 global expert ids */
+  float* topk_w;      /* [T, k] float32 routing weights */
+  int32_t* offsets;   /* [L+1] int32 segment offsets */
+  int32_t* pair_row;  /* [T*k] int32 sorted row of each pair, -1 = not local or dropped */
+  void* x_sorted;     /* [P_max, H] dtype */
+  void* gate;         /* [P_max, I] dtype: x_sorted Wg^T (rounded once) */
+  void* up;           /* [P_max, I] dtype: x_sorted Wu^T */
+  void* h;            /* [P_max, I] dtype: silu(gate) * up from the float32 products */
+  void* y_sorted;     /* [P_max, H] dtype */
+} moe_saved;
+
+/* moe_grouped_ffn that also keeps the gate and up pre-activations (and h in
+ * the caller's buffer instead of the workspace).  y_sorted and h are the
+ * values moe_grouped_ffn produces (the skinny decode kernel is not used).
+ *   h, gate, up  device [P_max, I] dtype out
+ *   ws           device workspace of MOE_STAGE_FFN bytes */
+moe_status moe_grouped_ffn_train(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
+                                 const void* w_gate, const void* w_up, const void* w_down, void* y_sorted,
+                                 void* h, void* gate, void* up, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward_ex that writes every intermediate the backward needs
+ * into `saved` (all nine pointers required).  counts_out and
+ * num_dropped_out are optional.  Workspace: MOE_STAGE_LAYER bytes. */
+moe_status moe_layer_forward_train(const moe_layer_desc* d, const moe_route_opts* opts, const void* x,
+                                   const void* w_router, const float* b_router, const void* w_gate,
+                                   const void* w_up, const void* w_down, void* y, const moe_saved* saved,
+                                   int32_t* counts_out, int64_t* num_dropped_out, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* Combine backward with the softmax over k.  For each kept local pair
+ * (t, j) at row q: dy_sorted[q] = topk_w[t,j] * dy[t] (rounded once), and
+ * dw[t,j] = <dy[t], y_sorted[q]> (float32; 0 for slots without a row); then
+ * dl[t,j] = topk_w[t,j] * (dw[t,j] - sum_i topk_w[t,i] dw[t,i]).
+ *   dy         device [T, H] dtype;  y_sorted device [P_max, H] dtype
+ *   pair_row   device [T*k] int32;   topk_w device [T, k] float32
+ *   dy_sorted  device [P_max, H] dtype out (rows >= P untouched)
+ *   dl         device [T, k] float32 out: gradient of the chosen logits */
+moe_status moe_combine_backward(const moe_layer_desc* d, const void* dy, const void* y_sorted,
+                                const int32_t* pair_row, const float* topk_w, void* dy_sorted, float* dl,
+                                void* stream);
+
+/* The local experts' backward.  Per expert e with rows [o_e, o_{e+1}):
+ *   dh = dy_sorted Wd_e;  dg = dh * up * silu'(gate);  du = dh * silu(gate)
+ *   dx_sorted = dg Wg_e + du Wu_e
+ *   dw_down[e] = dy_sorted^T h,  dw_gate[e] = dg^T x_sorted,  dw_up[e] = du^T x_sorted
+ * summed over the expert's rows (an empty expert gets zeros).
+ *   gate, up, h          device [P_max, I] dtype (from moe_grouped_ffn_train)
+ *   dy_sorted            device [P_max, H] dtype (from moe_combine_backward)
+ *   dx_sorted            device [P_max, H] dtype out
+ *   dw_gate, dw_up       device [L, I, H] dtype out;  dw_down [L, H, I] out
+ *   ws                   device workspace of MOE_STAGE_FFN_BACKWARD bytes */
+moe_status moe_grouped_ffn_backward(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
+                                    const void* w_gate, const void* w_up, const void* w_down, const void* gate,
+                                    const void* up, const void* h, const void* dy_sorted, void* dx_sorted,
+                                    void* dw_gate, void* dw_up, void* dw_down, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* The router's parameter gradients: dlogits[t, e] = sum of dl[t, j] over the
+ * slots with topk_ids[t, j] = e (0 elsewhere); dw_router = dlogits^T x and
+ * db_router = sum over tokens of dlogits.
+ *   x          device [T, H] dtype;  topk_ids device [T, k] int32
+ *   dl         device [T, k] float32 (from moe_combine_backward)
+ *   dw_router  device [E, H] dtype out
+ *   db_router  device [E] float32 out, or NULL when the router has no bias
+ *   ws         device workspace of MOE_STAGE_ROUTE_BACKWARD bytes */
+moe_status moe_route_backward(const moe_layer_desc* d, const void* x, const int32_t* topk_ids, const float* dl,
+                              void* dw_router, float* db_router, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient of the layer input: dx[t] = sum_j dx_sorted[pair_row[t*k+j]]
+ * (kept local pairs, slot order) + sum_j dl[t,j] w_router[topk_ids[t,j]],
+ * accumulated in float32 and rounded once.
+ *   dx_sorted  device [P_max, H] dtype;  pair_row device [T*k] int32
+ *   topk_ids   device [T, k] int32;      dl device [T, k] float32
+ *   w_router   device [E, H] dtype;      dx device [T, H] dtype out */
+moe_status moe_dispatch_backward(const moe_layer_desc* d, const void* dx_sorted, const int32_t* pair_row,
+                                 const int32_t* topk_ids, const float* dl, const void* w_router, void* dx,
+                                 void* stream);
+
+/* The four backward stages in one call, from the training forward's saved
+ * intermediates.  db_router may be NULL (no router bias).  Workspace:
+ * MOE_STAGE_LAYER_BACKWARD bytes.
+ *   dy  device [T, H] dtype;  dx device [T, H] dtype out
+ *   dw_router [E, H], dw_gate [L, I, H], dw_up [L, I, H], dw_down [L, H, I] dtype out */
+moe_status moe_layer_backward(const moe_layer_desc* d, const void* x, const void* w_router, const void* w_gate,
+                              const void* w_up, const void* w_down, const moe_saved* saved, const void* dy,
+                              void* dx, void* dw_router, float* db_router, void* dw_gate, void* dw_up,
+                              void* dw_down, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -169,3 +169,67 @@ def test_selection_bias_update_arguments_checked():
     assert lib.moe_selection_bias_update(ctypes.byref(d), None, 256, 0.001, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_selection_bias_update(ctypes.byref(d), 256, None, 0.001, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_selection_bias_update(ctypes.byref(d), 256, 256, float("nan"), None) == L.MOE_ERR_INVALID_ARG
+
+
+def _saved(**null):
+    v = L.Saved(*[None if n in null else 256 for n, _ in L.Saved._fields_])
+    return v
+
+
+def test_backward_workspace_sizes():
+    d = etd.make_desc(1000, 512, 896, 8, 2)
+    pm = 2000
+    assert etd.moe_workspace_size(d, L.MOE_STAGE_FFN_BACKWARD) >= 2 * pm * 896 * 2
+    assert etd.moe_workspace_size(d, L.MOE_STAGE_ROUTE_BACKWARD) >= 1000 * 8 * (2 + 4)
+    lb = etd.moe_workspace_size(d, L.MOE_STAGE_LAYER_BACKWARD)
+    assert lb >= (etd.moe_workspace_size(d, L.MOE_STAGE_FFN_BACKWARD) + etd.moe_workspace_size(d, L.MOE_STAGE_ROUTE_BACKWARD)
+                  + 2 * pm * 512 * 2 + 1000 * 2 * 4)
+    n = ctypes.c_size_t()
+    assert L.lib().moe_workspace_size(ctypes.byref(d), 8, ctypes.byref(n)) == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_arguments_rejected_before_launch():
+    lib = L.lib()
+    d = etd.make_desc(16, 64, 64, 8, 2)
+    b = ctypes.byref
+    # the fused backward needs the saved intermediates
+    st = lib.moe_layer_backward(b(d), 256, 256, 256, 256, 256, None, 256, 256, 256, None, 256, 256, 256, 256, 1 << 30,
+                                None)
+    assert st == L.MOE_ERR_INVALID_ARG and "saved is NULL" in L.moe_last_error()
+    v = _saved(gate=1)
+    st = lib.moe_layer_backward(b(d), 256, 256, 256, 256, 256, ctypes.addressof(v), 256, 256, 256, None, 256, 256, 256,
+                                256, 1 << 30, None)
+    assert st == L.MOE_ERR_INVALID_ARG and "gate" in L.moe_last_error()
+    v = _saved()
+    st = lib.moe_layer_backward(b(d), 256, 256, 256, 256, 256, ctypes.addressof(v), 256, 256, 256, None, 256, 256, 256,
+                                256, 16, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    v = _saved(h=1)
+    st = lib.moe_layer_forward_train(b(d), None, 256, 256, None, 256, 256, 256, 256, ctypes.addressof(v),
+                                     None, None, 256, 1 << 30, None)
+    assert st == L.MOE_ERR_INVALID_ARG and "h is NULL" in L.moe_last_error()
+    # stage calls
+    assert lib.moe_combine_backward(b(d), None, 256, 256, 256, 256, 256, None) == L.MOE_ERR_INVALID_ARG
+    assert "dy is NULL" in L.moe_last_error()
+    st = lib.moe_grouped_ffn_backward(b(d), *([256] * 13), 256, 16, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = lib.moe_route_backward(b(d), 256, 256, 256, 264, None, 256, 1 << 20, None)
+    assert st == L.MOE_ERR_INVALID_ARG and "dw_router" in L.moe_last_error()
+    assert lib.moe_dispatch_backward(b(d), 256, 256, 256, 256, None, 256, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_ffn_train(b(d), 256, 256, 256, 256, 256, 256, 256, None, 256, 256, 1 << 30, None) \
+        == L.MOE_ERR_INVALID_ARG
+
+
+def test_backward_with_zero_tokens():
+    # no rows: the stage calls that only touch rows are no-ops; the weight gradients of a
+    # layer that saw no tokens are zero, so those calls still need their buffers
+    lib = L.lib()
+    d = etd.make_desc(0, 64, 64, 8, 2)
+    b = ctypes.byref
+    assert lib.moe_combine_backward(b(d), *([None] * 6), None) == L.MOE_OK
+    assert lib.moe_dispatch_backward(b(d), *([None] * 6), None) == L.MOE_OK
+    assert lib.moe_grouped_ffn_train(b(d), *([None] * 10), 0, None) == L.MOE_OK
+    assert lib.moe_layer_forward_train(b(d), *([None] * 12), 0, None) == L.MOE_OK
+    assert lib.moe_grouped_ffn_backward(b(d), *([None] * 13), None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(b(d), None, None, None, None, None, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_backward(b(d), *([None] * 14), 0, None) == L.MOE_ERR_INVALID_ARG

@@ -1,0 +1,273 @@
+"""GPU parity of the backward pass (Transformers "Expert parallelism", "Token
+dispatch": an expert's gradient sums what reached it) through the C ABI.
+
+Scaled copies of the five workloads (several tiles, ragged tails): every
+stage output and gradient against the float64 backward oracle, which routes on
+the GPU's own float32 logits so both sides make the same discrete choices.
+Full sizes: the fused and staged calls agree bit for bit, the saved
+pre-activations and sampled experts' gradients match the oracle run on the
+GPU's own stage inputs, and the homogeneity identities hold.
+
+Measures (the float32 / bf16 bars of the forward):
+  * rows of dx, dx_sorted, dy_sorted, gate and up by the row measure of the
+    forward (float32: max |error| / max |row|; bf16: max |error| / |row|_2);
+  * weight gradients per expert matrix (and the router's as one matrix):
+    float32 max |error| / max |entry|, bf16 |error|_F / |matrix|_F.  A row of
+    an expert that saw a few rows is a few outer products, so its norm follows
+    dg or dh of those rows, which are dot products that can cancel: the
+    inputs' legitimate bf16 rounding then reads as a large error of that row
+    alone (an emulation of the rounding points alone gives 0.47 on the
+    decode-sized layer's row measure, 3e-3 per expert);
+  * rows or matrices the oracle makes exactly zero (empty experts, experts
+    never chosen, fully dropped tokens) must be exactly zero;
+  * dl (a difference of dot products): |error| <= 2 tol w[t,j] |dy_t| max_j |y_sorted row|,
+    the rounding bound of <dy, y_sorted> scaled through the softmax;
+  * db (a sum over tokens of terms of either sign): |error| <= tol * the L2 norm of its terms.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_backward as B
+import synth
+from tests._harness import layer_of, np_of, row_error, say, tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_fp32": synth.spec("tiny_fp32"),
+    "mixtral_like": synth.spec("mixtral_like", T=1000, H=512, I=896),
+    "gptoss_ep8_share": synth.spec("gptoss_ep8_share", T=2048, H=320, I=288),
+    "decode_small": synth.spec("decode_small", H=512, I=256),
+    "skewed_capacity": synth.spec("skewed_capacity", T=4096, H=256, I=384),
+}
+
+
+def to_dev(a, s):
+    from expert_token_dispatch_amd.layer import to_device
+    return to_device(a, s.dtype)
+
+
+def run_gpu(s, inp):
+    layer, x = layer_of(inp)
+    dy_h = synth.make_upstream_grad(s)
+    dy = to_dev(dy_h, s)
+    logits = layer.route(x, want_logits=True)["logits"]
+    y, saved = layer.forward_train(x)
+    st = layer.staged_backward(x, saved, dy)
+    fu = layer.backward(x, saved, dy)
+    torch.cuda.synchronize()
+    gpu = {k: np_of(v) for k, v in saved._tensors.items()}
+    gpu.update({k: (None if v is None else np_of(v)) for k, v in st.items()})
+    gpu["y"] = np_of(y)
+    gpu["logits"] = np_of(logits)
+    fused = {k: (None if v is None else np_of(v)) for k, v in fu.items()}
+    return layer, x, dy_h, gpu, fused
+
+
+def rows_ok(name, got, ref, dtype):
+    e = row_error(got.reshape(-1, got.shape[-1]), ref.reshape(-1, ref.shape[-1]), dtype)
+    say(f"[bwd]   {name}: row error {e:.2e}")
+    assert e <= tol(dtype), f"{name}: row error {e:.3e} above {tol(dtype)}"
+
+
+def mat_ok(name, got, ref, dtype):
+    """Per-matrix measure of a stack of weight gradients [n, rows, cols] (or one matrix)."""
+    got = got.reshape((-1,) + got.shape[-2:])
+    ref = ref.reshape((-1,) + ref.shape[-2:])
+    worst = 0.0
+    for g, r in zip(got, ref):
+        zr = ~np.any(r != 0, axis=1)
+        assert not np.any(g[zr]), f"{name}: rows that must be exactly zero are not"
+        if dtype == "f32":
+            n, e = np.abs(r).max(), np.abs(g - r).max()
+        else:
+            n, e = np.linalg.norm(r), np.linalg.norm(g - r)
+        if n > 0:
+            worst = max(worst, float(e / n))
+    say(f"[bwd]   {name}: matrix error {worst:.2e}")
+    assert worst <= tol(dtype), f"{name}: matrix error {worst:.3e} above {tol(dtype)}"
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def case(request):
+    s = SMALL[request.param]
+    say(f"[bwd] case {s}")
+    inp = synth.make_layer(s)
+    layer, x, dy_h, gpu, fused = run_gpu(s, inp)
+    dy = oracle.decode(dy_h, s.dtype)
+    ref = B.layer_backward(inp, dy, logits=gpu["logits"].astype(np.float64))
+    return s, inp, gpu, fused, ref
+
+
+def test_training_forward_keeps_the_forward(case):
+    s, inp, gpu, fused, ref = case
+    f = ref["forward"]
+    np.testing.assert_array_equal(gpu["topk_ids"], f["topk_ids"])
+    np.testing.assert_array_equal(gpu["offsets"], f["offsets"])
+    np.testing.assert_array_equal(gpu["pair_row"], f["pair_row"])
+    P = int(f["offsets"][-1])
+    np.testing.assert_array_equal(gpu["x_sorted"][:P], f["x_sorted"][:P])
+    rows_ok("y", gpu["y"], f["y"], s.dtype)
+    rows_ok("y_sorted", gpu["y_sorted"][:P], f["y_sorted"][:P], s.dtype)
+    # the saved pre-activations: x_sorted Wg^T and x_sorted Wu^T of each segment
+    off = f["offsets"]
+    for i in range(s.L):
+        a, b = int(off[i]), int(off[i + 1])
+        if a == b:
+            continue
+        xs = f["x_sorted"][a:b]
+        rows_ok(f"gate[{i}]", gpu["gate"][a:b], xs @ oracle.decode(inp["w_gate"][i], s.dtype).T, s.dtype)
+        rows_ok(f"up[{i}]", gpu["up"][a:b], xs @ oracle.decode(inp["w_up"][i], s.dtype).T, s.dtype)
+
+
+def test_combine_backward(case):
+    s, inp, gpu, fused, ref = case
+    P = int(ref["forward"]["offsets"][-1])
+    rows_ok("dy_sorted", gpu["dy_sorted"][:P], ref["dy_sorted"][:P], s.dtype)
+    # dl: rounding bound of the dot products, scaled through the softmax
+    f = ref["forward"]
+    dy = oracle.decode(synth.make_upstream_grad(s), s.dtype)
+    T, k = f["topk_w"].shape
+    ynorm = np.zeros((T, k))
+    pr = f["pair_row"].reshape(T, k)
+    has = pr >= 0
+    ynorm[has] = np.linalg.norm(f["y_sorted"][pr[has]], axis=1)
+    scale = np.linalg.norm(dy, axis=1) * ynorm.max(axis=1)
+    bound = 2 * tol(s.dtype) * f["topk_w"] * scale[:, None]
+    err = np.abs(gpu["dl"] - ref["dl"])
+    say(f"[bwd]   dl: max error / bound {float((err / np.maximum(bound, 1e-300)).max()):.2e}")
+    assert np.all(err <= bound)
+    assert np.all(gpu["dl"][scale == 0] == 0)
+
+
+def test_expert_gradients(case):
+    s, inp, gpu, fused, ref = case
+    P = int(ref["forward"]["offsets"][-1])
+    rows_ok("dx_sorted", gpu["dx_sorted"][:P], ref["dx_sorted"][:P], s.dtype)
+    mat_ok("dw_gate", gpu["dw_gate"], ref["dw_gate"], s.dtype)
+    mat_ok("dw_up", gpu["dw_up"], ref["dw_up"], s.dtype)
+    mat_ok("dw_down", gpu["dw_down"], ref["dw_down"], s.dtype)
+
+
+def test_router_and_input_gradients(case):
+    s, inp, gpu, fused, ref = case
+    mat_ok("dw_router", gpu["dw_router"], ref["dw_router"], s.dtype)
+    rows_ok("dx", gpu["dx"], ref["dx"], s.dtype)
+    if inp["b_router"] is None:
+        assert gpu["db_router"] is None
+    else:
+        terms = np.sqrt((ref["dlogits"] ** 2).sum(axis=0))
+        err = np.abs(gpu["db_router"] - ref["db_router"])
+        say(f"[bwd]   db: max error / term norm {float((err / np.maximum(terms, 1e-300)).max()):.2e}")
+        assert np.all(err <= tol(s.dtype) * terms)
+
+
+def test_fused_equals_staged(case):
+    s, inp, gpu, fused, ref = case
+    for k, v in fused.items():
+        if v is None:
+            assert gpu[k] is None
+        else:
+            np.testing.assert_array_equal(v, gpu[k], err_msg=k)
+
+
+def test_backward_determinism():
+    s = SMALL["skewed_capacity"]
+    inp = synth.make_layer(s)
+    a = run_gpu(s, inp)[4]
+    b = run_gpu(s, inp)[4]
+    for k in a:
+        if a[k] is not None:
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_backward_edges():
+    # an expert range at the end, empty experts, k = E, T not a tile multiple, f32 and bf16
+    for s in (synth.spec("tiny_fp32", T=37, E=8, k=8, local_begin=0, L=8),
+              synth.spec("gptoss_ep8_share", T=70, H=72, I=40, local_begin=112, L=16),
+              synth.spec("mixtral_like", T=3, H=136, I=200, E=8, k=2)):
+        say(f"[bwd] edge {s}")
+        inp = synth.make_layer(s)
+        layer, x, dy_h, gpu, fused = run_gpu(s, inp)
+        ref = B.layer_backward(inp, oracle.decode(dy_h, s.dtype), logits=gpu["logits"].astype(np.float64))
+        for k in ("dw_gate", "dw_up", "dw_down", "dw_router"):
+            mat_ok(k, gpu[k], ref[k], s.dtype)
+        rows_ok("dx", gpu["dx"], ref["dx"], s.dtype)
+
+
+def test_zero_tokens_zero_weight_gradients():
+    import expert_token_dispatch_amd as etd
+    from expert_token_dispatch_amd.layer import MoELayer
+    s = synth.spec("mixtral_like", T=0, H=64, I=32)
+    inp = synth.make_layer(s.replace(T=1))
+    layer = MoELayer.from_host(etd.make_desc(0, s.H, s.I, s.E, s.k, 0, s.L, 0.0, s.dtype), inp)
+    x = torch.empty((0, s.H), dtype=torch.bfloat16, device="cuda")
+    y, saved = layer.forward_train(x)
+    g = layer.grad_buffers(torch.bfloat16)
+    for v in g.values():
+        if v is not None:
+            v.fill_(1.0)
+    layer.backward(x, saved, x, grads=g)
+    torch.cuda.synchronize()
+    for k in ("dw_router", "dw_gate", "dw_up", "dw_down"):
+        assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+# --------------------------------------------------------------------------- full sizes
+FULL = ["tiny_fp32", "decode_small", "gptoss_ep8_share", "skewed_capacity", "mixtral_like"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_backward(name):
+    s = synth.spec(name)
+    say(f"[bwd] full size {s}")
+    inp = synth.make_layer(s)
+    layer, x, dy_h, gpu, fused = run_gpu(s, inp)
+    for k, v in fused.items():
+        if v is not None:
+            np.testing.assert_array_equal(v, gpu[k], err_msg=k)
+    off = gpu["offsets"].astype(np.int64)
+    sizes = np.diff(off)
+    # homogeneity: y is linear in Wd and in Wu, so sum <W, dW> = <dy, y>
+    dy = oracle.decode(dy_h, s.dtype)
+    ydy = float((dy * gpu["y"]).sum())
+    for wname in ("w_down", "w_up"):
+        w = layer.w_down if wname == "w_down" else layer.w_up
+        gw = torch.from_numpy(gpu["d" + wname]).to(w.device)
+        ip = float((w.double() * gw.double()).sum())
+        say(f"[bwd]   <{wname}, d{wname}> = {ip:.6e}, <dy, y> = {ydy:.6e}")
+        assert abs(ip - ydy) <= 2e-2 * np.sqrt(float((dy * dy).sum()) * float((gpu["y"] ** 2).sum()))
+    # sampled experts against the oracle, on the GPU's own x_sorted and dy_sorted
+    big = int(np.argmax(sizes))
+    experts = [big] if s.H * s.I * int(sizes[big]) > 2e10 else sorted({big, int(np.argsort(sizes)[len(sizes) // 2])})
+    for i in experts:
+        a, b = int(off[i]), int(off[i + 1])
+        if a == b:
+            continue
+        rows = np.arange(a, b)
+        if s.H * s.I * (b - a) > 2e10:   # the largest segments: 64 rows for dx_sorted, dW by its definition
+            rows = rows[:: max(1, (b - a) // 64)]
+        wg = oracle.decode(inp["w_gate"][i], s.dtype)
+        wu = oracle.decode(inp["w_up"][i], s.dtype)
+        wd = oracle.decode(inp["w_down"][i], s.dtype)
+        xs = gpu["x_sorted"][rows]
+        r = B.expert_ffn_backward(xs, wg, wu, wd, gpu["dy_sorted"][rows])
+        say(f"[bwd]   expert {i}: {b - a} rows, {len(rows)} checked")
+        rows_ok(f"gate[{i}]", gpu["gate"][rows], r["g"], s.dtype)
+        rows_ok(f"dx_sorted[{i}]", gpu["dx_sorted"][rows], r["dv"], s.dtype)
+        if len(rows) == b - a:
+            mat_ok(f"dw_gate[{i}]", gpu["dw_gate"][i], r["dwg"], s.dtype)
+            mat_ok(f"dw_up[{i}]", gpu["dw_up"][i], r["dwu"], s.dtype)
+            mat_ok(f"dw_down[{i}]", gpu["dw_down"][i], r["dwd"], s.dtype)
+        else:
+            # dW_down = dy_sorted^T h over the whole segment (hundreds of rows), on sampled output rows
+            hs = gpu["h"][a:b]
+            for hrow in (0, s.H // 3, s.H - 1):
+                want = gpu["dy_sorted"][a:b, hrow] @ hs
+                rows_ok(f"dw_down[{i}][{hrow}]", gpu["dw_down"][i][hrow][None], want[None], s.dtype)
+    # experts that received nothing get exactly zero
+    for i in np.flatnonzero(sizes == 0):
+        assert not np.any(gpu["dw_gate"][i]) and not np.any(gpu["dw_up"][i]) and not np.any(gpu["dw_down"][i])
