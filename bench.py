@@ -108,6 +108,10 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
         return (2 * P * I + 2 * touched_experts * I * H + P * H) * dt, 4.0 * P * H * I
     if name == "ffn_gate_up_wgrad":
         return (2 * P * I + P * H + 2 * Lc * I * H) * dt, 4.0 * P * H * I
+    if name == "ffn_bwd_transpose":  # one expert matrix stack read and written per launch
+        return 2 * Lc * H * I * dt, 0.0
+    if name == "ffn_bwd_seg_transpose":  # dy_sorted, h, dg|du, x_sorted: (2H + 3I) columns over 4 launches
+        return 2 * P * (2 * H + 3 * I) * dt / 4, 0.0
     if name == "route_bwd_dlogits":
         return T * k * 8 + T * Ep * (dt + 4), 0.0
     if name == "route_bwd_wgrad":

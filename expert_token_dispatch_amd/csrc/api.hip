@@ -146,8 +146,8 @@ LayerWs layer_layout(const moe_layer_desc* d, void* base) {
   return w;
 }
 
-// moe_grouped_ffn_backward's workspace: dg and du [P_max, I]
-size_t ffn_bwd_bytes(const moe_layer_desc* d) { return 2 * ffn_h_bytes(d); }
+// moe_grouped_ffn_backward's workspace: dg | du [P_max, 2I] and the large-tile path's scratch
+size_t ffn_bwd_bytes(const moe_layer_desc* d) { return ffn_bwd_scratch_bytes(d, max_pairs_of(d)); }
 
 // Layout of the moe_layer_backward workspace.
 struct LayerBwdWs {
@@ -660,7 +660,7 @@ moe_status moe_grouped_ffn_backward(const moe_layer_desc* d, const void* x_sorte
                      dw_down));
   TRY(check_ws(d, MOE_STAGE_FFN_BACKWARD, ws, ws_bytes));
   FfnBwdArgs a{d, x_sorted, offsets, w_gate, w_up, w_down, gate, up, h, dy_sorted, dx_sorted, dw_gate, dw_up,
-               dw_down, ws, static_cast<char*>(ws) + ffn_h_bytes(d), max_pairs_of(d), s};
+               dw_down, ws, max_pairs_of(d), s};
   return launch_grouped_ffn_backward(a);
 }
 
@@ -718,9 +718,8 @@ moe_status moe_layer_backward(const moe_layer_desc* d, const void* x, const void
   TRY(dispatch_bwd_checks(w.dx_sorted, v.pair_row, v.topk_ids, w.dl, w_router, dx));
   CombineBwdArgs ca{d, dy, v.y_sorted, v.pair_row, v.topk_w, w.dy_sorted, w.dl, s};
   TRY(launch_combine_backward(ca));
-  char* ffn = static_cast<char*>(w.ffn);
   FfnBwdArgs fa{d, v.x_sorted, v.offsets, w_gate, w_up, w_down, v.gate, v.up, v.h, w.dy_sorted, w.dx_sorted,
-                dw_gate, dw_up, dw_down, ffn, ffn + ffn_h_bytes(d), max_pairs_of(d), s};
+                dw_gate, dw_up, dw_down, w.ffn, max_pairs_of(d), s};
   TRY(launch_grouped_ffn_backward(fa));
   RouteBwdArgs ra{d, x, v.topk_ids, w.dl, dw_router, db_router, w.route, s};
   TRY(launch_route_backward(ra));

@@ -29,6 +29,8 @@
 // chunk per thread and written to LDS transposed, as (k, k+1) pairs.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -351,16 +353,16 @@ __device__ __forceinline__ void silu_and_grad(float g, float& a, float& da) {
 
 template <typename T>
 struct DgradArgs {
-  const T* A[2];         // [P, K[p]] rows = sorted pairs
+  const T* A[2];         // [P, K[p]] rows = sorted pairs, row stride lda
   int K[2];
+  int lda;
   const T* B[2];         // expert e: B[p] + e * b_estride, element (k, n) at [k * N + n]
   int64_t b_estride;
   int N;
   T* C;                  // [P, N] (plain epilogue)
   const T* G;            // SwiGLU epilogue: saved pre-activations [P, N] ...
   const T* U;
-  T* DG;                 // ... and their gradients [P, N]
-  T* DU;
+  T* DGU;                // ... and their gradients side by side: [P, 2N], dg then du
   const int32_t* offsets;
   int L;
 };
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradArgs<T> p) {
   const T* const A1 = p.A[1];
   const T* const B0 = p.B[0] + size_t(expert) * p.b_estride;
   const T* const B1 = p.B[1] + size_t(expert) * p.b_estride;
-  const int K0 = p.K[0], K1 = p.K[1], N = p.N;
+  const int K0 = p.K[0], K1 = p.K[1], N = p.N, lda = p.lda;
   const int nk0 = (K0 + BK - 1) / BK;
   const int nks = nk0 + (NPROD > 1 ? (K1 + BK - 1) / BK : 0);
   RowTile<T> ta;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradArgs<T> p) {
     const bool q = NPROD > 1 && s >= nk0;
     const int k0 = (s - (q ? nk0 : 0)) * BK;
     const int Kq = q ? K1 : K0;
-    ta.load(q ? A1 : A0, Kq, row0, rows, k0, Kq);
+    ta.load(q ? A1 : A0, lda, row0, rows, k0, Kq);
     tb.load(q ? B1 : B0, N, k0, Kq, n0, N);
   };
   if (nks > 0) {
@@ -454,8 +456,9 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradArgs<T> p) {
             const float gv = Elem<T>::to_f32(p.G[at]), uv = Elem<T>::to_f32(p.U[at]);
             float a, da;
             silu_and_grad(gv, a, da);
-            p.DG[at] = Elem<T>::from_f32(v * uv * da);
-            p.DU[at] = Elem<T>::from_f32(v * a);
+            const size_t o2 = size_t(row0 + rt) * 2 * p.N + col;
+            p.DGU[o2] = Elem<T>::from_f32(v * uv * da);
+            p.DGU[o2 + p.N] = Elem<T>::from_f32(v * a);
           }
         }
       }
@@ -472,6 +475,7 @@ struct WgradArgs {
   int M, N;
   const int32_t* offsets; // NULL: one segment [0, k_total)
   int64_t k_total;
+  float* partial;         // split-K (one segment): [gridDim.z, M, N] float32 pieces, else NULL
 };
 
 // C[z]_e = A[z]_e^T B_e, the reduction over expert e's segment; an empty
@@ -480,11 +484,19 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs<T> p) {
   using G = Mma<T>;
   constexpr int BK = G::BK;
-  const int z = blockIdx.z, e = blockIdx.y;
+  // split-K: blockIdx.z picks a K slice instead of the (A, C) pair
+  const bool split = p.partial != nullptr;
+  const int z = split ? 0 : blockIdx.z, e = blockIdx.y;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
-  const int64_t o = p.offsets ? p.offsets[e] : 0;
-  const int64_t kseg = p.offsets ? p.offsets[e + 1] - o : p.k_total;
+  int64_t o = p.offsets ? p.offsets[e] : 0;
+  int64_t kseg = p.offsets ? p.offsets[e + 1] - o : p.k_total;
+  if (split) {
+    const int64_t per = ((kseg + gridDim.z - 1) / gridDim.z + BK - 1) / BK * BK;
+    const int64_t lo = min(kseg, per * blockIdx.z);
+    o += lo;
+    kseg = min(kseg - lo, per);
+  }
   const T* A = (z ? p.A[1] : p.A[0]) + o * p.lda;
   const T* B = p.B + o * p.N;
   __shared__ __attribute__((aligned(16))) T As[2][BM * G::kLd];
@@ -524,6 +536,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs<T> p) {
   }
 
   T* C = (z ? p.C[1] : p.C[0]) + size_t(e) * p.M * p.N;
+  float* part = split ? p.partial + size_t(blockIdx.z) * p.M * p.N : nullptr;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -532,9 +545,102 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs<T> p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int mt = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (mt < p.M && col < p.N) C[size_t(mt) * p.N + col] = Elem<T>::from_f32(acc[i][j][r]);
+        if (mt < p.M && col < p.N) {
+          if (split)
+            part[size_t(mt) * p.N + col] = acc[i][j][r];
+          else
+            C[size_t(mt) * p.N + col] = Elem<T>::from_f32(acc[i][j][r]);
+        }
       }
     }
+}
+
+// Sums the split-K pieces in slice order and rounds once.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict__ partial, int pieces, int64_t n,
+                                                         T* __restrict__ C) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.0f;
+  for (int z = 0; z < pieces; ++z) v += partial[size_t(z) * n + i];
+  C[i] = Elem<T>::from_f32(v);
+}
+
+// Transpose of stacked matrices: dst[l][c][off + r] = src[l][r][c], src [L, R, C],
+// dst rows of ld elements.  64 x 64 tiles through LDS (R and C multiples of 64):
+// rows are read and written as 16-byte vectors.
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ src, int R, int C,
+                                                        bf16_t* __restrict__ dst, int ld, int off) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
+  const int l = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const bf16_t* s = src + size_t(l) * R * C;
+  bf16_t* d = dst + size_t(l) * C * ld;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = t / 8 + 32 * j, c8 = (t % 8) * 8;
+    *reinterpret_cast<u32x4_t*>(&tile[r][c8]) = *reinterpret_cast<const u32x4_t*>(s + size_t(r0 + r) * C + c0 + c8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = t / 8 + 32 * j, r8 = (t % 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = uint32_t(tile[r8 + 2 * e][c]) | (uint32_t(tile[r8 + 2 * e + 1][c]) << 16);
+    *reinterpret_cast<u32x4_t*>(d + size_t(c0 + c) * ld + off + r0 + r8) = u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Per-expert transposed blocks for the weight gradients on the large tile: for
+// expert e with rows [o_e, o_e + n_e) of X [P, Cw], the block at element offset
+// Cw * Q_e is [Cw, K_e] with [c][k] = X[o_e + k][c] for k < n_e and zero up to
+// K_e = max(64, n_e rounded up to 64); Q_e = sum of K_e' over e' < e.
+// blockIdx.y enumerates the 64-row blocks of all experts (at most
+// ceil(P_max/64) + L of them; surplus blocks exit), blockIdx.x the 64-column blocks.
+__device__ __forceinline__ int seg_k(int n) { return n <= 64 ? 64 : (n + 63) / 64 * 64; }
+
+__global__ __launch_bounds__(256) void seg_transpose_kernel(const bf16_t* __restrict__ X, int Cw,
+                                                            const int32_t* __restrict__ offsets, int L,
+                                                            bf16_t* __restrict__ XT) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
+  const int c0 = blockIdx.x * 64, t = threadIdx.x;
+  // row blocks y = blockIdx.y, blockIdx.y + gridDim.y, ... over all experts; the
+  // expert walk restarts where the previous block of this thread block left off
+  int e = 0, base = 0;  // expert e's row blocks start at block number base
+  int64_t q = 0;
+  for (int y = blockIdx.y;; y += gridDim.y) {
+    int o = 0, n = 0, K = 0;
+    for (; e < L; ++e) {
+      o = offsets[e];
+      n = offsets[e + 1] - o;
+      K = seg_k(n);
+      if (y < base + K / 64) break;
+      base += K / 64;
+      q += K;
+    }
+    if (e >= L) return;  // uniform: every thread of the block walks the same blocks
+    const int k0 = (y - base) * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = t / 8 + 32 * j, c8 = (t % 8) * 8;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (k0 + r < n) v = *reinterpret_cast<const u32x4_t*>(X + size_t(o + k0 + r) * Cw + c0 + c8);
+      *reinterpret_cast<u32x4_t*>(&tile[r][c8]) = v;
+    }
+    __syncthreads();
+    bf16_t* d = XT + q * Cw;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = t / 8 + 32 * j, r8 = (t % 8) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        w[e2] = uint32_t(tile[r8 + 2 * e2][c]) | (uint32_t(tile[r8 + 2 * e2 + 1][c]) << 16);
+      *reinterpret_cast<u32x4_t*>(d + size_t(c0 + c) * K + k0 + r8) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    __syncthreads();  // the tile is refilled next round
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -564,29 +670,118 @@ moe_status dispatch_bwd_t(const DispatchBwdArgs& a) {
   return MOE_OK;
 }
 
+// Scratch of the FFN backward: dg | du [P_max, 2I], then on the large-tile path the
+// tile plan and split-K pieces, wdT [L, I, H] and wguT [L, H, 2I].
+struct FfnBwdScratch {
+  void* dgu;
+  void* big;  // big_backward_scratch_bytes
+  void* wdT;
+  void* wguT;
+  // the weight gradients on the large tile: per-expert transposed blocks of
+  // dy_sorted [H], h [I], dg | du [2I] and x_sorted [H] rows (see seg_transpose_kernel)
+  void* dysT;
+  void* hT;
+  void* dguT;
+  void* xT;
+};
+
+FfnBwdScratch carve_ffn_bwd(const moe_layer_desc* d, int64_t max_pairs, void* base, size_t* bytes) {
+  const size_t dt = dtype_bytes(d->dtype);
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t n) -> void* {
+    void* r = p ? p + o : nullptr;
+    o += align_up(n, 256);
+    return r;
+  };
+  FfnBwdScratch w{};
+  w.dgu = take(size_t(max_pairs) * 2 * d->intermediate * dt);
+  if (big_backward_supported(d, max_pairs)) {
+    const size_t wbytes = size_t(d->local_count) * d->hidden * d->intermediate * dt;
+    w.big = take(big_backward_scratch_bytes(d));
+    w.wdT = take(wbytes);
+    w.wguT = take(2 * wbytes);
+    if (big_wgrad_supported(d, max_pairs)) {
+      const size_t q = size_t(max_pairs) + size_t(64) * d->local_count;
+      w.dysT = take(q * d->hidden * dt);
+      w.hT = take(q * d->intermediate * dt);
+      w.dguT = take(q * 2 * d->intermediate * dt);
+      w.xT = take(q * d->hidden * dt);
+    }
+  }
+  if (bytes) *bytes = o;
+  return w;
+}
+
 template <typename T>
 moe_status ffn_bwd_t(const FfnBwdArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  const FfnBwdScratch w = carve_ffn_bwd(d, a.max_pairs, a.scratch, nullptr);
+  T* dgu = static_cast<T*>(w.dgu);
+  bool big = false;
+  if constexpr (sizeof(T) == 2) {
+    if (w.big != nullptr) {
+      // the dgrad products on the large-tile kernel, with the weights transposed to [N, K] rows
+      big = true;
+      bf16_t* wdT = static_cast<bf16_t*>(w.wdT);
+      bf16_t* wguT = static_cast<bf16_t*>(w.wguT);
+      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(I / 64, H / 64, L), dim3(256), 0, a.s,
+                 static_cast<const bf16_t*>(a.w_down), H, I, wdT, H, 0);
+      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(H / 64, I / 64, L), dim3(256), 0, a.s,
+                 static_cast<const bf16_t*>(a.w_gate), I, H, wguT, 2 * I, 0);
+      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(H / 64, I / 64, L), dim3(256), 0, a.s,
+                 static_cast<const bf16_t*>(a.w_up), I, H, wguT, 2 * I, I);
+      const moe_status st = launch_big_backward_dgrad(
+          d, static_cast<const bf16_t*>(a.dy_sorted), a.offsets, wdT, static_cast<const bf16_t*>(a.gate),
+          static_cast<const bf16_t*>(a.up), dgu, wguT, static_cast<bf16_t*>(a.dx_sorted), a.max_pairs, w.big, a.s);
+      if (st != MOE_OK) return st;
+    }
+  }
   const unsigned mslots = unsigned((a.max_pairs + BM - 1) / BM + L);
-  T* dg = static_cast<T*>(a.dg);
-  T* du = static_cast<T*>(a.du);
-  {  // dh = dy_sorted Wd_e, then dg, du
+  if (!big) {  // dh = dy_sorted Wd_e, then dg, du
     DgradArgs<T> p{};
     p.A[0] = static_cast<const T*>(a.dy_sorted);
     p.K[0] = H;
+    p.lda = H;
     p.B[0] = static_cast<const T*>(a.w_down);
     p.b_estride = int64_t(H) * I;
     p.N = I;
     p.G = static_cast<const T*>(a.gate);
     p.U = static_cast<const T*>(a.up);
-    p.DG = dg;
-    p.DU = du;
+    p.DGU = dgu;
     p.offsets = a.offsets;
     p.L = L;
     MOE_LAUNCH("ffn_down_dgrad", (dgrad_kernel<T, 1, 1>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0, a.s, p);
   }
-  {  // dWd_e = dy_sorted_e^T h_e  [H, I]
+  bool big_w = false;
+  if constexpr (sizeof(T) == 2) {
+    if (w.dysT != nullptr) {
+      big_w = true;
+      // the row blocks actually present are not known on the host (no sync): a grid of
+      // about 4096 blocks strides over them
+      auto seg_t = [&](const void* X, int Cw, void* XT) -> moe_status {
+        const int64_t slots = std::min<int64_t>((a.max_pairs + 63) / 64 + L, std::max(1, 4096 / (Cw / 64)));
+        MOE_LAUNCH("ffn_bwd_seg_transpose", seg_transpose_kernel, dim3(unsigned(Cw / 64), unsigned(slots)), dim3(256), 0, a.s,
+                   static_cast<const bf16_t*>(X), Cw, a.offsets, L, static_cast<bf16_t*>(XT));
+        return MOE_OK;
+      };
+      moe_status st = seg_t(a.dy_sorted, H, w.dysT);
+      if (st == MOE_OK) st = seg_t(a.h, I, w.hT);
+      if (st == MOE_OK) st = seg_t(dgu, 2 * I, w.dguT);
+      if (st == MOE_OK) st = seg_t(a.x_sorted, H, w.xT);
+      if (st == MOE_OK)
+        st = launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, static_cast<const bf16_t*>(w.dysT), H,
+                                       static_cast<const bf16_t*>(w.hT), static_cast<bf16_t*>(a.dw_down), nullptr, H,
+                                       I, 1, a.max_pairs, a.s);
+      if (st == MOE_OK)
+        st = launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, static_cast<const bf16_t*>(w.dguT), 2 * I,
+                                       static_cast<const bf16_t*>(w.xT), static_cast<bf16_t*>(a.dw_gate),
+                                       static_cast<bf16_t*>(a.dw_up), I, H, 2, a.max_pairs, a.s);
+      if (st != MOE_OK) return st;
+    }
+  }
+  if (!big_w) {  // dWd_e = dy_sorted_e^T h_e  [H, I]
     WgradArgs<T> p{};
     p.A[0] = static_cast<const T*>(a.dy_sorted);
     p.lda = H;
@@ -599,11 +794,12 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
     const unsigned tiles = unsigned(((H + BM - 1) / BM) * ((I + BN - 1) / BN));
     MOE_LAUNCH("ffn_down_wgrad", wgrad_kernel<T>, dim3(tiles, L, 1), dim3(kThreads), 0, a.s, p);
   }
-  {  // dx_sorted = dg Wg_e + du Wu_e
+  if (!big) {  // dx_sorted = dg Wg_e + du Wu_e
     DgradArgs<T> p{};
-    p.A[0] = dg;
-    p.A[1] = du;
+    p.A[0] = dgu;
+    p.A[1] = dgu + I;
     p.K[0] = p.K[1] = I;
+    p.lda = 2 * I;
     p.B[0] = static_cast<const T*>(a.w_gate);
     p.B[1] = static_cast<const T*>(a.w_up);
     p.b_estride = int64_t(I) * H;
@@ -614,11 +810,11 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
     MOE_LAUNCH("ffn_gate_up_dgrad", (dgrad_kernel<T, 0, 2>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0,
                a.s, p);
   }
-  {  // dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e  [I, H]
+  if (!big_w) {  // dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e  [I, H]
     WgradArgs<T> p{};
-    p.A[0] = dg;
-    p.A[1] = du;
-    p.lda = I;
+    p.A[0] = dgu;
+    p.A[1] = dgu + I;
+    p.lda = 2 * I;
     p.m_load = I;
     p.B = static_cast<const T*>(a.x_sorted);
     p.C[0] = static_cast<T*>(a.dw_gate);
@@ -630,6 +826,15 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
     MOE_LAUNCH("ffn_gate_up_wgrad", wgrad_kernel<T>, dim3(tiles, L, 2), dim3(kThreads), 0, a.s, p);
   }
   return MOE_OK;
+}
+
+// The router's dW = dlogits^T x reduces over every token: K slices of at least
+// 256 tokens, enough to give ~1024 blocks, summed in slice order.
+int route_bwd_pieces(const moe_layer_desc* d) {
+  const int64_t tiles = int64_t((d->num_experts + BM - 1) / BM) * ((d->hidden + BN - 1) / BN);
+  int64_t z = (1024 + tiles - 1) / tiles;
+  z = std::min<int64_t>(z, (d->num_tokens + 255) / 256);
+  return int(std::max<int64_t>(1, std::min<int64_t>(z, 64)));
 }
 
 template <typename T>
@@ -652,8 +857,15 @@ moe_status route_bwd_t(const RouteBwdArgs& a) {
   p.N = H;
   p.offsets = nullptr;
   p.k_total = T_;
+  const int pieces = route_bwd_pieces(d);
+  p.partial = pieces > 1 ? w.pieces : nullptr;
   const unsigned tiles = unsigned(((E + BM - 1) / BM) * ((H + BN - 1) / BN));
-  MOE_LAUNCH("route_bwd_wgrad", wgrad_kernel<T>, dim3(tiles, 1, 1), dim3(kThreads), 0, a.s, p);
+  MOE_LAUNCH("route_bwd_wgrad", wgrad_kernel<T>, dim3(tiles, 1, unsigned(pieces)), dim3(kThreads), 0, a.s, p);
+  if (pieces > 1) {
+    const int64_t n = int64_t(E) * H;
+    MOE_LAUNCH("route_bwd_wgrad_sum", splitk_sum_kernel<T>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, a.s, w.pieces,
+               pieces, n, static_cast<T*>(a.dw_router));
+  }
   if (a.db_router != nullptr) {
     MOE_LAUNCH("route_bwd_bias", colsum_part_kernel, dim3(kColChunks), dim3(256), 0, a.s, w.dlogits32, T_, Ep,
                w.part);
@@ -667,7 +879,9 @@ moe_status route_bwd_t(const RouteBwdArgs& a) {
 size_t route_bwd_scratch_bytes(const moe_layer_desc* d) {
   const int Ep = padded_experts(d->num_experts);
   const size_t n = size_t(d->num_tokens) * Ep;
-  return align_up(n * dtype_bytes(d->dtype), 256) + align_up(n * 4, 256) + align_up(size_t(kColChunks) * Ep * 4, 256);
+  const int pieces = route_bwd_pieces(d);
+  return align_up(n * dtype_bytes(d->dtype), 256) + align_up(n * 4, 256) + align_up(size_t(kColChunks) * Ep * 4, 256) +
+         (pieces > 1 ? align_up(size_t(pieces) * d->num_experts * d->hidden * 4, 256) : 0);
 }
 
 RouteBwdScratch carve_route_bwd_scratch(const moe_layer_desc* d, void* ws) {
@@ -680,7 +894,15 @@ RouteBwdScratch carve_route_bwd_scratch(const moe_layer_desc* d, void* ws) {
   w.dlogits32 = reinterpret_cast<float*>(p);
   p += align_up(n * 4, 256);
   w.part = reinterpret_cast<float*>(p);
+  p += align_up(size_t(kColChunks) * Ep * 4, 256);
+  w.pieces = route_bwd_pieces(d) > 1 ? reinterpret_cast<float*>(p) : nullptr;
   return w;
+}
+
+size_t ffn_bwd_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs) {
+  size_t n = 0;
+  carve_ffn_bwd(d, max_pairs, nullptr, &n);
+  return n;
 }
 
 moe_status launch_zero(const char* name, void* p, size_t bytes, hipStream_t s) {

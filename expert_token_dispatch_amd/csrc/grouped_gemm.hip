@@ -486,10 +486,18 @@ constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true, 4>::kStage;  // 160
 // and parks it in LDS, rows padded by 16 bytes; then every thread copies
 // 16-byte row chunks out, so each store instruction writes whole row pieces.
 // The caller has made sure no wave still reads the loop's LDS stages.
-template <int NMAT, bool WIDE, int NW, bool SAVE>
+// EP: kPlain; kSave (gate/up of the training forward: the gate and up
+// pre-activations are written too, to Gs and Us); kSwigluBwd (the down
+// product's dgrad dh = dy_sorted Wd: reads the saved gate and up values Gs, Us
+// and writes dg and du side by side into C, rows of 2N).
+constexpr int kPlain = 0, kSave = 1, kSwigluBwd = 2;
+// the weight-gradient products (see wgrad_k): gemm_kernel decodes its own jobs
+constexpr int kWgrad = 3;
+
+template <int NMAT, bool WIDE, int NW, int EP>
 __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds, bf16_t* __restrict__ C, int row0,
                                          int rows, int n0, int N, bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
-  if constexpr (!SAVE) {
+  if constexpr (EP == kPlain || EP == kWgrad) {
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
@@ -527,7 +535,7 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds,
     // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
     if (r < rows && n0 + c * 8 < N) *reinterpret_cast<u32x4_t*>(C + size_t(row0 + r) * N + n0 + c * 8) = val;
   }
-  } else {
+  } else if constexpr (EP == kSave) {
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int TC = NMAT == 2 ? S::kB / 2 : S::kB;  // output columns of the tile
@@ -589,6 +597,65 @@ __device__ __forceinline__ void epilogue(f32x16_t (&acc)[4][16 / NW], char* lds,
       copy_out(sel == 1 ? Gs : Us);
     }
   }
+  } else {
+  // SwiGLU backward (NMAT == 1): dh is parked as bf16 like a plain output; the
+  // copy-out reads the saved gate and up values of the same 8 columns and
+  // writes dg = dh up silu'(gate) and du = dh silu(gate), silu'(g) = s (1 + g (1 - s)).
+  static_assert(NMAT == 1, "the SwiGLU backward epilogue follows the down product's dgrad");
+  using S = Shape<WIDE, NW>;
+  constexpr int NB = S::NB, kThreads = S::kThreads;
+  constexpr int TC = S::kB;
+  constexpr int RS = TC * 2 + 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = S::wm(wave), wn = S::wn(wave), fr = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rt = wm * 128 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        const int cl = wn * NB * 32 + j * 32 + 8 * q + 4 * g;
+        *reinterpret_cast<uint2*>(lds + rt * RS + cl * 2) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  block_barrier();
+  constexpr int CPR = TC / 8;
+#pragma unroll
+  for (int u = 0; u < S::kA * CPR / kThreads; ++u) {
+    const int id = tid + kThreads * u;
+    const int r = id / CPR, c = id % CPR;
+    if (r < rows && n0 + c * 8 < N) {
+      const u32x4_t dh = *reinterpret_cast<const u32x4_t*>(lds + r * RS + c * 16);
+      const size_t at = size_t(row0 + r) * N + n0 + c * 8;
+      const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(Gs + at);
+      const u32x4_t uv = *reinterpret_cast<const u32x4_t*>(Us + at);
+      u32x4_t dg, du;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float o_g[2], o_u[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float fd = __uint_as_float(h ? dh[w] & 0xFFFF0000u : dh[w] << 16);
+          const float fg = __uint_as_float(h ? gv[w] & 0xFFFF0000u : gv[w] << 16);
+          const float fu = __uint_as_float(h ? uv[w] & 0xFFFF0000u : uv[w] << 16);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-fg));
+          o_g[h] = fd * fu * (sg * (1.0f + fg * (1.0f - sg)));
+          o_u[h] = fd * (fg * sg);
+        }
+        dg[w] = pack_bf16x2(o_g[0], o_g[1]);
+        du[w] = pack_bf16x2(o_u[0], o_u[1]);
+      }
+      bf16_t* o = C + size_t(row0 + r) * 2 * N + n0 + c * 8;
+      *reinterpret_cast<u32x4_t*>(o) = dg;
+      *reinterpret_cast<u32x4_t*>(o + N) = du;
+    }
+  }
   }
 }
 
@@ -606,7 +673,7 @@ __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslo
 }
 
 // One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
-template <int NMAT, bool WIDE, int NW, bool SAVE>
+template <int NMAT, bool WIDE, int NW, int EP>
 __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
                                           const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
                                           const Job& jb, float* __restrict__ parts, char* lds,
@@ -822,16 +889,53 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   }
   MOE_LGKMCNT0();
   block_barrier();  // every wave is done reading the last stage
-  epilogue<NMAT, WIDE, NW, SAVE>(acc, lds, C, row0, rows, n0, N, Gs, Us);
+  epilogue<NMAT, WIDE, NW, EP>(acc, lds, C, row0, rows, n0, N, Gs, Us);
 }
 
-template <int NMAT, int NW, bool SAVE>
+// ---- weight gradients on the large tile --------------------------------------
+// Expert e's dW = A_e B_e^T reduces over its rows.  The caller has copied the
+// operands transposed into per-expert blocks [rows, K_e] with K_e the segment
+// length rounded up to 64 (at least 64; the padding is zero), at element offset
+// rows * Q_e (Q_e = sum of K_e' over e' < e), so each expert's product has
+// the forward's operand layout with its own K.  In gemm_kernel's kWgrad mode:
+// blockIdx x = tile (m major), y = expert, z = which of up to two (A, C) pairs
+// (A rows [z M, (z+1) M)); A = the transposed blocks (a_rows of them per
+// expert), B0 = B's blocks, C and Gs = the two outputs, K = M.
+__device__ __forceinline__ int wgrad_k(int n) { return n <= 64 ? 64 : (n + 63) / 64 * 64; }
+
+template <int NMAT, int NW, int EP>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                        bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
                                                         const int32_t* __restrict__ tpre, int cpx, int smax,
                                                         float* __restrict__ parts, bf16_t* __restrict__ Gs,
                                                         bf16_t* __restrict__ Us) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  if constexpr (EP == kWgrad) {
+    const int e = blockIdx.y, z = blockIdx.z, M = K;
+    int64_t q = 0;
+    for (int i = 0; i < e; ++i) q += wgrad_k(offsets[i + 1] - offsets[i]);
+    const int Ke = wgrad_k(offsets[e + 1] - offsets[e]);
+    const int tn = (N + BNE - 1) / BNE;
+    Job jb;
+    jb.expert = e;
+    jb.row0 = (blockIdx.x / tn) * BM;
+    jb.rows = min(BM, M - jb.row0);
+    jb.n0 = blockIdx.x % tn;
+    jb.wide = false;
+    jb.kb = 0;
+    jb.nks = Ke / BK;
+    jb.part = 0;
+    jb.nparts = 1;
+    jb.pslot = 0;
+    const bf16_t* Ae = A + q * a_rows + size_t(z) * M * Ke;
+    const bf16_t* Be = B0 + q * N;
+    bf16_t* Ce = (z ? Gs : C) + size_t(e) * M * N;
+    // (EP, not kPlain, as the template argument: hipcc's host pass rejects the literal
+    // here; the epilogue treats kWgrad as kPlain)
+    tile_body<NMAT, false, NW, EP>(Ae, M, Be, Be, Ce, N, Ke, jb, parts, lds, Us, Us);
+    return;
+  }
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
   const int NT = (N + ON - 1) / ON;
   const int nk = K / BK;
@@ -839,7 +943,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
   const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
   const XcdPlan xp = plan_xcd(tpre[L], nk, cpx, smax, xcd);
   if (loc >= xp.units) return;
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
   // the tile prefix into LDS for the search (the loop's stages overwrite it later)
   int32_t* spre = reinterpret_cast<int32_t*>(lds);
   for (int i = threadIdx.x; i <= L; i += NW * 64) spre[i] = tpre[i];
@@ -851,10 +954,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
   const bf16_t* Bg = B0 + boff;
   const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
   if (jb.wide)
-    tile_body<NMAT, true, NW, SAVE>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, true, NW, EP>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
   else
-    tile_body<NMAT, false, NW, SAVE>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, false, NW, EP>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
 }
+
 
 // Adds the pieces of each split tile in piece order and writes the tile.
 // kFixSub blocks share a tile; an item is one float4 of the accumulator
@@ -863,7 +967,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
 // gate/up: the gate float4 and its up partner j + NB/2).
 constexpr int kFixSub = 8;
 
-template <int NMAT, int NW, bool SAVE>
+template <int NMAT, int NW, int EP>
 __global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restrict__ offsets, bf16_t* __restrict__ C,
                                                          int L, int N, int K, const int32_t* __restrict__ tpre, int cpx,
                                                          int smax, const float* __restrict__ parts,
@@ -914,7 +1018,7 @@ __global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restric
       pk.x = pack_bf16x2(o[0], o[1]);
       pk.y = pack_bf16x2(o[2], o[3]);
       *reinterpret_cast<uint2*>(C + size_t(jb.row0 + rt) * N + n0 + cl) = pk;
-      if constexpr (NMAT == 2 && SAVE) {  // training: the pre-activations too
+      if constexpr (NMAT == 2 && EP == kSave) {  // training: the pre-activations too
         const size_t at = size_t(jb.row0 + rt) * N + n0 + cl;
         *reinterpret_cast<uint2*>(Gs + at) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
         *reinterpret_cast<uint2*>(Us + at) = make_uint2(pack_bf16x2(su[0], su[1]), pack_bf16x2(su[2], su[3]));
@@ -945,7 +1049,7 @@ bool splits(int K) { return K / BK >= kSplitMinSteps; }
 // skewed layer -1.5%); four for longer ones (mixtral-like layer: eight are 1% slower).
 constexpr int kEightWaveSteps = 64;
 
-template <int NMAT, int NW, bool SAVE>
+template <int NMAT, int NW, int EP>
 moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                       bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
                       hipStream_t s, bf16_t* Gs, bf16_t* Us);
@@ -953,18 +1057,24 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
 template <int NMAT, int NW>
 moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                     hipStream_t s, bf16_t* Gs, bf16_t* Us) {
-  if (NMAT == 2 && Gs != nullptr) return launch_nws<NMAT, NW, true>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
-  return launch_nws<NMAT, NW, false>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+                     hipStream_t s, bf16_t* Gs, bf16_t* Us, int ep) {
+  if constexpr (NMAT == 2) {
+    if (ep == kSave) return launch_nws<NMAT, NW, kSave>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+  } else {
+    if (ep == kSwigluBwd)
+      return launch_nws<NMAT, NW, kSwigluBwd>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, nullptr, s, Gs, Us);
+  }
+  return launch_nws<NMAT, NW, kPlain>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
 }
 
-// SAVE: the training forward's variant, which also writes the gate and up pre-activations
-template <int NMAT, int NW, bool SAVE>
+// EP: the epilogue (kSave: the training forward's gate/up, which also writes the
+// pre-activations; kSwigluBwd: the backward's down dgrad, never split along K)
+template <int NMAT, int NW, int EP>
 moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                       bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
                       hipStream_t s, bf16_t* Gs, bf16_t* Us) {
   constexpr int kThreads = NW * 64;
-  auto kern = gemm_kernel<NMAT, NW, SAVE>;
+  auto kern = gemm_kernel<NMAT, NW, EP>;
   constexpr size_t lds = lds_bytes<NMAT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
@@ -981,19 +1091,35 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
              int(max_pairs), tpre, cpx, smax, parts, Gs, Us);
   if (smax > 1) {
     const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
-    MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW, SAVE>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
+    MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW, EP>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
                offsets, C, L, N, K, tpre, cpx, smax, static_cast<const float*>(parts), Gs, Us);
   }
+  return MOE_OK;
+}
+
+template <int NW>
+moe_status launch_wgrad_nw(const char* name, const moe_layer_desc* d, const int32_t* offsets, const bf16_t* At,
+                           int a_rows_total, const bf16_t* Bt, bf16_t* C0, bf16_t* C1, int M, int N, int Z,
+                           hipStream_t s) {
+  auto kern = gemm_kernel<1, NW, kWgrad>;
+  constexpr size_t lds = lds_bytes<1>();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     int(lds));
+  if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
+  const unsigned tiles = unsigned(((M + BM - 1) / BM) * ((N + BNE - 1) / BNE));
+  MOE_LAUNCH(name, kern, dim3(tiles, unsigned(d->local_count), unsigned(Z)), dim3(NW * 64), lds, s, At, offsets, Bt,
+             Bt, C0, d->local_count, N, M, a_rows_total, static_cast<const int32_t*>(nullptr), 0, 1,
+             static_cast<float*>(nullptr), C1, static_cast<bf16_t*>(nullptr));
   return MOE_OK;
 }
 
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
                   bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                  hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
+                  hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr, int ep = kPlain) {
   if (K / BK < kEightWaveSteps)
-    return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
-  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+    return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us, ep);
+  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us, ep);
 }
 
 }  // namespace big
@@ -1198,6 +1324,55 @@ size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs) {
   return plan + (split ? size_t(big::kXcds) * big::kMaxParts * big::kPartBytes : 0);
 }
 
+// ---- the backward's dgrad products on the large-tile kernel ---------------------
+// With the expert weights transposed to [N, K] rows (wdT [L, I, H]; wguT [L, H, 2I],
+// the gate's transpose then the up's), both dgrad products have the forward's
+// operand layout: dh = dy_sorted wdT_e^T with the SwiGLU backward in the epilogue
+// (writing dg | du as [P, 2I]), then dx_sorted = [dg | du] wguT_e^T, one product
+// over K = 2I.
+bool big_backward_supported(const moe_layer_desc* d, int64_t max_pairs) {
+  return use_big(d, max_pairs) && big::supported(2 * d->intermediate) &&
+         big::addressable(d->hidden, 2 * int64_t(d->intermediate));
+}
+
+size_t big_backward_scratch_bytes(const moe_layer_desc* d) {
+  const size_t plan = align_up(size_t(2) * (d->local_count + 1) * sizeof(int32_t), 256);
+  return plan + (big::splits(2 * d->intermediate) ? size_t(big::kXcds) * big::kMaxParts * big::kPartBytes : 0);
+}
+
+moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const bf16_t* dy_sorted, const int32_t* offsets,
+                                     const bf16_t* wdT, const bf16_t* gate, const bf16_t* up, bf16_t* dgu,
+                                     const bf16_t* wguT, bf16_t* dx_sorted, int64_t max_pairs, void* scratch,
+                                     hipStream_t s) {
+  const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  int32_t* pre = static_cast<int32_t*>(scratch);
+  float* parts = big::splits(2 * I) ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
+                                                               align_up(size_t(2) * (L + 1) * sizeof(int32_t), 256))
+                                    : nullptr;
+  MOE_LAUNCH("ffn_bwd_plan", big::plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L, (I + big::BNE - 1) / big::BNE,
+             (H + big::BNE - 1) / big::BNE, pre);
+  moe_status st = big::launch<1>("ffn_down_dgrad", dy_sorted, offsets, wdT, wdT, dgu, L, I, H, max_pairs, pre, nullptr,
+                                 s, const_cast<bf16_t*>(gate), const_cast<bf16_t*>(up), big::kSwigluBwd);
+  if (st != MOE_OK) return st;
+  return big::launch<1>("ffn_gate_up_dgrad", dgu, offsets, wguT, wguT, dx_sorted, L, H, 2 * I, max_pairs, pre + L + 1,
+                        parts, s);
+}
+
+bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs) {
+  const int64_t kmax = (max_pairs + 63) / 64 * 64 + 64;
+  return big_backward_supported(d, max_pairs) && big::addressable(std::max(d->hidden, 2 * d->intermediate), kmax);
+}
+
+moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
+                                     const bf16_t* At, int a_rows_total, const bf16_t* Bt, bf16_t* C0, bf16_t* C1,
+                                     int M, int N, int Z, int64_t max_pairs, hipStream_t s) {
+  // eight waves when the average segment is under 64 k steps, as for the forward
+  const int64_t avg = max_pairs / std::max(1, d->local_count);
+  if (avg / big::BK < big::kEightWaveSteps)
+    return big::launch_wgrad_nw<8>(name, d, offsets, At, a_rows_total, Bt, C0, C1, M, N, Z, s);
+  return big::launch_wgrad_nw<4>(name, d, offsets, At, a_rows_total, Bt, C0, C1, M, N, Z, s);
+}
+
 moe_status launch_grouped_ffn(const FfnArgs& a) {
   if (a.max_pairs <= 0) return MOE_OK;
   const moe_layer_desc* d = a.d;
@@ -1215,7 +1390,8 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
              (H + big::BNE - 1) / big::BNE, pre);
   moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
                                  static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, pre, parts, a.s,
-                                 static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
+                                 static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out),
+                                 a.g_out != nullptr ? big::kSave : big::kPlain);
   if (st != MOE_OK) return st;
   return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
                         static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.max_pairs,

@@ -141,17 +141,32 @@ struct FfnBwdArgs {
   void* dw_gate;         // [L, I, H]
   void* dw_up;
   void* dw_down;         // [L, H, I]
-  void* dg;              // scratch [P_max, I] each
-  void* du;
+  void* scratch;         // ffn_bwd_scratch_bytes
   int64_t max_pairs;
   hipStream_t s;
 };
+// dg | du [P_max, 2I]; on the large-tile path also the transposed expert
+// weights, the tile plan and the split-K pieces.
+size_t ffn_bwd_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs);
 moe_status launch_grouped_ffn_backward(const FfnBwdArgs& a);
+// the large-tile kernel's part of it (grouped_gemm.hip)
+bool big_backward_supported(const moe_layer_desc* d, int64_t max_pairs);
+size_t big_backward_scratch_bytes(const moe_layer_desc* d);
+moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const uint16_t* dy_sorted, const int32_t* offsets,
+                                     const uint16_t* wdT, const uint16_t* gate, const uint16_t* up, uint16_t* dgu,
+                                     const uint16_t* wguT, uint16_t* dx_sorted, int64_t max_pairs, void* scratch,
+                                     hipStream_t s);
+// dW on the large tile from per-expert transposed blocks (see grouped_gemm.hip)
+bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs);
+moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
+                                     const uint16_t* At, int a_rows_total, const uint16_t* Bt, uint16_t* C0,
+                                     uint16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s);
 
 struct RouteBwdScratch {
   void* dlogits;     // [T, Ep] in the layer's type (Ep = E rounded up to 8)
   float* dlogits32;  // [T, Ep] float32 (bias gradient)
   float* part;       // column sums per token chunk
+  float* pieces;     // split-K pieces of dW (NULL when one piece)
 };
 size_t route_bwd_scratch_bytes(const moe_layer_desc* d);
 RouteBwdScratch carve_route_bwd_scratch(const moe_layer_desc* d, void* ws);
