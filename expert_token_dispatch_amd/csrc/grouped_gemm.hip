@@ -1150,10 +1150,12 @@ bool supported(int K) { return K % 32 == 0; }
 template <int NMAT>
 constexpr int cols_per_block() { return NMAT == 2 ? 64 : 128; }
 
-template <int NMAT>
+// SAVE (gate/up of the training forward): the gate and up pre-activations go to Gs, Us too.
+template <int NMAT, bool SAVE>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                         const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ C, int N, int K) {
+                                                        bf16_t* __restrict__ C, int N, int K, bf16_t* __restrict__ Gs,
+                                                        bf16_t* __restrict__ Us) {
   constexpr int kWaveCols = NMAT == 2 ? 16 : 32;
   const int expert = blockIdx.y;
   const int seg0 = offsets[expert];
@@ -1242,7 +1244,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
           bf16_t* crow = C + size_t(seg0 + r) * N;
           if (NMAT == 2) {
             const int col = col0 + (lane & 15);
-            if (col < N) crow[col] = f32_to_bf16(silu(acc[0][rb][i]) * acc[1][rb][i]);
+            if (col < N) {
+              crow[col] = f32_to_bf16(silu(acc[0][rb][i]) * acc[1][rb][i]);
+              if constexpr (SAVE) {
+                Gs[size_t(seg0 + r) * N + col] = f32_to_bf16(acc[0][rb][i]);
+                Us[size_t(seg0 + r) * N + col] = f32_to_bf16(acc[1][rb][i]);
+              }
+            }
           } else {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -1258,9 +1266,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
 
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, hipStream_t s) {
+                  bf16_t* C, int L, int N, int K, hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
   const dim3 grid(unsigned((N + cols_per_block<NMAT>() - 1) / cols_per_block<NMAT>()), unsigned(L));
-  MOE_LAUNCH(name, gemm_kernel<NMAT>, grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K);
+  if (NMAT == 2 && Gs != nullptr) {
+    MOE_LAUNCH(name, (gemm_kernel<NMAT, true>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us);
+  } else {
+    MOE_LAUNCH(name, (gemm_kernel<NMAT, false>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us);
+  }
   return MOE_OK;
 }
 
@@ -1302,12 +1314,11 @@ moe_status launch_small(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
   // decode-sized batches: a few rows per expert, bound by streaming the weights
-  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I) &&
-      a.g_out == nullptr) {
+  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I)) {
     bf16_t* h = static_cast<bf16_t*>(a.h);
     moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
                                       static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
-                                      H, a.s);
+                                      H, a.s, static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
     if (st != MOE_OK) return st;
     return skinny::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
                              static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.s);

@@ -317,7 +317,7 @@ typedef struct moe_saved {
 
 /* moe_grouped_ffn that also keeps the gate and up pre-activations (and h in
  * the caller's buffer instead of the workspace).  y_sorted and h are the
- * values moe_grouped_ffn produces (the skinny decode kernel is not used).
+ * values moe_grouped_ffn produces (the same kernels, with the extra stores).
  *   h, gate, up  device [P_max, I] dtype out
  *   ws           device workspace of MOE_STAGE_FFN bytes */
 moe_status moe_grouped_ffn_train(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,

@@ -55,6 +55,7 @@ def run_gpu(s, inp):
     dy_h = synth.make_upstream_grad(s)
     dy = to_dev(dy_h, s)
     logits = layer.route(x, want_logits=True)["logits"]
+    y_inf = layer.forward(x).clone()
     y, saved = layer.forward_train(x)
     st = layer.staged_backward(x, saved, dy)
     fu = layer.backward(x, saved, dy)
@@ -62,6 +63,7 @@ def run_gpu(s, inp):
     gpu = {k: np_of(v) for k, v in saved._tensors.items()}
     gpu.update({k: (None if v is None else np_of(v)) for k, v in st.items()})
     gpu["y"] = np_of(y)
+    gpu["y_inference"] = np_of(y_inf)
     gpu["logits"] = np_of(logits)
     fused = {k: (None if v is None else np_of(v)) for k, v in fu.items()}
     return layer, x, dy_h, gpu, fused
@@ -104,6 +106,8 @@ def case(request):
 
 def test_training_forward_keeps_the_forward(case):
     s, inp, gpu, fused, ref = case
+    # the same kernels as the inference forward, with the extra stores
+    np.testing.assert_array_equal(gpu["y"], gpu["y_inference"])
     f = ref["forward"]
     np.testing.assert_array_equal(gpu["topk_ids"], f["topk_ids"])
     np.testing.assert_array_equal(gpu["offsets"], f["offsets"])
