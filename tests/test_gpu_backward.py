@@ -50,13 +50,13 @@ def to_dev(a, s):
     return to_device(a, s.dtype)
 
 
-def run_gpu(s, inp):
+def run_gpu(s, inp, opts=None):
     layer, x = layer_of(inp)
     dy_h = synth.make_upstream_grad(s)
     dy = to_dev(dy_h, s)
     logits = layer.route(x, want_logits=True)["logits"]
-    y_inf = layer.forward(x).clone()
-    y, saved = layer.forward_train(x)
+    y_inf = layer.forward(x, opts=opts).clone()
+    y, saved = layer.forward_train(x, opts=opts)
     st = layer.staged_backward(x, saved, dy)
     fu = layer.backward(x, saved, dy)
     torch.cuda.synchronize()
@@ -200,6 +200,29 @@ def test_backward_edges():
         for k in ("dw_gate", "dw_up", "dw_down", "dw_router"):
             mat_ok(k, gpu[k], ref[k], s.dtype)
         rows_ok("dx", gpu["dx"], ref["dx"], s.dtype)
+
+
+def test_backward_with_route_options():
+    # selection-only bias and at most 2 of 8 expert groups per token (glossary "Load balancing
+    # and capacity"): the choice changes, the gradients follow the chosen slots; none reaches the bias
+    import expert_token_dispatch_amd as etd
+    s = SMALL["gptoss_ep8_share"]
+    say(f"[bwd] route options {s}")
+    inp = synth.make_layer(s)
+    bias = (np.random.default_rng(3).standard_normal(s.E) * 0.5).astype(np.float32)
+    opts = etd.make_route_opts(torch.from_numpy(bias).cuda(), 8, 2)
+    layer, x, dy_h, gpu, fused = run_gpu(s, inp, opts)
+    ref = B.layer_backward(inp, oracle.decode(dy_h, s.dtype), logits=gpu["logits"].astype(np.float64),
+                           route_opts={"selection_bias": bias, "num_groups": 8, "max_groups": 2})
+    np.testing.assert_array_equal(gpu["y"], gpu["y_inference"])
+    np.testing.assert_array_equal(gpu["topk_ids"], ref["forward"]["topk_ids"])
+    np.testing.assert_array_equal(gpu["pair_row"], ref["forward"]["pair_row"])
+    for k in ("dw_gate", "dw_up", "dw_down", "dw_router"):
+        mat_ok(k, gpu[k], ref[k], s.dtype)
+    rows_ok("dx", gpu["dx"], ref["dx"], s.dtype)
+    for k, v in fused.items():
+        if v is not None:
+            np.testing.assert_array_equal(v, gpu[k], err_msg=k)
 
 
 def test_zero_tokens_zero_weight_gradients():
