@@ -127,13 +127,14 @@ def source_digest(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_for(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they still match the source."""
+def traffic_for(kernel: str, workload: str, training: bool = False):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they still match the source
+    (training-step runs are recorded under their own keys: their kernels are other instantiations)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
-        rec = json.load(open(p)).get(f"{workload}:{kernel}")
+        rec = json.load(open(p)).get(f"{workload}:{kernel}" + (":training" if training else ""))
     except (OSError, ValueError):
         return None
     if not rec:
@@ -351,7 +352,7 @@ def main():
         achieved = b / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    tb = traffic_for(dom, s.name)
+    tb = traffic_for(dom, s.name, args.backward)
     roof["traffic"] = tb
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = f if roof["bound"] == "mfma" else b
