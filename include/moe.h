@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* a size, range or pointer is not acceptable */
-  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request the library does not handle */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   MOE_ERR_HIP = -4          /* the HIP runtime reported an error          */
 } moe_status;
