@@ -341,6 +341,19 @@ def main():
         for hc in h:
             hip.destroy([e for e in hc if e is not None])
     kern[dom] = kernel_entry(dom, dom_ms * 1e3, len(where))
+
+    # per-step durations (median and minimum), from K more steps each between two events
+    # of its own, after the timed region
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in pev:
+        a_.record()
+        step()
+        b_.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a_.elapsed_time(b_) for a_, b_ in pev)
+    step_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    step_min = per_step[0]
+
     b, f = kernel_work(dom, s, P, touched_tokens, touched_experts, nblk, args.backward)
     us = kern[dom]["us"]
     gemm_bound_hbm = dom.startswith("ffn") and (f / (MFMA_PEAK_TFLOPS[s.dtype] * 1e12) < b / (HBM_PEAK_GBS * 1e9))
@@ -372,6 +385,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(step_median, 4),
+        "ms_per_step_min": round(step_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
