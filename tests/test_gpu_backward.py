@@ -192,7 +192,9 @@ def test_backward_edges():
     # an expert range at the end, empty experts, k = E, T not a tile multiple, f32 and bf16
     for s in (synth.spec("tiny_fp32", T=37, E=8, k=8, local_begin=0, L=8),
               synth.spec("gptoss_ep8_share", T=70, H=72, I=40, local_begin=112, L=16),
-              synth.spec("mixtral_like", T=3, H=136, I=200, E=8, k=2)):
+              synth.spec("mixtral_like", T=3, H=136, I=200, E=8, k=2),
+              synth.spec("mixtral_like", T=1, H=64, I=128, E=8, k=2),
+              synth.spec("mixtral_like", T=300, H=256, I=192, E=1, k=1, L=1)):
         say(f"[bwd] edge {s}")
         inp = synth.make_layer(s)
         layer, x, dy_h, gpu, fused = run_gpu(s, inp)
@@ -200,6 +202,8 @@ def test_backward_edges():
         for k in ("dw_gate", "dw_up", "dw_down", "dw_router"):
             mat_ok(k, gpu[k], ref[k], s.dtype)
         rows_ok("dx", gpu["dx"], ref["dx"], s.dtype)
+        if s.E == 1:  # one expert: its weight is exactly 1, the router gets exactly nothing
+            assert not np.any(gpu["dl"]) and not np.any(gpu["dw_router"])
 
 
 def test_backward_with_route_options():
