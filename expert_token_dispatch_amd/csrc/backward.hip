@@ -41,7 +41,6 @@ namespace {
 // combine backward + softmax backward: one wave per token
 // ---------------------------------------------------------------------------
 constexpr int kTokensPerBlock = 4;
-constexpr int kSlices = 4;  // 16-byte slices per lane per pass
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -49,53 +48,70 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy, const uint4* __restrict__ ys,
+// KB: slots whose rows are loaded together (k rounded up to 2, 4 or 8; larger k in batches of 8);
+// each lane takes kSlices 16-byte slices of a row per pass, so KB * kSlices loads are in flight
+template <int KB>
+constexpr int slices_for() { return KB <= 2 ? 8 : 4; }
+
+template <typename T, int KB>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restrict__ dy, const u32x4_t* __restrict__ ys,
                                                           const int32_t* __restrict__ pair_row,
                                                           const float* __restrict__ tw, int64_t ntok, int k,
-                                                          int vec_per_row, uint4* __restrict__ dys,
+                                                          int vec_per_row, u32x4_t* __restrict__ dys,
                                                           float* __restrict__ dl) {
   constexpr int EPV = 16 / int(sizeof(T));
+  constexpr int kSlices = slices_for<KB>();
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
   const int my_row = lane < k ? pair_row[t * k + lane] : -1;
   const float my_w = lane < k ? tw[t * k + lane] : 0.0f;
   float my_dot = 0.0f;  // lane j: <dy[t], y_sorted[row of slot j]>
-  const uint4* src = dy + size_t(t) * vec_per_row;
-  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kSlices) {
+  const u32x4_t* src = dy + size_t(t) * vec_per_row;
+  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
     float g[kSlices][EPV];
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
-      const int c = c0 + lane + 64 * u;
-      if (c < vec_per_row) {
-        unpack16(src[c], T(), g[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) g[u][e] = 0.0f;
-      }
+      const int c = c0 + 64 * u;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (c < vec_per_row) v = src[c];
+      unpack16(make_uint4(v[0], v[1], v[2], v[3]), T(), g[u]);
     }
-    for (int j = 0; j < k; ++j) {
-      const int r = __shfl(my_row, j, 64);
-      if (r < 0) continue;
-      const float wj = __shfl(my_w, j, 64);
-      float p = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      u32x4_t v[KB][kSlices];
 #pragma unroll
-      for (int u = 0; u < kSlices; ++u) {
-        const int c = c0 + lane + 64 * u;
-        if (c < vec_per_row) {
-          float f[EPV], o[EPV];
-          unpack16(ys[size_t(r) * vec_per_row + c], T(), f);
+      for (int jj = 0; jj < KB; ++jj) {
+        const int r = __shfl(my_row, j0 + jj, 64);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            p = fmaf(g[u][e], f[e], p);
-            o[e] = wj * g[u][e];
-          }
-          dys[size_t(r) * vec_per_row + c] = pack16(o, T());
+        for (int u = 0; u < kSlices; ++u) {
+          const int c = c0 + 64 * u;
+          if (j0 + jj < k && r >= 0 && c < vec_per_row) v[jj][u] = ys[size_t(r) * vec_per_row + c];
         }
       }
-      p = wave_sum(p);
-      if (lane == j) my_dot += p;
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        const int r = __shfl(my_row, j0 + jj, 64);
+        if (j0 + jj >= k || r < 0) continue;  // uniform over the wave
+        const float wj = __shfl(my_w, j0 + jj, 64);
+        float p = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kSlices; ++u) {
+          const int c = c0 + 64 * u;
+          if (c < vec_per_row) {
+            float f[EPV], o[EPV];
+            unpack16(make_uint4(v[jj][u][0], v[jj][u][1], v[jj][u][2], v[jj][u][3]), T(), f);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              p = fmaf(g[u][e], f[e], p);
+              o[e] = wj * g[u][e];
+            }
+            const uint4 pk = pack16(o, T());
+            dys[size_t(r) * vec_per_row + c] = u32x4_t{pk.x, pk.y, pk.z, pk.w};
+          }
+        }
+        p = wave_sum(p);
+        if (lane == j0 + jj) my_dot += p;
+      }
     }
   }
   const float inner = wave_sum(my_w * my_dot);
@@ -105,60 +121,69 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 // ---------------------------------------------------------------------------
 // dispatch backward: dx[t] = sum_j dx_sorted[q(t,j)] + sum_j dl[t,j] Wr[e(t,j)]
 // (float32, the expert part in slot order, then the router part in slot
-// order, rounded once)
+// order, rounded once); rows of KB slots are loaded together
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void dispatch_bwd_kernel(const uint4* __restrict__ dxs,
+template <typename T, int KB>
+__global__ __launch_bounds__(256) void dispatch_bwd_kernel(const u32x4_t* __restrict__ dxs,
                                                            const int32_t* __restrict__ pair_row,
                                                            const int32_t* __restrict__ ids,
-                                                           const float* __restrict__ dl, const uint4* __restrict__ wr,
+                                                           const float* __restrict__ dl, const u32x4_t* __restrict__ wr,
                                                            int64_t ntok, int k, int vec_per_row,
-                                                           uint4* __restrict__ dx) {
+                                                           u32x4_t* __restrict__ dx) {
   constexpr int EPV = 16 / int(sizeof(T));
+  constexpr int kSlices = slices_for<KB>();
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
   const int my_row = lane < k ? pair_row[t * k + lane] : -1;
   const int my_e = lane < k ? ids[t * k + lane] : 0;
   const float my_dl = lane < k ? dl[t * k + lane] : 0.0f;
-  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kSlices) {
+  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
     float acc[kSlices][EPV];
 #pragma unroll
     for (int u = 0; u < kSlices; ++u)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = __shfl(my_row, j, 64);
-      if (r < 0) continue;
+    // the expert part, then the router part (pass 0, 1)
 #pragma unroll
-      for (int u = 0; u < kSlices; ++u) {
-        const int c = c0 + lane + 64 * u;
-        if (c < vec_per_row) {
-          float f[EPV];
-          unpack16(dxs[size_t(r) * vec_per_row + c], T(), f);
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int j0 = 0; j0 < k; j0 += KB) {
+        u32x4_t v[KB][kSlices];
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[u][e] += f[e];
+        for (int jj = 0; jj < KB; ++jj) {
+          const int r = pass == 0 ? __shfl(my_row, j0 + jj, 64) : __shfl(my_e, j0 + jj, 64);
+          const u32x4_t* base = pass == 0 ? dxs : wr;
+#pragma unroll
+          for (int u = 0; u < kSlices; ++u) {
+            const int c = c0 + 64 * u;
+            if (j0 + jj < k && r >= 0 && c < vec_per_row) v[jj][u] = base[size_t(r) * vec_per_row + c];
+          }
         }
-      }
-    }
-    for (int j = 0; j < k; ++j) {
-      const int e_j = __shfl(my_e, j, 64);
-      const float d = __shfl(my_dl, j, 64);
 #pragma unroll
-      for (int u = 0; u < kSlices; ++u) {
-        const int c = c0 + lane + 64 * u;
-        if (c < vec_per_row) {
-          float f[EPV];
-          unpack16(wr[size_t(e_j) * vec_per_row + c], T(), f);
+        for (int jj = 0; jj < KB; ++jj) {
+          const int r = pass == 0 ? __shfl(my_row, j0 + jj, 64) : 0;
+          if (j0 + jj >= k || r < 0) continue;  // uniform over the wave
+          const float d = pass == 0 ? 1.0f : __shfl(my_dl, j0 + jj, 64);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[u][e] = fmaf(d, f[e], acc[u][e]);
+          for (int u = 0; u < kSlices; ++u) {
+            const int c = c0 + 64 * u;
+            if (c < vec_per_row) {
+              float f[EPV];
+              unpack16(make_uint4(v[jj][u][0], v[jj][u][1], v[jj][u][2], v[jj][u][3]), T(), f);
+#pragma unroll
+              for (int e = 0; e < EPV; ++e) acc[u][e] = pass == 0 ? acc[u][e] + f[e] : fmaf(d, f[e], acc[u][e]);
+            }
+          }
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
-      const int c = c0 + lane + 64 * u;
-      if (c < vec_per_row) dx[size_t(t) * vec_per_row + c] = pack16(acc[u], T());
+      const int c = c0 + 64 * u;
+      if (c < vec_per_row) {
+        const uint4 pk = pack16(acc[u], T());
+        dx[size_t(t) * vec_per_row + c] = u32x4_t{pk.x, pk.y, pk.z, pk.w};
+      }
     }
   }
 }
@@ -653,9 +678,20 @@ moe_status combine_bwd_t(const CombineBwdArgs& a) {
   const moe_layer_desc* d = a.d;
   const int vpr = int(size_t(d->hidden) * sizeof(T) / 16);
   const dim3 grid(unsigned((d->num_tokens + kTokensPerBlock - 1) / kTokensPerBlock));
-  MOE_LAUNCH("combine_bwd", combine_bwd_kernel<T>, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.dy),
-             static_cast<const uint4*>(a.y_sorted), a.pair_row, a.topk_w, d->num_tokens, d->top_k, vpr,
-             static_cast<uint4*>(a.dy_sorted), a.dl);
+  const u32x4_t* dy = static_cast<const u32x4_t*>(a.dy);
+  const u32x4_t* ys = static_cast<const u32x4_t*>(a.y_sorted);
+  u32x4_t* dys = static_cast<u32x4_t*>(a.dy_sorted);
+  const int k = d->top_k;
+  if (k <= 2) {
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 2>), grid, dim3(256), 0, a.s, dy, ys, a.pair_row, a.topk_w,
+               d->num_tokens, k, vpr, dys, a.dl);
+  } else if (k <= 4) {
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 4>), grid, dim3(256), 0, a.s, dy, ys, a.pair_row, a.topk_w,
+               d->num_tokens, k, vpr, dys, a.dl);
+  } else {
+    MOE_LAUNCH("combine_bwd", (combine_bwd_kernel<T, 8>), grid, dim3(256), 0, a.s, dy, ys, a.pair_row, a.topk_w,
+               d->num_tokens, k, vpr, dys, a.dl);
+  }
   return MOE_OK;
 }
 
@@ -664,9 +700,20 @@ moe_status dispatch_bwd_t(const DispatchBwdArgs& a) {
   const moe_layer_desc* d = a.d;
   const int vpr = int(size_t(d->hidden) * sizeof(T) / 16);
   const dim3 grid(unsigned((d->num_tokens + kTokensPerBlock - 1) / kTokensPerBlock));
-  MOE_LAUNCH("dispatch_bwd", dispatch_bwd_kernel<T>, grid, dim3(256), 0, a.s, static_cast<const uint4*>(a.dx_sorted),
-             a.pair_row, a.topk_ids, a.dl, static_cast<const uint4*>(a.w_router), d->num_tokens, d->top_k, vpr,
-             static_cast<uint4*>(a.dx));
+  const u32x4_t* dxs = static_cast<const u32x4_t*>(a.dx_sorted);
+  const u32x4_t* wr = static_cast<const u32x4_t*>(a.w_router);
+  u32x4_t* dx = static_cast<u32x4_t*>(a.dx);
+  const int k = d->top_k;
+  if (k <= 2) {
+    MOE_LAUNCH("dispatch_bwd", (dispatch_bwd_kernel<T, 2>), grid, dim3(256), 0, a.s, dxs, a.pair_row, a.topk_ids,
+               a.dl, wr, d->num_tokens, k, vpr, dx);
+  } else if (k <= 4) {
+    MOE_LAUNCH("dispatch_bwd", (dispatch_bwd_kernel<T, 4>), grid, dim3(256), 0, a.s, dxs, a.pair_row, a.topk_ids,
+               a.dl, wr, d->num_tokens, k, vpr, dx);
+  } else {
+    MOE_LAUNCH("dispatch_bwd", (dispatch_bwd_kernel<T, 8>), grid, dim3(256), 0, a.s, dxs, a.pair_row, a.topk_ids,
+               a.dl, wr, d->num_tokens, k, vpr, dx);
+  }
   return MOE_OK;
 }
 
