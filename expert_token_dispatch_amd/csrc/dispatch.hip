@@ -493,7 +493,8 @@ int place_split(int nblk) {  // power of two, kDispatchTokens divisible by it
 }
 // With few chunks and experts the place blocks find their own bases: every
 // block sums the chunk histograms it needs (no separate scan launch).
-constexpr int kFuseEntries = 16384;  // chunks x experts up to which the scan is folded in
+constexpr int kFuseEntries = 65536;  // chunks x experts up to which the scan is folded in (gpt-oss-like
+                                     // share, 256 x 128: layer -2% against a scan launch)
 
 // FUSED: run[i] = (pairs of local experts before i) + (pairs of local expert i
 // in earlier chunks), from the chunk histograms; block 0 also writes counts,
