@@ -34,6 +34,12 @@
 //             block also sums the columns it needs itself, so no scan launch
 //             sits between the router and the copy;
 //   gather    with a capacity cut, the same token-major copy after it.
+// The gather writes x_sorted with nontemporal stores: a capacity-limited layer
+// has many pairs (hundreds of MB of rows, more than the last-level cache), so
+// the rows stream to memory instead of evicting what the caches hold (same-box
+// A/B on the skewed layer with capacity: dispatch stage 151 -> 130 us).  The
+// place kernel keeps ordinary stores: there the rows are read back from the
+// caches by the grouped GEMM.
 #include "common.h"
 #include "kernels.h"
 
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int c = c0 + u * 64 + lane;
-        if (c < vec_per_row) dst[c] = v[u];
+        if (c < vec_per_row) __builtin_nontemporal_store(v[u], dst + c);
       }
     }
   }

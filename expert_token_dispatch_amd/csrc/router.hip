@@ -47,25 +47,22 @@ typedef __attribute__((address_space(1))) void* glb_ptr_t;
 template <typename T> struct RouterMma;
 template <> struct RouterMma<bf16_t> {
   static constexpr int kStepK = 64;  // k per 128-byte chunk
-  // two MFMA 16x16x32 per chunk; the lane supplies k = 32*s + 8*(lane/16) .. +7
-  __device__ static void mma(const u32x4_t* a, const u32x4_t* b, f32x4_t& c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[0]), __builtin_bit_cast(bf16x8_t, b[0]),
-                                                c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[1]), __builtin_bit_cast(bf16x8_t, b[1]),
-                                                c, 0, 0, 0);
+  // one MFMA 16x16x32 per 16-byte piece s (two per chunk); the lane supplies
+  // k = 32*s + 8*(lane/16) .. +7
+  __device__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x4_t& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                0, 0, 0);
   }
   // byte offset inside a 128-byte chunk of the lane's 16-byte piece s (s = 0, 1)
   __device__ static int piece(int lane, int s) { return s * 64 + (lane >> 4) * 16; }
 };
 template <> struct RouterMma<float> {
   static constexpr int kStepK = 32;
-  // eight MFMA 16x16x4 per chunk; the lane supplies k = 16*s + 4*(lane/16) .. +3
-  __device__ static void mma(const u32x4_t* a, const u32x4_t* b, f32x4_t& c) {
+  // four MFMA 16x16x4 per 16-byte piece s (eight per chunk); the lane supplies
+  // k = 16*s + 4*(lane/16) .. +3
+  __device__ static void mma(const u32x4_t& a, const u32x4_t& b, f32x4_t& c) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[s][v]), __uint_as_float(b[s][v]), c, 0, 0, 0);
+    for (int v = 0; v < 4; ++v) c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[v]), __uint_as_float(b[v]), c, 0, 0, 0);
   }
   __device__ static int piece(int lane, int s) { return s * 64 + (lane >> 4) * 16; }
 };
@@ -164,17 +161,26 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(const T* __restrict__ 
       a[p] = *reinterpret_cast<const u32x4_t*>(slot + arow * kRowBytes + swz(arow, c) * 16);
       if (kb + M::kStepK > k_end && kb + c * EPC >= k_end) a[p] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    // every fragment of the stage first, then the products with the expert
+    // blocks interleaved (each accumulator still takes piece 0, then piece 1,
+    // so the sums are those of one expert block at a time); independent
+    // products back to back keep the matrix pipe from waiting on a result
+    // (same-box A/B: route stage 42.0 -> 39.1 us on the gpt-oss-like layer)
+    u32x4_t b[NEB][2];
 #pragma unroll
     for (int nb = 0; nb < NEB; ++nb) {
       const int r = kTok + nb * 16 + (lane & 15);
-      u32x4_t b[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int c = M::piece(lane, p) >> 4;
-        b[p] = *reinterpret_cast<const u32x4_t*>(slot + r * kRowBytes + swz(r, c) * 16);
+        b[nb][p] = *reinterpret_cast<const u32x4_t*>(slot + r * kRowBytes + swz(r, c) * 16);
       }
-      M::mma(a, b, acc[nb]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int nb = 0; nb < NEB; ++nb) M::mma(a[p], b[nb][p], acc[nb]);
   }
   MOE_VMCNT(0);
 
