@@ -165,10 +165,17 @@ def cpu_baseline(inp, tokens: int, backward: bool = False) -> dict:
         oracle.layer_forward(sub)
     dt = time.perf_counter() - t0
     blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1), "kind": "oracle",
             "sample": f"first {tokens} of {s.T} tokens of the same layer, all {s.L} experts' weights; "
                       f"whole oracle {'forward + backward' if backward else 'path'} (float64) in {dt:.1f} s; "
-                      f"host has {os.cpu_count()} CPUs"}
+                      f"host has {os.cpu_count()} CPUs ({model}); BLAS threads {int(max(blas) if blas else 1)}, "
+                      f"routing and counting-sort loops single-threaded"}
 
 
 def main():
