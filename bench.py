@@ -145,9 +145,37 @@ def traffic_for(kernel: str, workload: str, training: bool = False):
     return rec["bytes_per_launch"]
 
 
+def _oracle_forward_steps(sub) -> tuple[dict, dict]:
+    """The oracle layer forward step by step (its own functions, in the order of its
+    layer_forward), with the seconds each step took."""
+    import oracle
+    from oracle.moe_oracle import _ExpertView
+    s = sub["spec"]
+    dt = s.dtype
+    sec = {}
+    t0 = time.perf_counter()
+    x = oracle.decode(sub["x"], dt)
+    wr = oracle.decode(sub["w_router"], dt)
+    br = sub.get("b_router")
+    br = None if br is None else br.astype("float64")
+    r = oracle.route(x, wr, br, s.k)
+    t1 = time.perf_counter()
+    sec["route"] = t1 - t0
+    d = oracle.dispatch(r["topk_ids"], r["topk_logit"], s.E, s.local_begin, s.L, s.capacity_factor, x=x)
+    t2 = time.perf_counter()
+    sec["dispatch"] = t2 - t1
+    ys = oracle.grouped_ffn(d["x_sorted"], d["offsets"], _ExpertView(sub["w_gate"], dt), _ExpertView(sub["w_up"], dt),
+                            _ExpertView(sub["w_down"], dt))
+    t3 = time.perf_counter()
+    sec["grouped_ffn"] = t3 - t2
+    y = oracle.combine(ys, d["pair_row"], r["topk_w"])
+    sec["combine"] = time.perf_counter() - t3
+    return {**r, **d, "y_sorted": ys, "y": y, "tokens": None}, sec
+
+
 def cpu_baseline(inp, tokens: int, backward: bool = False) -> dict:
     """The oracle as it stands, on the first `tokens` tokens of the same layer
-    (with backward: its forward and backward, a training step)."""
+    (with backward: its forward and backward, a training step), timed per step."""
     import numpy as np
     import oracle
     import oracle.moe_backward as ob
@@ -159,23 +187,65 @@ def cpu_baseline(inp, tokens: int, backward: bool = False) -> dict:
     sub["x"] = np.ascontiguousarray(inp["x"][:tokens])
     dy = oracle.decode(synth.make_upstream_grad(s)[:tokens], s.dtype) if backward else None
     t0 = time.perf_counter()
+    fwd, sec = _oracle_forward_steps(sub)
     if backward:
-        ob.layer_backward(sub, dy)
-    else:
-        oracle.layer_forward(sub)
+        tb = time.perf_counter()
+        ob.layer_backward(sub, dy, fwd_out=fwd)
+        sec["backward"] = time.perf_counter() - tb
     dt = time.perf_counter() - t0
-    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    blas = [i.get("num_threads", 1) for i in info]
+    lib = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info})) or "none"
     model = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1), "kind": "oracle",
+    nth = int(max(blas) if blas else 1)
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": nth, "kind": "oracle",
+            "seconds_per_step": {k: round(v, 3) for k, v in sec.items()},
+            "blas": lib,
             "sample": f"first {tokens} of {s.T} tokens of the same layer, all {s.L} experts' weights; "
                       f"whole oracle {'forward + backward' if backward else 'path'} (float64) in {dt:.1f} s; "
-                      f"host has {os.cpu_count()} CPUs ({model}); BLAS threads {int(max(blas) if blas else 1)}, "
-                      f"routing and counting-sort loops single-threaded"}
+                      f"host has {os.cpu_count()} CPUs ({model}); BLAS ({lib}) threads {nth} in the expert "
+                      f"products; routing, counting-sort and combine loops single-threaded NumPy"}
+
+
+def routing_report(inp, ids_gpu, counts_gpu, dropped: int, P: int, with_oracle: bool) -> dict:
+    """The realised routing of the timed layer: per-expert loads (all E, before any capacity
+    cut), per-rank loads of an expert-parallel split when this GPU holds one block, the drop
+    count; and, from the oracle's float64 logits, the top-k flips (tokens whose chosen set
+    differs) with the smallest and largest logit gap among them."""
+    import numpy as np
+    s = inp["spec"]
+    cnt = np.asarray(counts_gpu, dtype=np.int64)
+    out = {"expert_load_min": int(cnt.min()), "expert_load_max": int(cnt.max()),
+           "even_share": s.T * s.k / s.E, "experts_empty": int((cnt == 0).sum()),
+           "local_pairs_routed": int(cnt[s.local_begin:s.local_begin + s.L].sum()),
+           "pairs_kept": P, "pairs_dropped": dropped}
+    if s.L < s.E and s.E % s.L == 0:
+        ranks = cnt.reshape(s.E // s.L, s.L).sum(axis=1)
+        out["rank_loads"] = {"ranks": s.E // s.L, "min": int(ranks.min()), "max": int(ranks.max())}
+    if with_oracle:
+        import oracle
+        x = oracle.decode(inp["x"], s.dtype)
+        wr = oracle.decode(inp["w_router"], s.dtype)
+        br = None if inp["b_router"] is None else inp["b_router"].astype(np.float64)
+        lg64 = oracle.router_logits(x, wr, br)
+        del x
+        ref = oracle.topk_select(lg64, s.k)
+        bad = np.flatnonzero(np.any(np.sort(ids_gpu, axis=1) != np.sort(ref, axis=1), axis=1))
+        if s.k < s.E:
+            srt = -np.sort(-lg64, axis=1)
+            gap = srt[:, s.k - 1] - srt[:, s.k]
+        else:
+            gap = np.full(s.T, np.inf)
+        out["topk_flips"] = int(len(bad))
+        out["flip_gap_min"] = float(gap[bad].min()) if len(bad) else None
+        out["flip_gap_max"] = float(gap[bad].max()) if len(bad) else None
+        out["flip_gap_allowed"] = 1e-5
+    return out
 
 
 def main():
@@ -411,6 +481,7 @@ def main():
         "kernels": kern,
         "roofline": roof,
     }
+    out["routing"] = routing_report(inp, ids_h, cnt_h, int(dropped.item()), P, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, s.T), backward=args.backward)

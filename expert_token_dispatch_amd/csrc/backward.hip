@@ -68,11 +68,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restr
   const float my_w = lane < k ? tw[t * k + lane] : 0.0f;
   float my_dot = 0.0f;  // lane j: <dy[t], y_sorted[row of slot j]>
   const u32x4_t* src = dy + size_t(t) * vec_per_row;
-  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
+  // every lane runs every pass (slot broadcasts and wave sums read other
+  // lanes' registers); slice c0 + 64u + lane
+  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kSlices) {
     float g[kSlices][EPV];
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
-      const int c = c0 + 64 * u;
+      const int c = c0 + 64 * u + lane;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (c < vec_per_row) v = src[c];
       unpack16(make_uint4(v[0], v[1], v[2], v[3]), T(), g[u]);
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restr
         const int r = __shfl(my_row, j0 + jj, 64);
 #pragma unroll
         for (int u = 0; u < kSlices; ++u) {
-          const int c = c0 + 64 * u;
+          const int c = c0 + 64 * u + lane;
           if (j0 + jj < k && r >= 0 && c < vec_per_row) v[jj][u] = ys[size_t(r) * vec_per_row + c];
         }
       }
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const u32x4_t* __restr
         float p = 0.0f;
 #pragma unroll
         for (int u = 0; u < kSlices; ++u) {
-          const int c = c0 + 64 * u;
+          const int c = c0 + 64 * u + lane;
           if (c < vec_per_row) {
             float f[EPV], o[EPV];
             unpack16(make_uint4(v[jj][u][0], v[jj][u][1], v[jj][u][2], v[jj][u][3]), T(), f);
@@ -138,7 +140,9 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const u32x4_t* __rest
   const int my_row = lane < k ? pair_row[t * k + lane] : -1;
   const int my_e = lane < k ? ids[t * k + lane] : 0;
   const float my_dl = lane < k ? dl[t * k + lane] : 0.0f;
-  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
+  // every lane runs every pass (slot broadcasts and wave sums read other
+  // lanes' registers); slice c0 + 64u + lane
+  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kSlices) {
     float acc[kSlices][EPV];
 #pragma unroll
     for (int u = 0; u < kSlices; ++u)
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const u32x4_t* __rest
           const u32x4_t* base = pass == 0 ? dxs : wr;
 #pragma unroll
           for (int u = 0; u < kSlices; ++u) {
-            const int c = c0 + 64 * u;
+            const int c = c0 + 64 * u + lane;
             if (j0 + jj < k && r >= 0 && c < vec_per_row) v[jj][u] = base[size_t(r) * vec_per_row + c];
           }
         }
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const u32x4_t* __rest
           const float d = pass == 0 ? 1.0f : __shfl(my_dl, j0 + jj, 64);
 #pragma unroll
           for (int u = 0; u < kSlices; ++u) {
-            const int c = c0 + 64 * u;
+            const int c = c0 + 64 * u + lane;
             if (c < vec_per_row) {
               float f[EPV];
               unpack16(make_uint4(v[jj][u][0], v[jj][u][1], v[jj][u][2], v[jj][u][3]), T(), f);
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(256) void dispatch_bwd_kernel(const u32x4_t* __rest
     }
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
-      const int c = c0 + 64 * u;
+      const int c = c0 + 64 * u + lane;
       if (c < vec_per_row) {
         const uint4 pk = pack16(acc[u], T());
         dx[size_t(t) * vec_per_row + c] = u32x4_t{pk.x, pk.y, pk.z, pk.w};

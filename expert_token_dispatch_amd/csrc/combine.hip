@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   const float my_w = lane < k ? tw[t * k + lane] : 0.0f;
   uint4* dst = y + size_t(t) * vec_per_row;
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(ys);
-  for (int c0 = lane; c0 < vec_per_row; c0 += 64 * kSlices) {
+  // every lane runs every pass (the slot broadcasts below read other lanes'
+  // registers, so no lane may leave the loop early); slice c0 + 64u + lane
+  for (int c0 = 0; c0 < vec_per_row; c0 += 64 * kSlices) {
     float acc[kSlices][EPV];
 #pragma unroll
     for (int u = 0; u < kSlices; ++u)
@@ -50,7 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
         const int r = __shfl(my_row, j0 + jj, 64);
 #pragma unroll
         for (int u = 0; u < kSlices; ++u) {
-          const int c = c0 + 64 * u;
+          const int c = c0 + 64 * u + lane;
           if (j0 + jj < k && r >= 0 && c < vec_per_row) v[u][jj] = src[size_t(r) * vec_per_row + c];
         }
       }
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < kSlices; ++u) {
-      const int c = c0 + 64 * u;
+      const int c = c0 + 64 * u + lane;
       if (c < vec_per_row) dst[c] = pack16(acc[u], T());
     }
   }

@@ -367,9 +367,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
         chosen |= 1u << win;
         if (r == win) avail = false;
       }
+      // slots past the last expert are already taken (and their group index could
+      // exceed the mask's 32 bits)
 #pragma unroll
       for (int c = 0; c < VPL; ++c)
-        if (!((chosen >> ((r * VPL + c) / gsize)) & 1u)) taken |= 1u << c;
+        if (r * VPL + c < E && !((chosen >> ((r * VPL + c) / gsize)) & 1u)) taken |= 1u << c;
     }
     float sel_v[MAXK];
     int sel_i[MAXK];

@@ -271,7 +271,19 @@ def test_full_size_backward(name):
         ip = float((w.double() * gw.double()).sum())
         say(f"[bwd]   <{wname}, d{wname}> = {ip:.6e}, <dy, y> = {ydy:.6e}")
         assert abs(ip - ydy) <= 2e-2 * np.sqrt(float((dy * dy).sum()) * float((gpu["y"] ** 2).sum()))
-    # sampled experts against the oracle, on the GPU's own x_sorted and dy_sorted
+    # the oracle's own stage inputs of the experts: x_sorted from its dispatch (on the GPU's logits),
+    # dy_sorted = w * dy from its combine backward
+    f = oracle.layer_forward(inp, logits=gpu["logits"], tokens=np.zeros(0, dtype=np.int64))
+    np.testing.assert_array_equal(gpu["offsets"], f["offsets"])
+    np.testing.assert_array_equal(gpu["pair_row"], f["pair_row"])
+    f_xs = f["x_sorted"]
+    P = int(f["offsets"][-1])
+    f_dys = np.zeros((P, s.H))
+    pr = f["pair_row"].reshape(s.T, s.k)
+    for j in range(s.k):
+        has = pr[:, j] >= 0
+        f_dys[pr[has, j]] = f["topk_w"][has, j][:, None] * dy[has]
+    # sampled experts against the oracle's expert backward on those inputs
     big = int(np.argmax(sizes))
     experts = [big] if s.H * s.I * int(sizes[big]) > 2e10 else sorted({big, int(np.argsort(sizes)[len(sizes) // 2])})
     for i in experts:
@@ -284,8 +296,9 @@ def test_full_size_backward(name):
         wg = oracle.decode(inp["w_gate"][i], s.dtype)
         wu = oracle.decode(inp["w_up"][i], s.dtype)
         wd = oracle.decode(inp["w_down"][i], s.dtype)
-        xs = gpu["x_sorted"][rows]
-        r = B.expert_ffn_backward(xs, wg, wu, wd, gpu["dy_sorted"][rows])
+        xs = f_xs[rows]
+        rows_ok(f"dy_sorted[{i}]", gpu["dy_sorted"][rows], f_dys[rows], s.dtype)
+        r = B.expert_ffn_backward(xs, wg, wu, wd, f_dys[rows])
         say(f"[bwd]   expert {i}: {b - a} rows, {len(rows)} checked")
         rows_ok(f"gate[{i}]", gpu["gate"][rows], r["g"], s.dtype)
         rows_ok(f"dx_sorted[{i}]", gpu["dx_sorted"][rows], r["dv"], s.dtype)
@@ -294,11 +307,26 @@ def test_full_size_backward(name):
             mat_ok(f"dw_up[{i}]", gpu["dw_up"][i], r["dwu"], s.dtype)
             mat_ok(f"dw_down[{i}]", gpu["dw_down"][i], r["dwd"], s.dtype)
         else:
-            # dW_down = dy_sorted^T h over the whole segment (hundreds of rows), on sampled output rows
-            hs = gpu["h"][a:b]
+            # the largest segments: weight gradients on sampled output rows, every input column,
+            # from the oracle's own intermediates (x_sorted, w * dy, the gate/up products in float64)
+            xs_all = gpu["x_sorted"][a:b].astype(np.float64)
+            np.testing.assert_array_equal(xs_all, f_xs[a:b])
+            dout = f_dys[a:b]
+            g = xs_all @ wg.T
+            u = xs_all @ wu.T
+            with np.errstate(over="ignore"):
+                sg = 1.0 / (1.0 + np.exp(-g))
+            hh = g * sg * u
             for hrow in (0, s.H // 3, s.H - 1):
-                want = gpu["dy_sorted"][a:b, hrow] @ hs
+                want = dout[:, hrow] @ hh
                 rows_ok(f"dw_down[{i}][{hrow}]", gpu["dw_down"][i][hrow][None], want[None], s.dtype)
+            for c in (0, s.I // 2, s.I - 1):
+                dh = dout @ wd[:, c]
+                dg = dh * u[:, c] * sg[:, c] * (1.0 + g[:, c] * (1.0 - sg[:, c]))
+                du = dh * g[:, c] * sg[:, c]
+                rows_ok(f"dw_gate[{i}][{c}]", gpu["dw_gate"][i][c][None], (dg @ xs_all)[None], s.dtype)
+                rows_ok(f"dw_up[{i}][{c}]", gpu["dw_up"][i][c][None], (du @ xs_all)[None], s.dtype)
+            del g, u, sg, hh
     # experts that received nothing get exactly zero
     for i in np.flatnonzero(sizes == 0):
         assert not np.any(gpu["dw_gate"][i]) and not np.any(gpu["dw_up"][i]) and not np.any(gpu["dw_down"][i])
