@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     moe_capacity,
     moe_combine,
     moe_dispatch,
+    moe_dispatch_noalloc,
     moe_ep_local_range,
     moe_grouped_ffn,
     moe_last_error,

@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "moe_profile_kernel_count": (ctypes.c_int32, []),
             "moe_route": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
             "moe_dispatch": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+            "moe_dispatch_noalloc": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "moe_grouped_ffn": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
             "moe_combine": (st, [_DP, _VP, _VP, _VP, _VP, _VP]),
             "moe_layer_forward": (st, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -224,6 +225,12 @@ def moe_dispatch(d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair
     wp, wn = _ws(ws)
     _check(lib().moe_dispatch(ctypes.byref(d), _p(x), _p(topk_ids), _p(topk_logit), _p(counts), _p(offsets),
                               _p(sorted_pairs), _p(pair_row), _p(x_sorted), _p(num_dropped), wp, wn, _s(stream)))
+
+
+def moe_dispatch_noalloc(d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted,
+                         num_dropped=None, stream=None) -> None:
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(d), _p(x), _p(topk_ids), _p(topk_logit), _p(counts), _p(offsets),
+                                      _p(sorted_pairs), _p(pair_row), _p(x_sorted), _p(num_dropped), _s(stream)))
 
 
 def moe_grouped_ffn(d, x_sorted, offsets, w_gate, w_up, w_down, y_sorted, ws=None, stream=None) -> None:

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -403,6 +404,44 @@ void apply_opts(RouteArgs& a, const moe_layer_desc* d, const moe_route_opts* o) 
 }  // namespace
 }  // namespace moe
 
+// ---- the dispatch scratch of moe_dispatch_noalloc -----------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid hipMalloc): the dispatch kernels'
+// scratch (per-chunk histograms, per-chunk segment bases, pre-capacity
+// offsets and permutation) lives in this file-scope device array instead of a
+// caller workspace.  Each GPU holds its own copy for the life of the process.
+// Host code never passes the array's name to a kernel (on the host it only
+// names a stand-in): it resolves the device address once per device with
+// hipGetSymbolAddress and passes that.
+namespace moe {
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (resolved on the first call per device).
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return set_error(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(ge));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return set_error(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
@@ -506,6 +545,26 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
   TRY(check_ws(d, MOE_STAGE_DISPATCH, ws, ws_bytes));
   DispatchArgs a{d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped,
                  carve_dispatch_scratch(d, ws), capacity_of(d), false, static_cast<hipStream_t>(stream)};
+  return launch_dispatch(a);
+}
+
+moe_status moe_dispatch_noalloc(const moe_layer_desc* d, const void* x, const int32_t* topk_ids,
+                                const float* topk_logit, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                                int32_t* pair_row, void* x_sorted, int64_t* num_dropped, void* stream) {
+  CallScope scope;
+  TRY(check_desc(d));
+  if (d->num_tokens == 0) return MOE_OK;
+  TRY(dispatch_checks(d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped));
+  const size_t need = dispatch_scratch_bytes(d);
+  if (need > kNoAllocScratchBytes)
+    return set_error(MOE_ERR_UNSUPPORTED, "dispatch_noalloc: %zu bytes of scratch needed, the static buffer holds %zu",
+                     need, kNoAllocScratchBytes);
+  void* scr = nullptr;
+  TRY(noalloc_scratch(&scr));
+  // every scratch entry the kernels read is written earlier in the same call, so
+  // nothing needs clearing between calls
+  DispatchArgs a{d, x, topk_ids, topk_logit, counts, offsets, sorted_pairs, pair_row, x_sorted, num_dropped,
+                 carve_dispatch_scratch(d, scr), capacity_of(d), false, static_cast<hipStream_t>(stream)};
   return launch_dispatch(a);
 }
 

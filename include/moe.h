@@ -18,7 +18,8 @@
  *  - Pointers marked "device" are GPU memory on the current HIP device;
  *    "host" pointers are CPU memory.  The caller owns every buffer; the
  *    library allocates no memory and keeps no state between calls apart from
- *    a thread-local error message and the optional profiling events.
+ *    a thread-local error message, the optional profiling events and the
+ *    static device buffer of moe_dispatch_noalloc.
  *  - Tensors are dense and row-major.  Device pointers to activations,
  *    weights and outputs must be 16-byte aligned; index arrays 4-byte aligned.
  *  - Activations and weights share one element type, desc->dtype: MOE_BF16
@@ -232,6 +233,27 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
                         const float* topk_logit, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_pairs, int32_t* pair_row, void* x_sorted,
                         int64_t* num_dropped, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and outputs as moe_dispatch, bit for bit, but the
+ * dispatch scratch (per-chunk expert histograms, per-chunk segment bases,
+ * the pre-capacity offsets and permutation) lives in a static 16 MiB device
+ * buffer of the library instead of a caller workspace.  Each GPU the library
+ * runs on holds its own buffer until the process ends; its address is
+ * resolved on the first call on each device.  The call allocates nothing.
+ * Arguments as moe_dispatch, without ws / ws_bytes.  Every call on one GPU
+ * shares that GPU's buffer: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Each call writes every scratch entry it reads, so nothing carries over
+ * from the previous call.  MOE_ERR_UNSUPPORTED (nothing enqueued) when the
+ * layer needs more scratch than the buffer holds (the MOE_STAGE_DISPATCH
+ * size, moe_workspace_size, above 16 MiB: roughly T * (E + L) / 16 + 4 T k
+ * bytes); other errors as moe_dispatch. */
+moe_status moe_dispatch_noalloc(const moe_layer_desc* d, const void* x, const int32_t* topk_ids,
+                                const float* topk_logit, int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_pairs, int32_t* pair_row, void* x_sorted,
+                                int64_t* num_dropped, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Stage 3: local experts as one grouped GEMM.  Glossary, step 3: each GPU  */
