@@ -149,7 +149,7 @@ def _oracle_forward_steps(sub) -> tuple[dict, dict]:
     """The oracle layer forward step by step (its own functions, in the order of its
     layer_forward), with the seconds each step took."""
     import oracle
-    from oracle.moe_oracle import _ExpertView
+    from oracle.moe_oracle import expert_views
     s = sub["spec"]
     dt = s.dtype
     sec = {}
@@ -164,8 +164,7 @@ def _oracle_forward_steps(sub) -> tuple[dict, dict]:
     d = oracle.dispatch(r["topk_ids"], r["topk_logit"], s.E, s.local_begin, s.L, s.capacity_factor, x=x)
     t2 = time.perf_counter()
     sec["dispatch"] = t2 - t1
-    ys = oracle.grouped_ffn(d["x_sorted"], d["offsets"], _ExpertView(sub["w_gate"], dt), _ExpertView(sub["w_up"], dt),
-                            _ExpertView(sub["w_down"], dt))
+    ys = oracle.grouped_ffn(d["x_sorted"], d["offsets"], *expert_views(sub))
     t3 = time.perf_counter()
     sec["grouped_ffn"] = t3 - t2
     y = oracle.combine(ys, d["pair_row"], r["topk_w"])
@@ -255,6 +254,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_like")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--weight-layout", choices=["out_in", "in_out"], default="out_in",
+                    help="expert weights as a linear layer stores them ([L, I, H] gate/up) or in the math form "
+                         "([L, H, I] gate/up, [L, I, H] down)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--route-groups", type=int, nargs=2, default=None, metavar=("G", "M"),
@@ -281,10 +283,10 @@ def main():
     import expert_token_dispatch_amd as etd
     from expert_token_dispatch_amd.layer import MoELayer, to_device
 
-    s = synth.spec(args.workload, seed=args.seed)
+    s = synth.spec(args.workload, seed=args.seed, weight_layout=args.weight_layout)
     log(f"[bench] generating {s}")
     inp = synth.make_layer(s)
-    desc = etd.make_desc(s.T, s.H, s.I, s.E, s.k, s.local_begin, s.L, s.capacity_factor, s.dtype)
+    desc = etd.make_desc(s.T, s.H, s.I, s.E, s.k, s.local_begin, s.L, s.capacity_factor, s.dtype, s.weight_layout)
     layer = MoELayer.from_host(desc, inp)
     x = to_device(inp["x"], s.dtype)
     y = torch.empty_like(x)
@@ -472,6 +474,7 @@ def main():
         "config": {"workload": s.name, "tokens": s.T, "hidden": s.H, "intermediate": s.I, "experts": s.E,
                    "top_k": s.k, "local_experts": [s.local_begin, s.local_begin + s.L],
                    "capacity_factor": s.capacity_factor, "pairs_kept": P, "seed": s.seed,
+                   "weight_layout": s.weight_layout,
                    **({"route_groups": args.route_groups} if args.route_groups else {}),
                    **({"balance_gamma": args.balance_gamma} if args.balance_gamma is not None else {})},
         "grouped_gemm_mfma_frac": round(gemm_frac, 4) if gemm_frac else None,

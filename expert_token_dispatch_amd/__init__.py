@@ -10,6 +10,8 @@ library is not built, every call raises.
 from ._lib import (  # noqa: F401
     MOE_BF16,
     MOE_F32,
+    MOE_WEIGHTS_OUT_IN,
+    MOE_WEIGHTS_IN_OUT,
     MOE_STAGE_COMBINE,
     MOE_STAGE_DISPATCH,
     MOE_STAGE_FFN,

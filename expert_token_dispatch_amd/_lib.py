@@ -11,6 +11,7 @@ lib_path = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WEIGHTS_OUT_IN, MOE_WEIGHTS_IN_OUT = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_FFN, MOE_STAGE_COMBINE, MOE_STAGE_LAYER = 0, 1, 2, 3, 4
 MOE_STAGE_FFN_BACKWARD, MOE_STAGE_ROUTE_BACKWARD, MOE_STAGE_LAYER_BACKWARD = 5, 6, 7
 
@@ -35,6 +36,7 @@ class LayerDesc(ctypes.Structure):
         ("local_count", ctypes.c_int32),
         ("capacity_factor", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -71,11 +73,15 @@ def make_route_opts(selection_bias=None, num_groups: int = 0, max_groups: int = 
 
 def make_desc(num_tokens: int, hidden: int, intermediate: int, num_experts: int, top_k: int,
               local_begin: int = 0, local_count: Optional[int] = None, capacity_factor: float = 0.0,
-              dtype="bf16") -> LayerDesc:
+              dtype="bf16", weight_layout="out_in") -> LayerDesc:
+    """weight_layout: "out_in" (w_gate, w_up [L, I, H], w_down [L, H, I]) or "in_out"
+    (w_gate, w_up [L, H, I], w_down [L, I, H]), or the MOE_WEIGHTS_* value."""
     if isinstance(dtype, str):
         dtype = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
+    if isinstance(weight_layout, str):
+        weight_layout = {"out_in": MOE_WEIGHTS_OUT_IN, "in_out": MOE_WEIGHTS_IN_OUT}[weight_layout]
     return LayerDesc(num_tokens, hidden, intermediate, num_experts, top_k, local_begin,
-                     num_experts if local_count is None else local_count, capacity_factor, dtype)
+                     num_experts if local_count is None else local_count, capacity_factor, dtype, weight_layout)
 
 
 _LIB = None

@@ -71,6 +71,8 @@ moe_status check_desc(const moe_layer_desc* d) {
     return set_error(MOE_ERR_INVALID_ARG, "local experts [%d, %d+%d) do not fit in [0, %d)", d->local_begin,
                      d->local_begin, d->local_count, d->num_experts);
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return set_error(MOE_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->weight_layout != MOE_WEIGHTS_OUT_IN && d->weight_layout != MOE_WEIGHTS_IN_OUT)
+    return set_error(MOE_ERR_INVALID_ARG, "unknown weight_layout %d", d->weight_layout);
   if (isnan(d->capacity_factor) || isinf(d->capacity_factor))
     return set_error(MOE_ERR_INVALID_ARG, "capacity_factor must be finite");
   if (d->num_tokens * int64_t(d->top_k) > INT32_MAX)

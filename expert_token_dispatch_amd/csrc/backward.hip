@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -386,7 +387,7 @@ struct DgradArgs {
   int K[2];
   int lda;
   const T* B[2];         // expert e: B[p] + e * b_estride, element (k, n) at [k * N + n]
-  int64_t b_estride;
+  int64_t b_estride;     //   (BNK: at [n * K[p] + k])
   int N;
   T* C;                  // [P, N] (plain epilogue)
   const T* G;            // SwiGLU epilogue: saved pre-activations [P, N] ...
@@ -397,8 +398,9 @@ struct DgradArgs {
 };
 
 // C = sum_p A[p] B[p]_e over the sorted rows of each expert (EPI 0), or the
-// SwiGLU backward of the result (EPI 1: C is dh; writes dg, du).
-template <typename T, int EPI, int NPROD>
+// SwiGLU backward of the result (EPI 1: C is dh; writes dg, du).  BNK: the
+// weight operand is n-major (rows of K), else k-major (rows of N).
+template <typename T, int EPI, int NPROD, bool BNK>
 __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradArgs<T> p) {
   using G = Mma<T>;
   constexpr int BK = G::BK, kLd = G::kLd;
@@ -442,13 +444,16 @@ __global__ __launch_bounds__(kThreads) void dgrad_kernel(DgradArgs<T> p) {
   const int nk0 = (K0 + BK - 1) / BK;
   const int nks = nk0 + (NPROD > 1 ? (K1 + BK - 1) / BK : 0);
   RowTile<T> ta;
-  ColTile<T> tb;
+  typename std::conditional<BNK, RowTile<T>, ColTile<T>>::type tb;
   auto gload = [&](int s) {
     const bool q = NPROD > 1 && s >= nk0;
     const int k0 = (s - (q ? nk0 : 0)) * BK;
     const int Kq = q ? K1 : K0;
     ta.load(q ? A1 : A0, lda, row0, rows, k0, Kq);
-    tb.load(q ? B1 : B0, N, k0, Kq, n0, N);
+    if constexpr (BNK)
+      tb.load(q ? B1 : B0, Kq, n0, N - n0, k0, Kq);
+    else
+      tb.load(q ? B1 : B0, N, k0, Kq, n0, N);
   };
   if (nks > 0) {
     gload(0);
@@ -499,7 +504,8 @@ struct WgradArgs {
   const T* A[2];          // element (m, k) of expert e at A[z][(o_e + k) * lda + m]
   int lda;
   int m_load;             // columns of A that may be read (a multiple of the vector width)
-  const T* B;             // element (k, n) at B[(o_e + k) * N + n]
+  const T* B[2];          // element (k, n) at B[z][(o_e + k) * ldb + n] (B[1] NULL: B[0] for both)
+  int ldb;
   T* C[2];                // expert e: C[z] + e * M * N, [M, N]
   int M, N;
   const int32_t* offsets; // NULL: one segment [0, k_total)
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs<T> p) {
     kseg = min(kseg - lo, per);
   }
   const T* A = (z ? p.A[1] : p.A[0]) + o * p.lda;
-  const T* B = p.B + o * p.N;
+  const T* B = (z && p.B[1] != nullptr ? p.B[1] : p.B[0]) + o * p.ldb;
   __shared__ __attribute__((aligned(16))) T As[2][BM * G::kLd];
   __shared__ __attribute__((aligned(16))) T Bs[2][BN * G::kLd];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, wm = wave >> 1, wn = wave & 1;
@@ -541,11 +547,11 @@ __global__ __launch_bounds__(kThreads) void wgrad_kernel(WgradArgs<T> p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nks = int((kseg + BK - 1) / BK);
-  const int lda = p.lda, m_load = p.m_load, N = p.N;
+  const int lda = p.lda, m_load = p.m_load, ldb = p.ldb, N = p.N;
   ColTile<T> ta, tb;
   auto gload = [&](int s) {
     ta.load(A, lda, s * BK, kseg, m0, m_load);
-    tb.load(B, N, s * BK, kseg, n0, N);
+    tb.load(B, ldb, s * BK, kseg, n0, N);
   };
   if (nks > 0) {
     gload(0);
@@ -593,32 +599,6 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
   float v = 0.0f;
   for (int z = 0; z < pieces; ++z) v += partial[size_t(z) * n + i];
   C[i] = Elem<T>::from_f32(v);
-}
-
-// Transpose of stacked matrices: dst[l][c][off + r] = src[l][r][c], src [L, R, C],
-// dst rows of ld elements.  64 x 64 tiles through LDS (R and C multiples of 64):
-// rows are read and written as 16-byte vectors.
-__global__ __launch_bounds__(256) void transpose_kernel(const bf16_t* __restrict__ src, int R, int C,
-                                                        bf16_t* __restrict__ dst, int ld, int off) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
-  const int l = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const bf16_t* s = src + size_t(l) * R * C;
-  bf16_t* d = dst + size_t(l) * C * ld;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = t / 8 + 32 * j, c8 = (t % 8) * 8;
-    *reinterpret_cast<u32x4_t*>(&tile[r][c8]) = *reinterpret_cast<const u32x4_t*>(s + size_t(r0 + r) * C + c0 + c8);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = t / 8 + 32 * j, r8 = (t % 8) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = uint32_t(tile[r8 + 2 * e][c]) | (uint32_t(tile[r8 + 2 * e + 1][c]) << 16);
-    *reinterpret_cast<u32x4_t*>(d + size_t(c0 + c) * ld + off + r0 + r8) = u32x4_t{w[0], w[1], w[2], w[3]};
-  }
 }
 
 // Per-expert transposed blocks for the weight gradients on the large tile: for
@@ -722,12 +702,10 @@ moe_status dispatch_bwd_t(const DispatchBwdArgs& a) {
 }
 
 // Scratch of the FFN backward: dg | du [P_max, 2I], then on the large-tile path the
-// tile plan and split-K pieces, wdT [L, I, H] and wguT [L, H, 2I].
+// tile plan and split-K pieces.
 struct FfnBwdScratch {
   void* dgu;
   void* big;  // big_backward_scratch_bytes
-  void* wdT;
-  void* wguT;
   // the weight gradients on the large tile: per-expert transposed blocks of
   // dy_sorted [H], h [I], dg | du [2I] and x_sorted [H] rows (see seg_transpose_kernel)
   void* dysT;
@@ -748,10 +726,7 @@ FfnBwdScratch carve_ffn_bwd(const moe_layer_desc* d, int64_t max_pairs, void* ba
   FfnBwdScratch w{};
   w.dgu = take(size_t(max_pairs) * 2 * d->intermediate * dt);
   if (big_backward_supported(d, max_pairs)) {
-    const size_t wbytes = size_t(d->local_count) * d->hidden * d->intermediate * dt;
     w.big = take(big_backward_scratch_bytes(d));
-    w.wdT = take(wbytes);
-    w.wguT = take(2 * wbytes);
     if (big_wgrad_supported(d, max_pairs)) {
       const size_t q = size_t(max_pairs) + size_t(64) * d->local_count;
       w.dysT = take(q * d->hidden * dt);
@@ -764,33 +739,33 @@ FfnBwdScratch carve_ffn_bwd(const moe_layer_desc* d, int64_t max_pairs, void* ba
   return w;
 }
 
+// With the math-form weights (MOE_WEIGHTS_IN_OUT) Wd_e is [I, H] and Wg_e, Wu_e [H, I];
+// the linear layout stores their transposes.  dh = dy_sorted Wd_e^T and
+// dx_sorted = dg Wg_e^T + du Wu_e^T read the weights in place either way (n-major
+// operands for the math form, k-major for the linear layout); the weight gradients
+// are written in the weights' layout: dWd_e = h^T dy_sorted [I, H] or its transpose
+// dy_sorted^T h [H, I], and likewise x_sorted^T dg or dg^T x_sorted.
 template <typename T>
 moe_status ffn_bwd_t(const FfnBwdArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  const bool io = d->weight_layout == MOE_WEIGHTS_IN_OUT;
   const FfnBwdScratch w = carve_ffn_bwd(d, a.max_pairs, a.scratch, nullptr);
   T* dgu = static_cast<T*>(w.dgu);
   bool big = false;
   if constexpr (sizeof(T) == 2) {
     if (w.big != nullptr) {
-      // the dgrad products on the large-tile kernel, with the weights transposed to [N, K] rows
+      // the dgrad products on the large-tile kernel, reading the weights in place
       big = true;
-      bf16_t* wdT = static_cast<bf16_t*>(w.wdT);
-      bf16_t* wguT = static_cast<bf16_t*>(w.wguT);
-      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(I / 64, H / 64, L), dim3(256), 0, a.s,
-                 static_cast<const bf16_t*>(a.w_down), H, I, wdT, H, 0);
-      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(H / 64, I / 64, L), dim3(256), 0, a.s,
-                 static_cast<const bf16_t*>(a.w_gate), I, H, wguT, 2 * I, 0);
-      MOE_LAUNCH("ffn_bwd_transpose", transpose_kernel, dim3(H / 64, I / 64, L), dim3(256), 0, a.s,
-                 static_cast<const bf16_t*>(a.w_up), I, H, wguT, 2 * I, I);
       const moe_status st = launch_big_backward_dgrad(
-          d, static_cast<const bf16_t*>(a.dy_sorted), a.offsets, wdT, static_cast<const bf16_t*>(a.gate),
-          static_cast<const bf16_t*>(a.up), dgu, wguT, static_cast<bf16_t*>(a.dx_sorted), a.max_pairs, w.big, a.s);
+          d, static_cast<const bf16_t*>(a.dy_sorted), a.offsets, static_cast<const bf16_t*>(a.w_down),
+          static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), static_cast<const bf16_t*>(a.gate),
+          static_cast<const bf16_t*>(a.up), dgu, static_cast<bf16_t*>(a.dx_sorted), a.max_pairs, w.big, a.s);
       if (st != MOE_OK) return st;
     }
   }
   const unsigned mslots = unsigned((a.max_pairs + BM - 1) / BM + L);
-  if (!big) {  // dh = dy_sorted Wd_e, then dg, du
+  if (!big) {  // dh = dy_sorted Wd_e^T, then dg, du
     DgradArgs<T> p{};
     p.A[0] = static_cast<const T*>(a.dy_sorted);
     p.K[0] = H;
@@ -803,7 +778,13 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
     p.DGU = dgu;
     p.offsets = a.offsets;
     p.L = L;
-    MOE_LAUNCH("ffn_down_dgrad", (dgrad_kernel<T, 1, 1>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0, a.s, p);
+    if (io) {
+      MOE_LAUNCH("ffn_down_dgrad", (dgrad_kernel<T, 1, 1, true>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
+                 a.s, p);
+    } else {
+      MOE_LAUNCH("ffn_down_dgrad", (dgrad_kernel<T, 1, 1, false>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
+                 a.s, p);
+    }
   }
   bool big_w = false;
   if constexpr (sizeof(T) == 2) {
@@ -817,35 +798,48 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
                    static_cast<const bf16_t*>(X), Cw, a.offsets, L, static_cast<bf16_t*>(XT));
         return MOE_OK;
       };
+      const bf16_t* dysT = static_cast<const bf16_t*>(w.dysT);
+      const bf16_t* hT = static_cast<const bf16_t*>(w.hT);
+      const bf16_t* dguT = static_cast<const bf16_t*>(w.dguT);
+      const bf16_t* xT = static_cast<const bf16_t*>(w.xT);
       moe_status st = seg_t(a.dy_sorted, H, w.dysT);
       if (st == MOE_OK) st = seg_t(a.h, I, w.hT);
       if (st == MOE_OK) st = seg_t(dgu, 2 * I, w.dguT);
       if (st == MOE_OK) st = seg_t(a.x_sorted, H, w.xT);
-      if (st == MOE_OK)
-        st = launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, static_cast<const bf16_t*>(w.dysT), H,
-                                       static_cast<const bf16_t*>(w.hT), static_cast<bf16_t*>(a.dw_down), nullptr, H,
-                                       I, 1, a.max_pairs, a.s);
-      if (st == MOE_OK)
-        st = launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, static_cast<const bf16_t*>(w.dguT), 2 * I,
-                                       static_cast<const bf16_t*>(w.xT), static_cast<bf16_t*>(a.dw_gate),
-                                       static_cast<bf16_t*>(a.dw_up), I, H, 2, a.max_pairs, a.s);
+      if (st == MOE_OK) {
+        st = io ? launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, hT, I, dysT, 0,
+                                            static_cast<bf16_t*>(a.dw_down), nullptr, I, H, 1, a.max_pairs, a.s)
+                : launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, dysT, H, hT, 0,
+                                            static_cast<bf16_t*>(a.dw_down), nullptr, H, I, 1, a.max_pairs, a.s);
+      }
+      if (st == MOE_OK) {
+        st = io ? launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, xT, H, dguT, 2 * I,
+                                            static_cast<bf16_t*>(a.dw_gate), static_cast<bf16_t*>(a.dw_up), H, I, 2,
+                                            a.max_pairs, a.s)
+                : launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, dguT, 2 * I, xT, 0,
+                                            static_cast<bf16_t*>(a.dw_gate), static_cast<bf16_t*>(a.dw_up), I, H, 2,
+                                            a.max_pairs, a.s);
+      }
       if (st != MOE_OK) return st;
     }
   }
-  if (!big_w) {  // dWd_e = dy_sorted_e^T h_e  [H, I]
+  if (!big_w) {  // dWd_e = h_e^T dy_sorted_e [I, H] (math form) or dy_sorted_e^T h_e [H, I]
     WgradArgs<T> p{};
-    p.A[0] = static_cast<const T*>(a.dy_sorted);
-    p.lda = H;
-    p.m_load = H;
-    p.B = static_cast<const T*>(a.h);
+    const T* dys = static_cast<const T*>(a.dy_sorted);
+    const T* h = static_cast<const T*>(a.h);
+    p.A[0] = io ? h : dys;
+    p.lda = io ? I : H;
+    p.m_load = io ? I : H;
+    p.B[0] = io ? dys : h;
+    p.ldb = io ? H : I;
     p.C[0] = static_cast<T*>(a.dw_down);
-    p.M = H;
-    p.N = I;
+    p.M = io ? I : H;
+    p.N = io ? H : I;
     p.offsets = a.offsets;
-    const unsigned tiles = unsigned(((H + BM - 1) / BM) * ((I + BN - 1) / BN));
+    const unsigned tiles = unsigned(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
     MOE_LAUNCH("ffn_down_wgrad", wgrad_kernel<T>, dim3(tiles, L, 1), dim3(kThreads), 0, a.s, p);
   }
-  if (!big) {  // dx_sorted = dg Wg_e + du Wu_e
+  if (!big) {  // dx_sorted = dg Wg_e^T + du Wu_e^T, one product over K = 2I
     DgradArgs<T> p{};
     p.A[0] = dgu;
     p.A[1] = dgu + I;
@@ -858,22 +852,40 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
     p.C = static_cast<T*>(a.dx_sorted);
     p.offsets = a.offsets;
     p.L = L;
-    MOE_LAUNCH("ffn_gate_up_dgrad", (dgrad_kernel<T, 0, 2>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0,
-               a.s, p);
+    if (io) {
+      MOE_LAUNCH("ffn_gate_up_dgrad", (dgrad_kernel<T, 0, 2, true>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0,
+                 a.s, p);
+    } else {
+      MOE_LAUNCH("ffn_gate_up_dgrad", (dgrad_kernel<T, 0, 2, false>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads),
+                 0, a.s, p);
+    }
   }
-  if (!big_w) {  // dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e  [I, H]
+  if (!big_w) {  // dWg_e = x_e^T dg_e, dWu_e = x_e^T du_e [H, I] (math form), or dg_e^T x_e, du_e^T x_e [I, H]
     WgradArgs<T> p{};
-    p.A[0] = dgu;
-    p.A[1] = dgu + I;
-    p.lda = 2 * I;
-    p.m_load = I;
-    p.B = static_cast<const T*>(a.x_sorted);
+    const T* xs = static_cast<const T*>(a.x_sorted);
+    if (io) {
+      p.A[0] = p.A[1] = xs;
+      p.lda = H;
+      p.m_load = H;
+      p.B[0] = dgu;
+      p.B[1] = dgu + I;
+      p.ldb = 2 * I;
+      p.M = H;
+      p.N = I;
+    } else {
+      p.A[0] = dgu;
+      p.A[1] = dgu + I;
+      p.lda = 2 * I;
+      p.m_load = I;
+      p.B[0] = xs;
+      p.ldb = H;
+      p.M = I;
+      p.N = H;
+    }
     p.C[0] = static_cast<T*>(a.dw_gate);
     p.C[1] = static_cast<T*>(a.dw_up);
-    p.M = I;
-    p.N = H;
     p.offsets = a.offsets;
-    const unsigned tiles = unsigned(((I + BM - 1) / BM) * ((H + BN - 1) / BN));
+    const unsigned tiles = unsigned(((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN));
     MOE_LAUNCH("ffn_gate_up_wgrad", wgrad_kernel<T>, dim3(tiles, L, 2), dim3(kThreads), 0, a.s, p);
   }
   return MOE_OK;
@@ -902,7 +914,8 @@ moe_status route_bwd_t(const RouteBwdArgs& a) {
   p.A[0] = dlog;
   p.lda = Ep;
   p.m_load = Ep;
-  p.B = static_cast<const T*>(a.x);
+  p.B[0] = static_cast<const T*>(a.x);
+  p.ldb = H;
   p.C[0] = static_cast<T*>(a.dw_router);
   p.M = E;
   p.N = H;

@@ -66,8 +66,11 @@ __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcp
 
 // NMAT = 2: gate and up products with the SwiGLU epilogue; NMAT = 1: plain product.
 // Tiles of BMT (128 or 64) token rows x BN weight rows; the waves split them 2 x 2,
-// so a wave holds BMT/64 x 2 MFMA 32x32 blocks per matrix.
-template <typename T, int NMAT, int BMT>
+// so a wave holds BMT/64 x 2 MFMA 32x32 blocks per matrix.  BKN: the weights are
+// k-major (element (k, n) at B[k * N + n]); thread t then loads k rows 2p and 2p+1
+// (p = t % (BK/2)) of 16-byte column chunk t / (BK/2) and stores them into the
+// [BN][BK] tile as (k, k+1) pairs, so the tile is the one n-major weights give.
+template <typename T, int NMAT, int BMT, bool BKN>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restrict__ A,
                                                                 const int32_t* __restrict__ offsets,
                                                                 const T* __restrict__ B0, const T* __restrict__ B1,
@@ -113,6 +116,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
   const uint4 zero = make_uint4(0, 0, 0, 0);
 
   uint4 ra[CPTA], rb[NMAT][CPTB];
+  constexpr int KP = BK / 2;  // k-major weights: (k, k+1) pairs per tile column
+  static_assert(!BKN || (KP * (BN / EPV) == kThreads && CPTB == 2), "one pair unit per thread");
   auto gload = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < CPTA; ++j) {
@@ -122,16 +127,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
       const int ar = min(r, rows - 1);  // rows past the segment repeat its last row; never stored
       ra[j] = kk < K ? *reinterpret_cast<const uint4*>(A + size_t(row0 + ar) * K + kk) : zero;
     }
+    if constexpr (!BKN) {
 #pragma unroll
-    for (int j = 0; j < CPTB; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / CPR, col = c % CPR;
-      const int kk = k0 + col * EPV;
+      for (int j = 0; j < CPTB; ++j) {
+        const int c = tid + j * kThreads;
+        const int r = c / CPR, col = c % CPR;
+        const int kk = k0 + col * EPV;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const int nr = n0 + r;
-        rb[m][j] = (kk < K && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
+        for (int m = 0; m < NMAT; ++m) {
+          const int nr = n0 + r;
+          rb[m][j] = (kk < K && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
+        }
       }
+    } else {
+      // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
+      const int p = tid % KP, n = n0 + (tid / KP) * EPV, kk = k0 + 2 * p;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          rb[m][h] = (n < N && kk + h < K) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(kk + h) * N + n) : zero;
     }
   };
   auto sstore = [&](int buf) {
@@ -141,12 +156,34 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
       const int r = c / CPR, col = c % CPR;
       *reinterpret_cast<uint4*>(&As[buf][r * kLd + col * EPV]) = ra[j];
     }
+    if constexpr (!BKN) {
 #pragma unroll
-    for (int j = 0; j < CPTB; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / CPR, col = c % CPR;
+      for (int j = 0; j < CPTB; ++j) {
+        const int c = tid + j * kThreads;
+        const int r = c / CPR, col = c % CPR;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) *reinterpret_cast<uint4*>(&Bs[buf][m][r * kLd + col * EPV]) = rb[m][j];
+        for (int m = 0; m < NMAT; ++m) *reinterpret_cast<uint4*>(&Bs[buf][m][r * kLd + col * EPV]) = rb[m][j];
+      }
+    } else {
+      const int p = tid % KP, c0 = (tid / KP) * EPV;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint32_t a[4] = {rb[m][0].x, rb[m][0].y, rb[m][0].z, rb[m][0].w};
+        const uint32_t b[4] = {rb[m][1].x, rb[m][1].y, rb[m][1].z, rb[m][1].w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // column 2w: the low halves of rows k and k+1, column 2w+1: the high halves
+            *reinterpret_cast<uint32_t*>(&Bs[buf][m][(c0 + 2 * w) * kLd + 2 * p]) = (a[w] & 0xFFFFu) | (b[w] << 16);
+            *reinterpret_cast<uint32_t*>(&Bs[buf][m][(c0 + 2 * w + 1) * kLd + 2 * p]) =
+                (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            *reinterpret_cast<uint2*>(&Bs[buf][m][(c0 + w) * kLd + 2 * p]) = make_uint2(a[w], b[w]);
+        }
+      }
     }
   };
 
@@ -265,8 +302,32 @@ namespace big {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
 constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2;
+
+// A weight fragment from a tile stored k-major in LDS (rows of k, n contiguous).
+// gfx950's transposing read ds_read_b64_tr_b16 works on groups of 16 lanes:
+// lane i of a group receives element i % 4 of the 8-byte rows addressed by
+// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its group, in that order (checked
+// on the GPU).  With lane i of a group addressing row kb + i/4, columns
+// nb + 4(i%4) .. +3, lane i receives column nb + i at rows kb .. kb+3; a second
+// read four rows down gives kb+4 .. kb+7, so the lane holds eight consecutive k
+// of one column: the same register contents as the fragment read from an
+// n-major tile.
+__device__ __forceinline__ bf16x8_t read_kn_frag(const char* p) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p + 4 * 256));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The same from the lane's two addresses (rows kb + i/4 and four rows down) of a
+// block with its own row placement.
+__device__ __forceinline__ bf16x8_t read_kn_frag2(const char* p0, const char* p1) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p1));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 constexpr int kRowBytes = BK * 2;              // 128
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
@@ -673,10 +734,17 @@ __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslo
 }
 
 // One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
-template <int NMAT, bool WIDE, int NW, int EP>
+//
+// The weight operand (Bg, and Bu for the up rows of gate/up) is stored one of two ways:
+//   BKN false: n-major, element (n, k) at B[n * kw + k] (a linear layer's [out, in]);
+//   BKN true:  k-major, element (k, n) at B[k * N + n] (the math form's [in, out]).
+// kw is K, or with kcat > 0 (one-matrix products only) 64 * kcat: the k steps from
+// kcat on then read Bu at step - kcat (a product over two matrices side by side
+// along K, such as dg Wg + du Wu).
+template <int NMAT, bool WIDE, int NW, int EP, bool BKN>
 __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
                                           const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
-                                          const Job& jb, float* __restrict__ parts, char* lds,
+                                          int kcat, const Job& jb, float* __restrict__ parts, char* lds,
                                           bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
@@ -700,11 +768,14 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   const uint32_t a_bytes = uint32_t(min(int64_t(a_rows - row0) * K * 2, int64_t(0xFFFFFFFF)));
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(A + size_t(row0) * K), 0, a_bytes, kRsrcFlags);
-  int b_lrow;
-  if (NMAT == 2) b_lrow = ((S::kB / NW) * wave + (lane >> 3)) & (S::kB / 2 - 1);  // first half of the waves: gate rows
-  else b_lrow = (S::kB / NW) * wave + (lane >> 3);
+  // the first half of the waves loads gate rows (or the only matrix), the second half up rows;
+  // b_rsrc2 is the second matrix of a product split along K
+  const int kw = kcat > 0 ? kcat * BK : K;
+  const uint32_t b_bytes = uint32_t(N) * uint32_t(kw) * 2u;
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(NMAT == 2 && wave >= NW / 2 ? Bu : Bg), 0, uint32_t(N) * uint32_t(K) * 2u, kRsrcFlags);
+      const_cast<bf16_t*>(NMAT == 2 && wave >= NW / 2 ? Bu : Bg), 0, b_bytes, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t b_rsrc2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bu), 0, b_bytes,
+                                                                           kRsrcFlags);
   // Rows past the segment (A) or past N (B) feed only outputs that are never
   // stored, so they may read any valid row: A takes the rows that follow (up
   // to the last row of the buffer), B wraps around to the first rows.  Letting
@@ -720,12 +791,33 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     const int cc = (j & 1) ? c_odd : c_even;
     a_vo[j] = (uint32_t(min(a_lrow + 8 * j, a_lim)) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
   }
+  if constexpr (!BKN) {
+    int b_lrow;
+    if (NMAT == 2) b_lrow = ((S::kB / NW) * wave + (lane >> 3)) & (S::kB / 2 - 1);
+    else b_lrow = (S::kB / NW) * wave + (lane >> 3);
 #pragma unroll
-  for (int j = 0; j < S::kLdB; ++j) {
-    const int cc = (j & 1) ? c_odd : c_even;
-    int r = n0 + b_lrow + 8 * j;
-    if (r >= N) r %= N;
-    b_vo[j] = (uint32_t(r) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
+    for (int j = 0; j < S::kLdB; ++j) {
+      const int cc = (j & 1) ? c_odd : c_even;
+      int r = n0 + b_lrow + 8 * j;
+      if (r >= N) r %= N;
+      b_vo[j] = (uint32_t(r) * uint32_t(kw) + uint32_t(cc * 8)) * 2u;
+    }
+  } else {
+    // k-major stage: the tile's B rows in regions of 128 columns (gate regions, then
+    // up regions), each 64 k rows of 256 bytes; 64-byte unit u (32 columns) of k row
+    // r sits at physical unit u ^ (r % 4), so the four rows a transposing read
+    // touches per half wave fall in four different bank groups.  Block j of the wave
+    // (1 KB: four k rows of one region) is global block kLdB*wave + j; its lane l
+    // writes k row 4*(block % 16) + l/16, physical 16-byte chunk l % 16.
+#pragma unroll
+    for (int j = 0; j < S::kLdB; ++j) {
+      const int gb = S::kLdB * wave + j;
+      const int reg = gb >> 4, krow = 4 * (gb & 15) + (lane >> 4);
+      const int u = ((lane & 15) >> 2) ^ ((lane >> 4) & 3);
+      const int col = n0 + 128 * (NMAT == 2 ? reg % (S::kB / 256) : reg) + 32 * u + 8 * (lane & 3);
+      // columns past N read what follows in memory (or zeros past the matrix): never stored
+      b_vo[j] = (uint32_t(krow) * uint32_t(N) + uint32_t(col)) * 2u;
+    }
   }
 // loads q0..q1-1 of stage kt_, in the order A0 B0 A1 B1 ... (then the B rows
 // past the last A block)
@@ -733,13 +825,17 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   do {                                                                                                      \
     char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
     char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
-    const uint32_t k0_ = uint32_t(kb + (kt_)) * (BK * 2);                                                   \
+    const int s_ = kb + (kt_);                                                                              \
+    const uint32_t k0_ = uint32_t(s_) * (BK * 2);                                                           \
+    const bool sec_ = kcat > 0 && s_ >= kcat;                                                               \
+    const uint32_t kbo_ = uint32_t(sec_ ? s_ - kcat : s_) * (BKN ? uint32_t(BK * 2) * uint32_t(N) : uint32_t(BK * 2)); \
     _Pragma("unroll") for (int q = (q0_); q < (q1_); ++q) {                                                 \
       const int j_ = q < 2 * S::kLdA ? q / 2 : q - S::kLdA;                                                 \
       if (q < 2 * S::kLdA && q % 2 == 0)                                                                    \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + j_ * 1024), 16, a_vo[j_], k0_, 0, 0); \
       else                                                                                                  \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(sb_ + j_ * 1024), 16, b_vo[j_], k0_, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sec_ ? b_rsrc2 : b_rsrc, (lds_ptr_t)(sb_ + j_ * 1024), 16, b_vo[j_], \
+                                                 kbo_, 0, 0);                                              \
     }                                                                                                       \
   } while (0)
 
@@ -762,7 +858,15 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   for (int j = 0; j < NB; ++j) {
     const int br = NMAT == 2 ? (j < NB / 2 ? wn * NB * 16 + j * 32 : S::kB / 2 + wn * NB * 16 + (j - NB / 2) * 32)
                              : wn * NB * 32 + j * 32;
-    boffs[j] = S::kStageA + (br + fr) * kRowBytes;
+    if constexpr (!BKN) {
+      boffs[j] = S::kStageA + (br + fr) * kRowBytes;
+    } else {
+      // 32-column block br: region br / 128, unit (br % 128) / 32; lane group G = lane / 16
+      // reads k rows 8 (G / 2) + i / 4 (i = lane % 16) and columns 16 (G % 2) + 4 (i % 4)
+      const int G = lane >> 4, i = lane & 15, u = (br & 127) >> 5;
+      boffs[j] = S::kStageA + (br >> 7) * 16384 + (8 * (G >> 1) + (i >> 2)) * 256 + 64 * (u ^ (i >> 2)) +
+                 32 * (G & 1) + 8 * (i & 3);
+    }
   }
   const int a_off = (wm * 128 + fr) * kRowBytes;
   bf16x8_t fa[2][4], fb[2][NB];
@@ -772,7 +876,8 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
       fa[buf_][i] = *reinterpret_cast<const bf16x8_t*>((st_) + a_off + i * 32 * kRowBytes + co_);          \
     _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                        \
-      fb[buf_][j] = *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                            \
+      fb[buf_][j] = BKN ? read_kn_frag((st_) + boffs[j] + (kc_) * 16 * 256)                                \
+                        : *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                      \
   } while (0)
 #define MOE_MMA(buf_)                                                                                     \
   do {                                                                                                    \
@@ -780,21 +885,25 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                      \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][i], acc[i][j], 0, 0, 0); \
   } while (0)
-  // 8 x {MFMA, LDS read, MFMA}: the next chunk's fragment reads spread over the whole group
+  // LDS reads per chunk (a k-major B fragment takes two transposing reads) and MFMAs per chunk
+  constexpr int kDs = 4 + NB * (BKN ? 2 : 1), kMf = 4 * NB;
+  // {MFMA, LDS read, MFMA} (or {MFMA, LDS read} when the reads outnumber half the
+  // MFMAs): the next chunk's fragment reads spread over the whole group
 #define MOE_PIPE_DS()                                                                                     \
   do {                                                                                                    \
-    if constexpr (NB == 4) {                                                                              \
-      _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                  \
+    if constexpr (kMf >= 2 * kDs) {                                                                       \
+      _Pragma("unroll") for (int p_ = 0; p_ < kDs; ++p_) {                                                \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
       }                                                                                                   \
+      if constexpr (kMf > 2 * kDs) __builtin_amdgcn_sched_group_barrier(0x008, kMf - 2 * kDs, 0);         \
     } else {                                                                                              \
-      _Pragma("unroll") for (int p_ = 0; p_ < 4 + NB; ++p_) {                                             \
+      _Pragma("unroll") for (int p_ = 0; p_ < kDs; ++p_) {                                                \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
       }                                                                                                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NB - (4 + NB), 0);                                  \
+      if constexpr (kMf > kDs) __builtin_amdgcn_sched_group_barrier(0x008, kMf - kDs, 0);                 \
     }                                                                                                     \
   } while (0)
 
@@ -809,7 +918,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   // spread over its 4 * NB MFMAs
 #define MOE_CHUNK_LOADS()                                                                                 \
   do {                                                                                                    \
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NB, 0);                                               \
+    __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);                                                  \
     if constexpr (NB == 4) {                                                                              \
       _Pragma("unroll") for (int p_ = 0; p_ < 8; ++p_) {                                                  \
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                \
@@ -898,15 +1007,17 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
 // length rounded up to 64 (at least 64; the padding is zero), at element offset
 // rows * Q_e (Q_e = sum of K_e' over e' < e), so each expert's product has
 // the forward's operand layout with its own K.  In gemm_kernel's kWgrad mode:
-// blockIdx x = tile (m major), y = expert, z = which of up to two (A, C) pairs
-// (A rows [z M, (z+1) M)); A = the transposed blocks (a_rows of them per
-// expert), B0 = B's blocks, C and Gs = the two outputs, K = M.
+// blockIdx x = tile (m major), y = expert, z = which of up to two outputs (C, Gs);
+// A = the transposed blocks (a_rows of them per expert), B0 = B's blocks, K = M;
+// kcat = 0: output z takes A rows [z M, (z+1) M); kcat > 0: B's blocks have kcat
+// rows per expert and output z takes B rows [z N, (z+1) N).
 __device__ __forceinline__ int wgrad_k(int n) { return n <= 64 ? 64 : (n + 63) / 64 * 64; }
 
-template <int NMAT, int NW, int EP>
+// BKN, kcat: the weight operand's layout and K split (see tile_body)
+template <int NMAT, int NW, int EP, bool BKN>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                       bf16_t* __restrict__ C, int L, int N, int K, int a_rows,
+                                                       bf16_t* __restrict__ C, int L, int N, int K, int kcat, int a_rows,
                                                         const int32_t* __restrict__ tpre, int cpx, int smax,
                                                         float* __restrict__ parts, bf16_t* __restrict__ Gs,
                                                         bf16_t* __restrict__ Us) {
@@ -928,12 +1039,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
     jb.part = 0;
     jb.nparts = 1;
     jb.pslot = 0;
-    const bf16_t* Ae = A + q * a_rows + size_t(z) * M * Ke;
-    const bf16_t* Be = B0 + q * N;
+    const bool zb = kcat > 0;
+    const bf16_t* Ae = A + q * a_rows + (zb ? 0 : size_t(z) * M * Ke);
+    const bf16_t* Be = B0 + q * (zb ? kcat : N) + (zb ? size_t(z) * N * Ke : 0);
     bf16_t* Ce = (z ? Gs : C) + size_t(e) * M * N;
     // (EP, not kPlain, as the template argument: hipcc's host pass rejects the literal
     // here; the epilogue treats kWgrad as kPlain)
-    tile_body<NMAT, false, NW, EP>(Ae, M, Be, Be, Ce, N, Ke, jb, parts, lds, Us, Us);
+    tile_body<NMAT, false, NW, EP, false>(Ae, M, Be, Be, Ce, N, Ke, 0, jb, parts, lds, Us, Us);
     return;
   }
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
@@ -950,13 +1062,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
   Job jb;
   unit_job(offsets, spre, L, NT, nk, cpx, xcd, xp, loc, jb);
   __syncthreads();  // every wave has its job before the first loads land in the LDS
-  const size_t boff = size_t(jb.expert) * N * K;
+  const size_t boff = size_t(jb.expert) * N * (kcat > 0 ? kcat * BK : K);
   const bf16_t* Bg = B0 + boff;
-  const bf16_t* Bu = (NMAT == 2 ? B1 : B0) + boff;
+  const bf16_t* Bu = (NMAT == 2 || kcat > 0 ? B1 : B0) + boff;
   if (jb.wide)
-    tile_body<NMAT, true, NW, EP>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, true, NW, EP, BKN>(A, a_rows, Bg, Bu, C, N, K, kcat, jb, parts, lds, Gs, Us);
   else
-    tile_body<NMAT, false, NW, EP>(A, a_rows, Bg, Bu, C, N, K, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, false, NW, EP, BKN>(A, a_rows, Bg, Bu, C, N, K, kcat, jb, parts, lds, Gs, Us);
 }
 
 
@@ -1049,32 +1161,35 @@ bool splits(int K) { return K / BK >= kSplitMinSteps; }
 // skewed layer -1.5%); four for longer ones (mixtral-like layer: eight are 1% slower).
 constexpr int kEightWaveSteps = 64;
 
-template <int NMAT, int NW, int EP>
+template <int NMAT, int NW, int EP, bool BKN>
 moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                      bf16_t* C, int L, int N, int K, int kcat, int64_t max_pairs, const int32_t* tpre, float* parts,
                       hipStream_t s, bf16_t* Gs, bf16_t* Us);
 
 template <int NMAT, int NW>
 moe_status launch_nw(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                     bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                     hipStream_t s, bf16_t* Gs, bf16_t* Us, int ep) {
+                     bf16_t* C, int L, int N, int K, int kcat, bool bkn, int64_t max_pairs, const int32_t* tpre,
+                     float* parts, hipStream_t s, bf16_t* Gs, bf16_t* Us, int ep) {
+#define MOE_NWS(EP_, PARTS_)                                                                                      \
+  (bkn ? launch_nws<NMAT, NW, EP_, true>(name, A, offsets, B0, B1, C, L, N, K, kcat, max_pairs, tpre, PARTS_, s, Gs, Us) \
+       : launch_nws<NMAT, NW, EP_, false>(name, A, offsets, B0, B1, C, L, N, K, kcat, max_pairs, tpre, PARTS_, s, Gs, Us))
   if constexpr (NMAT == 2) {
-    if (ep == kSave) return launch_nws<NMAT, NW, kSave>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+    if (ep == kSave) return MOE_NWS(kSave, parts);
   } else {
-    if (ep == kSwigluBwd)
-      return launch_nws<NMAT, NW, kSwigluBwd>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, nullptr, s, Gs, Us);
+    if (ep == kSwigluBwd) return MOE_NWS(kSwigluBwd, nullptr);
   }
-  return launch_nws<NMAT, NW, kPlain>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us);
+  return MOE_NWS(kPlain, parts);
+#undef MOE_NWS
 }
 
 // EP: the epilogue (kSave: the training forward's gate/up, which also writes the
 // pre-activations; kSwigluBwd: the backward's down dgrad, never split along K)
-template <int NMAT, int NW, int EP>
+template <int NMAT, int NW, int EP, bool BKN>
 moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                      bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
+                      bf16_t* C, int L, int N, int K, int kcat, int64_t max_pairs, const int32_t* tpre, float* parts,
                       hipStream_t s, bf16_t* Gs, bf16_t* Us) {
   constexpr int kThreads = NW * 64;
-  auto kern = gemm_kernel<NMAT, NW, EP>;
+  auto kern = gemm_kernel<NMAT, NW, EP, BKN>;
   constexpr size_t lds = lds_bytes<NMAT>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
@@ -1087,7 +1202,7 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
   const int64_t tiles = ((max_pairs + BM - 1) / BM + L) * ((N + ON - 1) / ON);
   const int64_t per_xcd = (tiles + kXcds - 1) / kXcds + (smax > 1 ? kMaxParts - kMaxTail : 0);
   // A holds max_pairs rows (the caller's x_sorted or h)
-  MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K,
+  MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K, kcat,
              int(max_pairs), tpre, cpx, smax, parts, Gs, Us);
   if (smax > 1) {
     const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
@@ -1099,27 +1214,29 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
 
 template <int NW>
 moe_status launch_wgrad_nw(const char* name, const moe_layer_desc* d, const int32_t* offsets, const bf16_t* At,
-                           int a_rows_total, const bf16_t* Bt, bf16_t* C0, bf16_t* C1, int M, int N, int Z,
-                           hipStream_t s) {
-  auto kern = gemm_kernel<1, NW, kWgrad>;
+                           int a_rows_total, const bf16_t* Bt, int b_rows_total, bf16_t* C0, bf16_t* C1, int M, int N,
+                           int Z, hipStream_t s) {
+  auto kern = gemm_kernel<1, NW, kWgrad, false>;
   constexpr size_t lds = lds_bytes<1>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
   const unsigned tiles = unsigned(((M + BM - 1) / BM) * ((N + BNE - 1) / BNE));
   MOE_LAUNCH(name, kern, dim3(tiles, unsigned(d->local_count), unsigned(Z)), dim3(NW * 64), lds, s, At, offsets, Bt,
-             Bt, C0, d->local_count, N, M, a_rows_total, static_cast<const int32_t*>(nullptr), 0, 1,
+             Bt, C0, d->local_count, N, M, b_rows_total, a_rows_total, static_cast<const int32_t*>(nullptr), 0, 1,
              static_cast<float*>(nullptr), C1, static_cast<bf16_t*>(nullptr));
   return MOE_OK;
 }
 
+// bkn: the weight operand is k-major (element (k, n) at B[k * N + n]); kcat > 0: a
+// one-matrix product over B0 for the first 64 * kcat of K, then B1 (see tile_body)
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, int64_t max_pairs, const int32_t* tpre, float* parts,
-                  hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr, int ep = kPlain) {
+                  bf16_t* C, int L, int N, int K, int kcat, bool bkn, int64_t max_pairs, const int32_t* tpre,
+                  float* parts, hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr, int ep = kPlain) {
   if (K / BK < kEightWaveSteps)
-    return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us, ep);
-  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, max_pairs, tpre, parts, s, Gs, Us, ep);
+    return launch_nw<NMAT, 8>(name, A, offsets, B0, B1, C, L, N, K, kcat, bkn, max_pairs, tpre, parts, s, Gs, Us, ep);
+  return launch_nw<NMAT, 4>(name, A, offsets, B0, B1, C, L, N, K, kcat, bkn, max_pairs, tpre, parts, s, Gs, Us, ep);
 }
 
 }  // namespace big
@@ -1151,12 +1268,17 @@ template <int NMAT>
 constexpr int cols_per_block() { return NMAT == 2 ? 64 : 128; }
 
 // SAVE (gate/up of the training forward): the gate and up pre-activations go to Gs, Us too.
-template <int NMAT, bool SAVE>
+// BKN: the weights are k-major (element (k, n) at B[k * N + n]): each lane then loads
+// 16 bytes of one k row (a 32 x 16 block of a stream per step is 32 rows of 32 bytes),
+// the wave parks the block in its own 1 KB of LDS and reads the fragments back with
+// transposing reads, so the MFMAs see the same operands as with n-major weights.
+template <int NMAT, bool SAVE, bool BKN>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                         const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                         bf16_t* __restrict__ C, int N, int K, bf16_t* __restrict__ Gs,
                                                         bf16_t* __restrict__ Us) {
   constexpr int kWaveCols = NMAT == 2 ? 16 : 32;
+  constexpr int kPipe = 4;
   const int expert = blockIdx.y;
   const int seg0 = offsets[expert];
   const int seg_n = offsets[expert + 1] - seg0;
@@ -1166,11 +1288,35 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   if (col0 >= N) return;
   const size_t boff = size_t(expert) * N * K;
   const int kg = (lane >> 4) * 8;  // the lane's 8 k values within a step
-  // stream 0 / 1 weight row of this lane (rows past N repeat row N-1; never stored)
-  const int wrow0 = min(col0 + (lane & 15), N - 1);
-  const int wrow1 = NMAT == 2 ? wrow0 : min(col0 + 16 + (lane & 15), N - 1);
-  const bf16_t* bs0 = B0 + boff + size_t(wrow0) * K + kg;
-  const bf16_t* bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow1) * K + kg;
+  const bf16_t* bs0;
+  const bf16_t* bs1;
+  size_t kstride;  // elements between consecutive k of a lane's stream
+  if constexpr (!BKN) {
+    // stream 0 / 1 weight row of this lane (rows past N repeat row N-1; never stored)
+    const int wrow0 = min(col0 + (lane & 15), N - 1);
+    const int wrow1 = NMAT == 2 ? wrow0 : min(col0 + 16 + (lane & 15), N - 1);
+    bs0 = B0 + boff + size_t(wrow0) * K + kg;
+    bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow1) * K + kg;
+    kstride = 1;
+  } else {
+    // lane l loads k row l/2 of the step, columns c + 8 (l % 2) .. +7 of its stream's 16
+    // (chunks past N re-read the last chunk of the row; never stored)
+    const int c0 = min(col0 + 8 * (lane & 1), N - 8);
+    const int c1 = NMAT == 2 ? c0 : min(col0 + 16 + 8 * (lane & 1), N - 8);
+    bs0 = B0 + boff + size_t(lane >> 1) * N + c0;
+    bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(lane >> 1) * N + c1;
+    kstride = size_t(N);
+  }
+  // the wave's LDS blocks (k-major weights only): [stream][step] 1 KB each; row r of a
+  // block at 32-byte slot r ^ 4 (r / 8 % 2), so a transposing read's two row quads per
+  // half wave fall in different bank halves
+  __shared__ __attribute__((aligned(1024))) char park[BKN ? 4 * 2 * kPipe * 1024 : 16];
+  char* wpark = park + (BKN ? wave * 2 * kPipe * 1024 : 0);
+  auto slot = [](int r) { return (r ^ (((r >> 3) & 1) << 2)) * 32; };
+  const int woff = slot(lane >> 1) + 16 * (lane & 1);  // this lane's store
+  // its transposing reads: k rows 8 (lane / 16) + (lane % 16) / 4 and four rows down
+  const int roff0 = slot(8 * (lane >> 4) + ((lane & 15) >> 2)) + 8 * (lane & 3);
+  const int roff1 = slot(8 * (lane >> 4) + ((lane & 15) >> 2) + 4) + 8 * (lane & 3);
 
   for (int m0 = 0; m0 < seg_n; m0 += 16 * kMaxRowBlocks) {
     const int nrb = min(kMaxRowBlocks, (seg_n - m0 + 15) / 16);
@@ -1190,18 +1336,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     // fit, but each keeps more in flight; same-box A/B on the decode-sized
     // layer: 0 to -4% per layer against two steps, while capping registers for
     // more waves per SIMD made it 12% slower)
-    constexpr int kPipe = 4;
     bf16x8_t w0[2][kPipe], w1[2][kPipe], a0[2][kPipe];
     const int nset = K / (32 * kPipe);
     auto load_set = [&](int b, int k0) {
 #pragma unroll
       for (int u = 0; u < kPipe; ++u) {
-        w0[b][u] = *reinterpret_cast<const bf16x8_t*>(bs0 + k0 + 32 * u);
-        w1[b][u] = *reinterpret_cast<const bf16x8_t*>(bs1 + k0 + 32 * u);
+        w0[b][u] = *reinterpret_cast<const bf16x8_t*>(bs0 + size_t(k0 + 32 * u) * kstride);
+        w1[b][u] = *reinterpret_cast<const bf16x8_t*>(bs1 + size_t(k0 + 32 * u) * kstride);
         a0[b][u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);
       }
     };
+    // k-major weights: park the loaded blocks, then read the fragments back transposed
+    auto transpose_set = [&](int b) {
+      if constexpr (BKN) {
+#pragma unroll
+        for (int u = 0; u < kPipe; ++u) {
+          *reinterpret_cast<bf16x8_t*>(wpark + u * 1024 + woff) = w0[b][u];
+          *reinterpret_cast<bf16x8_t*>(wpark + (kPipe + u) * 1024 + woff) = w1[b][u];
+        }
+#pragma unroll
+        for (int u = 0; u < kPipe; ++u) {
+          w0[b][u] = big::read_kn_frag2(wpark + u * 1024 + roff0, wpark + u * 1024 + roff1);
+          w1[b][u] = big::read_kn_frag2(wpark + (kPipe + u) * 1024 + roff0, wpark + (kPipe + u) * 1024 + roff1);
+        }
+      }
+    };
     auto mma_set = [&](int b, int k0) {
+      transpose_set(b);
 #pragma unroll
       for (int u = 0; u < kPipe; ++u) {
 #pragma unroll
@@ -1225,14 +1386,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
     if (set < nset) mma_set(0, set * 32 * kPipe);
     int k0 = nset * 32 * kPipe;
     for (; k0 < K; k0 += 32) {
-      const bf16x8_t w0 = *reinterpret_cast<const bf16x8_t*>(bs0 + k0);
-      const bf16x8_t w1 = *reinterpret_cast<const bf16x8_t*>(bs1 + k0);
+      bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(bs0 + size_t(k0) * kstride);
+      bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(bs1 + size_t(k0) * kstride);
+      if constexpr (BKN) {
+        *reinterpret_cast<bf16x8_t*>(wpark + woff) = v0;
+        *reinterpret_cast<bf16x8_t*>(wpark + kPipe * 1024 + woff) = v1;
+        v0 = big::read_kn_frag2(wpark + roff0, wpark + roff1);
+        v1 = big::read_kn_frag2(wpark + kPipe * 1024 + roff0, wpark + kPipe * 1024 + roff1);
+      }
 #pragma unroll
       for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
         if (rb < nrb) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0);
-          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0, acc[0][rb], 0, 0, 0);
-          acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1, acc[1][rb], 0, 0, 0);
+          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, v0, acc[0][rb], 0, 0, 0);
+          acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, v1, acc[1][rb], 0, 0, 0);
         }
       }
     }
@@ -1267,33 +1434,48 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict
   }
 }
 
+// bkn: k-major weights (see gemm_kernel)
 template <int NMAT>
 moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
+                  bf16_t* C, int L, int N, int K, bool bkn, hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
   const dim3 grid(unsigned((N + cols_per_block<NMAT>() - 1) / cols_per_block<NMAT>()), unsigned(L));
+#define MOE_SKINNY(SAVE_)                                                                                          \
+  do {                                                                                                             \
+    if (bkn)                                                                                                       \
+      MOE_LAUNCH(name, (gemm_kernel<NMAT, SAVE_, true>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us); \
+    else                                                                                                           \
+      MOE_LAUNCH(name, (gemm_kernel<NMAT, SAVE_, false>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us); \
+  } while (0)
   if (NMAT == 2 && Gs != nullptr) {
-    MOE_LAUNCH(name, (gemm_kernel<NMAT, true>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us);
+    MOE_SKINNY(true);
   } else {
-    MOE_LAUNCH(name, (gemm_kernel<NMAT, false>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us);
+    MOE_SKINNY(false);
   }
+#undef MOE_SKINNY
   return MOE_OK;
 }
 
 }  // namespace skinny
 
-template <typename T, int BMT>
+template <typename T, int BMT, bool BKN>
 moe_status launch_bm(const FfnArgs& a) {
   const moe_layer_desc* d = a.d;
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
   const unsigned mslots = unsigned((a.max_pairs + BMT - 1) / BMT + L);
-  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2, BMT>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
+  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2, BMT, BKN>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
              a.s, static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
              static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H, static_cast<T*>(a.g_out),
              static_cast<T*>(a.u_out));
-  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1, BMT>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0, a.s,
-             static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down), static_cast<const T*>(a.w_down),
-             static_cast<T*>(a.y_sorted), L, H, I, static_cast<T*>(nullptr), static_cast<T*>(nullptr));
+  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1, BMT, BKN>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0,
+             a.s, static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down),
+             static_cast<const T*>(a.w_down), static_cast<T*>(a.y_sorted), L, H, I, static_cast<T*>(nullptr),
+             static_cast<T*>(nullptr));
   return MOE_OK;
+}
+
+template <typename T, int BMT>
+moe_status launch_bm(const FfnArgs& a) {
+  return a.d->weight_layout == MOE_WEIGHTS_IN_OUT ? launch_bm<T, BMT, true>(a) : launch_bm<T, BMT, false>(a);
 }
 
 // 64-row tiles when 128-row tiles would leave fewer than two blocks per CU (the
@@ -1319,12 +1501,13 @@ moe_status launch_small(const FfnArgs& a) {
   // decode-sized batches: a few rows per expert, bound by streaming the weights
   if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I)) {
     bf16_t* h = static_cast<bf16_t*>(a.h);
+    const bool kn = d->weight_layout == MOE_WEIGHTS_IN_OUT;
     moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
                                       static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
-                                      H, a.s, static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
+                                      H, kn, a.s, static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
     if (st != MOE_OK) return st;
     return skinny::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
-                             static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.s);
+                             static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, kn, a.s);
   }
   return d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
@@ -1339,11 +1522,11 @@ size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs) {
 }
 
 // ---- the backward's dgrad products on the large-tile kernel ---------------------
-// With the expert weights transposed to [N, K] rows (wdT [L, I, H]; wguT [L, H, 2I],
-// the gate's transpose then the up's), both dgrad products have the forward's
-// operand layout: dh = dy_sorted wdT_e^T with the SwiGLU backward in the epilogue
-// (writing dg | du as [P, 2I]), then dx_sorted = [dg | du] wguT_e^T, one product
-// over K = 2I.
+// dh = dy_sorted Wd^T (math form: Wd_e is [I, H]) with the SwiGLU backward in the
+// epilogue (writing dg | du as [P, 2I]), then dx_sorted = [dg | du] [Wg_e | Wu_e]^T, one
+// product over K = 2I whose first I read Wg_e and the rest Wu_e.  Each weight is read
+// in place: the math-form layout gives these products n-major operands (Wd_e rows are
+// the I outputs, Wg_e rows the H outputs), the linear layout k-major ones.
 bool big_backward_supported(const moe_layer_desc* d, int64_t max_pairs) {
   return use_big(d, max_pairs) && big::supported(2 * d->intermediate) &&
          big::addressable(d->hidden, 2 * int64_t(d->intermediate));
@@ -1355,21 +1538,22 @@ size_t big_backward_scratch_bytes(const moe_layer_desc* d) {
 }
 
 moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const bf16_t* dy_sorted, const int32_t* offsets,
-                                     const bf16_t* wdT, const bf16_t* gate, const bf16_t* up, bf16_t* dgu,
-                                     const bf16_t* wguT, bf16_t* dx_sorted, int64_t max_pairs, void* scratch,
-                                     hipStream_t s) {
+                                     const bf16_t* w_down, const bf16_t* w_gate, const bf16_t* w_up,
+                                     const bf16_t* gate, const bf16_t* up, bf16_t* dgu, bf16_t* dx_sorted,
+                                     int64_t max_pairs, void* scratch, hipStream_t s) {
   const int L = d->local_count, H = d->hidden, I = d->intermediate;
+  const bool kn = d->weight_layout != MOE_WEIGHTS_IN_OUT;
   int32_t* pre = static_cast<int32_t*>(scratch);
   float* parts = big::splits(2 * I) ? reinterpret_cast<float*>(static_cast<char*>(scratch) +
                                                                align_up(size_t(2) * (L + 1) * sizeof(int32_t), 256))
                                     : nullptr;
   MOE_LAUNCH("ffn_bwd_plan", big::plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L, (I + big::BNE - 1) / big::BNE,
              (H + big::BNE - 1) / big::BNE, pre);
-  moe_status st = big::launch<1>("ffn_down_dgrad", dy_sorted, offsets, wdT, wdT, dgu, L, I, H, max_pairs, pre, nullptr,
-                                 s, const_cast<bf16_t*>(gate), const_cast<bf16_t*>(up), big::kSwigluBwd);
+  moe_status st = big::launch<1>("ffn_down_dgrad", dy_sorted, offsets, w_down, w_down, dgu, L, I, H, 0, kn, max_pairs,
+                                 pre, nullptr, s, const_cast<bf16_t*>(gate), const_cast<bf16_t*>(up), big::kSwigluBwd);
   if (st != MOE_OK) return st;
-  return big::launch<1>("ffn_gate_up_dgrad", dgu, offsets, wguT, wguT, dx_sorted, L, H, 2 * I, max_pairs, pre + L + 1,
-                        parts, s);
+  return big::launch<1>("ffn_gate_up_dgrad", dgu, offsets, w_gate, w_up, dx_sorted, L, H, 2 * I, I / big::BK, kn,
+                        max_pairs, pre + L + 1, parts, s);
 }
 
 bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs) {
@@ -1378,13 +1562,13 @@ bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs) {
 }
 
 moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
-                                     const bf16_t* At, int a_rows_total, const bf16_t* Bt, bf16_t* C0, bf16_t* C1,
-                                     int M, int N, int Z, int64_t max_pairs, hipStream_t s) {
+                                     const bf16_t* At, int a_rows_total, const bf16_t* Bt, int b_rows_total,
+                                     bf16_t* C0, bf16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s) {
   // eight waves when the average segment is under 64 k steps, as for the forward
   const int64_t avg = max_pairs / std::max(1, d->local_count);
   if (avg / big::BK < big::kEightWaveSteps)
-    return big::launch_wgrad_nw<8>(name, d, offsets, At, a_rows_total, Bt, C0, C1, M, N, Z, s);
-  return big::launch_wgrad_nw<4>(name, d, offsets, At, a_rows_total, Bt, C0, C1, M, N, Z, s);
+    return big::launch_wgrad_nw<8>(name, d, offsets, At, a_rows_total, Bt, b_rows_total, C0, C1, M, N, Z, s);
+  return big::launch_wgrad_nw<4>(name, d, offsets, At, a_rows_total, Bt, b_rows_total, C0, C1, M, N, Z, s);
 }
 
 moe_status launch_grouped_ffn(const FfnArgs& a) {
@@ -1402,14 +1586,16 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
                      : nullptr;
   MOE_LAUNCH("ffn_plan", big::plan_kernel, dim3(1), dim3(1024), 0, a.s, a.offsets, L, (I + big::BNE / 2 - 1) / (big::BNE / 2),
              (H + big::BNE - 1) / big::BNE, pre);
+  // the math-form layout stores the weights k-major
+  const bool kn = d->weight_layout == MOE_WEIGHTS_IN_OUT;
   moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
-                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, a.max_pairs, pre, parts, a.s,
+                                 static_cast<const bf16_t*>(a.w_up), h, L, I, H, 0, kn, a.max_pairs, pre, parts, a.s,
                                  static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out),
                                  a.g_out != nullptr ? big::kSave : big::kPlain);
   if (st != MOE_OK) return st;
   return big::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
-                        static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, a.max_pairs,
-                        pre + L + 1, parts, a.s);
+                        static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, 0, kn,
+                        a.max_pairs, pre + L + 1, parts, a.s);
 }
 
 }  // namespace moe

@@ -153,14 +153,16 @@ moe_status launch_grouped_ffn_backward(const FfnBwdArgs& a);
 bool big_backward_supported(const moe_layer_desc* d, int64_t max_pairs);
 size_t big_backward_scratch_bytes(const moe_layer_desc* d);
 moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const uint16_t* dy_sorted, const int32_t* offsets,
-                                     const uint16_t* wdT, const uint16_t* gate, const uint16_t* up, uint16_t* dgu,
-                                     const uint16_t* wguT, uint16_t* dx_sorted, int64_t max_pairs, void* scratch,
-                                     hipStream_t s);
+                                     const uint16_t* w_down, const uint16_t* w_gate, const uint16_t* w_up,
+                                     const uint16_t* gate, const uint16_t* up, uint16_t* dgu, uint16_t* dx_sorted,
+                                     int64_t max_pairs, void* scratch, hipStream_t s);
 // dW on the large tile from per-expert transposed blocks (see grouped_gemm.hip)
 bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs);
+// Z outputs; b_rows_total = 0: output z takes A rows [zM, (z+1)M), else B's blocks have
+// b_rows_total rows and output z takes B rows [zN, (z+1)N)
 moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
-                                     const uint16_t* At, int a_rows_total, const uint16_t* Bt, uint16_t* C0,
-                                     uint16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s);
+                                     const uint16_t* At, int a_rows_total, const uint16_t* Bt, int b_rows_total,
+                                     uint16_t* C0, uint16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s);
 
 struct RouteBwdScratch {
   void* dlogits;     // [T, Ep] in the layer's type (Ep = E rounded up to 8)

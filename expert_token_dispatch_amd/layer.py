@@ -158,9 +158,10 @@ class MoELayer:
             "dx": self._empty((max(T, 1), H), x_dtype),
             "dw_router": self._empty((E, H), x_dtype),
             "db_router": self._empty((E,), torch.float32) if self.b_router is not None else None,
-            "dw_gate": self._empty((Lc, I, H), x_dtype),
-            "dw_up": self._empty((Lc, I, H), x_dtype),
-            "dw_down": self._empty((Lc, H, I), x_dtype),
+            # the weight gradients take the weights' layout
+            "dw_gate": self._empty(tuple(self.w_gate.shape), x_dtype),
+            "dw_up": self._empty(tuple(self.w_up.shape), x_dtype),
+            "dw_down": self._empty(tuple(self.w_down.shape), x_dtype),
         }
 
     def backward(self, x, saved, dy, grads=None) -> dict:

@@ -25,10 +25,18 @@
  *  - Activations and weights share one element type, desc->dtype: MOE_BF16
  *    (bfloat16 storage, float32 accumulation) or MOE_F32.  Router bias,
  *    logits and routing weights are always float32; ids and rows int32.
- *  - Weights are stored as a linear layer stores them, [out, in]:
- *      router  w_router [E, H]
- *      experts w_gate [L, I, H], w_up [L, I, H], w_down [L, H, I]
- *    so expert e computes y = (silu(v Wg_e^T) * (v Wu_e^T)) Wd_e^T.
+ *  - The router weight is stored as a linear layer stores it, [out, in]:
+ *    w_router [E, H].  The expert weights are stacked along the expert
+ *    dimension (Transformers "Expert parallelism": the grouped_gemm style
+ *    splits them along that dimension) in one of two layouts, chosen by
+ *    desc->weight_layout:
+ *      MOE_WEIGHTS_OUT_IN (0)  w_gate, w_up [L, I, H], w_down [L, H, I]
+ *                              (each matrix [out, in], as a linear layer
+ *                              stores it): y = (silu(v Wg^T) * (v Wu^T)) Wd^T
+ *      MOE_WEIGHTS_IN_OUT (1)  w_gate, w_up [L, H, I], w_down [L, I, H]
+ *                              (the math form):  y = (silu(v Wg) * (v Wu)) Wd
+ *    Both describe the same layer; the weight gradients of the backward take
+ *    the layout of the weights.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and runs asynchronously; no call synchronises or copies device data to
  *    the host.  Device-side data produced by an earlier call (ids, offsets,
@@ -59,6 +67,9 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Layout of the stacked expert weights (see the conventions above). */
+typedef enum { MOE_WEIGHTS_OUT_IN = 0, MOE_WEIGHTS_IN_OUT = 1 } moe_weight_layout;
+
 /* Problem statement of one layer on one GPU.
  *   num_tokens       T >= 0 tokens held by this GPU (T == 0: every call is a
  *                    successful no-op).
@@ -75,6 +86,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *                    capacity"); the pairs with the largest router logit are
  *                    kept, ties to the lower token index.
  *   dtype            a moe_dtype value.
+ *   weight_layout    a moe_weight_layout value (0, the zero-initialised
+ *                    default, is MOE_WEIGHTS_OUT_IN).
  */
 typedef struct {
   int64_t num_tokens;
@@ -86,6 +99,7 @@ typedef struct {
   int32_t local_count;
   float capacity_factor;
   int32_t dtype;
+  int32_t weight_layout;
 } moe_layer_desc;
 
 /* Stages whose workspace size can be queried. */
@@ -259,13 +273,15 @@ moe_status moe_dispatch_noalloc(const moe_layer_desc* d, const void* x, const in
 /* Stage 3: local experts as one grouped GEMM.  Glossary, step 3: each GPU  */
 /* runs its local experts on the tokens it received; Transformers names the */
 /* expert kernel style "grouped_gemm".  Segment i of x_sorted goes through  */
-/* expert local_begin + i:  y = (silu(x Wg^T) * (x Wu^T)) Wd^T, with        */
+/* expert local_begin + i:  y = (silu(x Wg) * (x Wu)) Wd (in the math     */
+/* form; see the weight layouts above), with                               */
 /* silu(z) = z / (1 + exp(-z)), float32 accumulation, the gate/up product   */
 /* rounded to dtype once.  Offsets are read on the device (no host sync).   */
 /* ------------------------------------------------------------------------ */
 /*   x_sorted  device [P_max, H] dtype
  *   offsets   device [L+1] int32 (from moe_dispatch)
- *   w_gate    device [L, I, H] dtype;  w_up [L, I, H];  w_down [L, H, I]
+ *   w_gate, w_up  device dtype, [L, I, H] (MOE_WEIGHTS_OUT_IN) or [L, H, I]
+ *                 (MOE_WEIGHTS_IN_OUT);  w_down [L, H, I] or [L, I, H]
  *   y_sorted  device [P_max, H] dtype out (rows >= P untouched)
  *   ws        device workspace of MOE_STAGE_FFN bytes: h [P_max, I], and on
  *             the large-tile path its tile plan and (K >= 2048) the float32
@@ -367,15 +383,17 @@ moe_status moe_combine_backward(const moe_layer_desc* d, const void* dy, const v
                                 const int32_t* pair_row, const float* topk_w, void* dy_sorted, float* dl,
                                 void* stream);
 
-/* The local experts' backward.  Per expert e with rows [o_e, o_{e+1}):
- *   dh = dy_sorted Wd_e;  dg = dh * up * silu'(gate);  du = dh * silu(gate)
- *   dx_sorted = dg Wg_e + du Wu_e
- *   dw_down[e] = dy_sorted^T h,  dw_gate[e] = dg^T x_sorted,  dw_up[e] = du^T x_sorted
+/* The local experts' backward.  Per expert e with rows [o_e, o_{e+1}), with
+ * the weights in the math form (MOE_WEIGHTS_IN_OUT; the other layout stores
+ * the transposes):
+ *   dh = dy_sorted Wd_e^T;  dg = dh * up * silu'(gate);  du = dh * silu(gate)
+ *   dx_sorted = dg Wg_e^T + du Wu_e^T
+ *   dWd_e = h^T dy_sorted,  dWg_e = x_sorted^T dg,  dWu_e = x_sorted^T du
  * summed over the expert's rows (an empty expert gets zeros).
  *   gate, up, h          device [P_max, I] dtype (from moe_grouped_ffn_train)
  *   dy_sorted            device [P_max, H] dtype (from moe_combine_backward)
  *   dx_sorted            device [P_max, H] dtype out
- *   dw_gate, dw_up       device [L, I, H] dtype out;  dw_down [L, H, I] out
+ *   dw_gate, dw_up, dw_down  device dtype out, in the layout of w_gate, w_up, w_down
  *   ws                   device workspace of MOE_STAGE_FFN_BACKWARD bytes */
 moe_status moe_grouped_ffn_backward(const moe_layer_desc* d, const void* x_sorted, const int32_t* offsets,
                                     const void* w_gate, const void* w_up, const void* w_down, const void* gate,
@@ -408,7 +426,7 @@ moe_status moe_dispatch_backward(const moe_layer_desc* d, const void* dx_sorted,
  * intermediates.  db_router may be NULL (no router bias).  Workspace:
  * MOE_STAGE_LAYER_BACKWARD bytes.
  *   dy  device [T, H] dtype;  dx device [T, H] dtype out
- *   dw_router [E, H], dw_gate [L, I, H], dw_up [L, I, H], dw_down [L, H, I] dtype out */
+ *   dw_router [E, H] dtype out; dw_gate, dw_up, dw_down dtype out in the layout of the weights */
 moe_status moe_layer_backward(const moe_layer_desc* d, const void* x, const void* w_router, const void* w_gate,
                               const void* w_up, const void* w_down, const moe_saved* saved, const void* dy,
                               void* dx, void* dw_router, float* db_router, void* dw_gate, void* dw_up,

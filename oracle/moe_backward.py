@@ -189,10 +189,12 @@ def layer_backward(inp: dict, dy: np.ndarray, *, logits: Optional[np.ndarray] = 
     dy = np.asarray(dy, dtype=np.float64)
     cb = combine_backward(dy, f["y_sorted"], f["pair_row"], f["topk_w"])
     dl = softmax_over_k_backward(f["topk_w"], cb["d_topk_w"])
-    wg = fwd._ExpertView(inp["w_gate"], dt)
-    wu = fwd._ExpertView(inp["w_up"], dt)
-    wd = fwd._ExpertView(inp["w_down"], dt)
+    wg, wu, wd = fwd.expert_views(inp)
     fb = grouped_ffn_backward(f["x_sorted"], f["offsets"], wg, wu, wd, cb["dy_sorted"])
+    if getattr(s, "weight_layout", "out_in") == "in_out":
+        # the weight gradients take the layout of the weights
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            fb[k] = np.ascontiguousarray(fb[k].transpose(0, 2, 1))
     rb = route_backward(x, f["topk_ids"], dl, s.E)
     dx = dispatch_backward(fb["dx_sorted"], f["pair_row"], f["topk_ids"], dl, wr)
     out = {"forward": f, "dy_sorted": cb["dy_sorted"], "d_topk_w": cb["d_topk_w"], "dl": dl, "dx": dx, **fb,

@@ -432,9 +432,7 @@ def layer_forward(inp: dict, *, logits: Optional[np.ndarray] = None,
         want = np.zeros(s.T, dtype=bool)
         want[tokens] = True
         rows = want[d["sorted_pairs"] // s.k] if d["sorted_pairs"].size else np.zeros(0, dtype=bool)
-    wg = _ExpertView(inp["w_gate"], dt)
-    wu = _ExpertView(inp["w_up"], dt)
-    wd = _ExpertView(inp["w_down"], dt)
+    wg, wu, wd = expert_views(inp)
     y_sorted = grouped_ffn(d["x_sorted"], d["offsets"], wg, wu, wd, rows=rows)
     out["y_sorted"] = y_sorted
     out["y"] = combine(y_sorted, d["pair_row"], r["topk_w"], tokens=tokens)
@@ -443,17 +441,32 @@ def layer_forward(inp: dict, *, logits: Optional[np.ndarray] = None,
 
 
 class _ExpertView:
-    """Decodes one expert's matrix at a time, so float64 copies stay small."""
+    """Decodes one expert's matrix at a time, so float64 copies stay small.
 
-    def __init__(self, a: np.ndarray, dtype: str):
-        self.a, self.dtype = a, dtype
+    The matrix is returned as [out, in] (how expert_ffn takes it) whichever way it
+    is stored: layout "in_out" stores each expert matrix transposed, [in, out].
+    """
+
+    def __init__(self, a: np.ndarray, dtype: str, layout: str = "out_in"):
+        if layout not in ("out_in", "in_out"):
+            raise ValueError(f"unknown weight layout {layout!r}")
+        self.a, self.dtype, self.layout = a, dtype, layout
 
     def __getitem__(self, i: int) -> np.ndarray:
-        return decode(self.a[i], self.dtype)
+        m = decode(self.a[i], self.dtype)
+        return m.T if self.layout == "in_out" else m
 
     @property
     def shape(self):
-        return self.a.shape
+        L, r, c = self.a.shape
+        return (L, c, r) if self.layout == "in_out" else (L, r, c)
+
+
+def expert_views(inp: dict):
+    """The gate, up and down weights of a layer's inputs as [out, in] views (any stored layout)."""
+    lay = getattr(inp["spec"], "weight_layout", "out_in")
+    dt = inp["spec"].dtype
+    return tuple(_ExpertView(inp[k], dt, lay) for k in ("w_gate", "w_up", "w_down"))
 
 
 # --------------------------------------------------------------------------- #

@@ -31,8 +31,11 @@ so the values do not depend on how the work is split over threads):
 Large arrays are split into row chunks of at most 2^20 elements, chunk c
 drawing from child c of its array's stream.  Normals are drawn as float32
 (numpy's float32 ziggurat) and scaled in float32; bf16 layers round those float32 values to bf16 (nearest, ties to
-even).  Every expert matrix is stored as nn.Linear stores its weight,
-[out_features, in_features]; the math form of the layer is x @ W.T.
+even).  Every expert matrix is drawn as nn.Linear stores its weight,
+[out_features, in_features] (the math form of the layer is x @ W.T); a spec
+with weight_layout "in_out" then stores each expert matrix transposed
+(w_gate, w_up [L, H, I], w_down [L, I, H]), the same values in the other
+layout.
 """
 
 from __future__ import annotations
@@ -68,6 +71,7 @@ class LayerSpec:
     zipf_s: float = 1.2
     capacity_factor: float = 0.0   # <= 0: no capacity limit
     seed: int = 0
+    weight_layout: str = "out_in"  # "out_in": w_gate [L,I,H] ...; "in_out": w_gate [L,H,I] ...
 
     def replace(self, **kw) -> "LayerSpec":
         return dataclasses.replace(self, **kw)
@@ -136,6 +140,7 @@ def make_layer(s: LayerSpec, with_experts: bool = True) -> dict:
 
     Returns a dict with
       x [T,H], w_router [E,H], w_gate [L,I,H], w_up [L,I,H], w_down [L,H,I]
+        (weight_layout "in_out": w_gate, w_up [L,H,I], w_down [L,I,H], the same values)
         -- float32 arrays for dtype "f32", uint16 bf16 bit patterns for "bf16";
       b_router [E] float32 or None; and "spec".
     """
@@ -165,6 +170,10 @@ def make_layer(s: LayerSpec, with_experts: bool = True) -> dict:
             _normal_into(wg[e], kids[3 * e + 0], 1.0 / math.sqrt(s.H), s.dtype)
             _normal_into(wu[e], kids[3 * e + 1], 1.0 / math.sqrt(s.H), s.dtype)
             _normal_into(wd[e], kids[3 * e + 2], 1.0 / math.sqrt(s.I), s.dtype)
+        if s.weight_layout == "in_out":
+            wg, wu, wd = (np.ascontiguousarray(w.transpose(0, 2, 1)) for w in (wg, wu, wd))
+        elif s.weight_layout != "out_in":
+            raise ValueError(f"unknown weight layout {s.weight_layout!r}")
         out["w_gate"], out["w_up"], out["w_down"] = wg, wu, wd
     return out
 

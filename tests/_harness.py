@@ -31,7 +31,7 @@ def np_of(t) -> np.ndarray:
 
 def desc_of(s):
     import expert_token_dispatch_amd as etd
-    return etd.make_desc(s.T, s.H, s.I, s.E, s.k, s.local_begin, s.L, s.capacity_factor, s.dtype)
+    return etd.make_desc(s.T, s.H, s.I, s.E, s.k, s.local_begin, s.L, s.capacity_factor, s.dtype, s.weight_layout)
 
 
 def layer_of(inp):

@@ -223,3 +223,19 @@ def test_planted_mistakes_fail_finite_differences(monkeypatch, fn, mutant):
     inp, dy = tiny(T=6, H=4, I=3, E=4, k=2, lb=0, L=4, seed=10)
     with pytest.raises(AssertionError):
         fd_check(inp, dy)
+
+
+def test_weight_gradients_take_the_weights_layout():
+    # math-form weights (w_gate, w_up [L, H, I], w_down [L, I, H]): the same layer, so the
+    # same gradients (up to the BLAS summation order of transposed operands), with each
+    # expert's weight gradient stored transposed
+    import oracle as fwd_oracle
+    base = synth.spec("gptoss_ep8_share", T=200, H=40, I=24, E=16, k=4, L=8, local_begin=4)
+    dy = fwd_oracle.decode(synth.make_upstream_grad(base), base.dtype)
+    a = B.layer_backward(synth.make_layer(base), dy)
+    b = B.layer_backward(synth.make_layer(base.replace(weight_layout="in_out")), dy)
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert b[k].shape == a[k].transpose(0, 2, 1).shape
+        np.testing.assert_allclose(b[k], a[k].transpose(0, 2, 1), rtol=1e-12, atol=1e-12)
+    for k in ("dx", "dw_router", "dx_sorted"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-12, atol=1e-12)

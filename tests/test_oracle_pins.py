@@ -609,3 +609,21 @@ def test_planted_mistake_is_caught(monkeypatch, target, mutant):
     monkeypatch.setattr(oracle.moe_oracle, target, mutant)
     monkeypatch.setattr(oracle, target, mutant, raising=False)
     assert not _pins_pass(), f"a planted mistake in {target} went unnoticed"
+
+
+def test_math_form_weight_layout():
+    # the stacked layout of the workloads' math form (w_gate, w_up [L, H, I], w_down [L, I, H]):
+    # with one expert and k = 1 the layer is (silu(x Wg) * (x Wu)) Wd written directly on
+    # the stored arrays, and any layer equals the linear-layout layer on the same draws
+    s1 = synth.spec("tiny_fp32", T=40, H=24, I=16, E=1, k=1, L=1, weight_layout="in_out")
+    inp = synth.make_layer(s1)
+    assert inp["w_gate"].shape == (1, 24, 16) and inp["w_down"].shape == (1, 16, 24)
+    x = inp["x"].astype(np.float64)
+    g = x @ inp["w_gate"][0].astype(np.float64)
+    want = (g / (1 + np.exp(-g)) * (x @ inp["w_up"][0].astype(np.float64))) @ inp["w_down"][0].astype(np.float64)
+    np.testing.assert_allclose(oracle.layer_forward(inp)["y"], want, rtol=1e-13, atol=1e-14)
+    for name in ("skewed_capacity", "gptoss_ep8_share"):
+        base = synth.spec(name, T=300, H=64, I=48)
+        a = oracle.layer_forward(synth.make_layer(base))
+        b = oracle.layer_forward(synth.make_layer(base.replace(weight_layout="in_out")))
+        np.testing.assert_allclose(a["y"], b["y"], rtol=1e-12, atol=1e-13)
