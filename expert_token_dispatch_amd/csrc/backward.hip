@@ -601,57 +601,6 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* __restrict
   C[i] = Elem<T>::from_f32(v);
 }
 
-// Per-expert transposed blocks for the weight gradients on the large tile: for
-// expert e with rows [o_e, o_e + n_e) of X [P, Cw], the block at element offset
-// Cw * Q_e is [Cw, K_e] with [c][k] = X[o_e + k][c] for k < n_e and zero up to
-// K_e = max(64, n_e rounded up to 64); Q_e = sum of K_e' over e' < e.
-// blockIdx.y enumerates the 64-row blocks of all experts (at most
-// ceil(P_max/64) + L of them; surplus blocks exit), blockIdx.x the 64-column blocks.
-__device__ __forceinline__ int seg_k(int n) { return n <= 64 ? 64 : (n + 63) / 64 * 64; }
-
-__global__ __launch_bounds__(256) void seg_transpose_kernel(const bf16_t* __restrict__ X, int Cw,
-                                                            const int32_t* __restrict__ offsets, int L,
-                                                            bf16_t* __restrict__ XT) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[64][72];
-  const int c0 = blockIdx.x * 64, t = threadIdx.x;
-  // row blocks y = blockIdx.y, blockIdx.y + gridDim.y, ... over all experts; the
-  // expert walk restarts where the previous block of this thread block left off
-  int e = 0, base = 0;  // expert e's row blocks start at block number base
-  int64_t q = 0;
-  for (int y = blockIdx.y;; y += gridDim.y) {
-    int o = 0, n = 0, K = 0;
-    for (; e < L; ++e) {
-      o = offsets[e];
-      n = offsets[e + 1] - o;
-      K = seg_k(n);
-      if (y < base + K / 64) break;
-      base += K / 64;
-      q += K;
-    }
-    if (e >= L) return;  // uniform: every thread of the block walks the same blocks
-    const int k0 = (y - base) * 64;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = t / 8 + 32 * j, c8 = (t % 8) * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (k0 + r < n) v = *reinterpret_cast<const u32x4_t*>(X + size_t(o + k0 + r) * Cw + c0 + c8);
-      *reinterpret_cast<u32x4_t*>(&tile[r][c8]) = v;
-    }
-    __syncthreads();
-    bf16_t* d = XT + q * Cw;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = t / 8 + 32 * j, r8 = (t % 8) * 8;
-      uint32_t w[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        w[e2] = uint32_t(tile[r8 + 2 * e2][c]) | (uint32_t(tile[r8 + 2 * e2 + 1][c]) << 16);
-      *reinterpret_cast<u32x4_t*>(d + size_t(c0 + c) * K + k0 + r8) = u32x4_t{w[0], w[1], w[2], w[3]};
-    }
-    __syncthreads();  // the tile is refilled next round
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -706,12 +655,7 @@ moe_status dispatch_bwd_t(const DispatchBwdArgs& a) {
 struct FfnBwdScratch {
   void* dgu;
   void* big;  // big_backward_scratch_bytes
-  // the weight gradients on the large tile: per-expert transposed blocks of
-  // dy_sorted [H], h [I], dg | du [2I] and x_sorted [H] rows (see seg_transpose_kernel)
-  void* dysT;
-  void* hT;
-  void* dguT;
-  void* xT;
+  bool big_wgrad;  // the weight gradients on the large tile (no scratch of their own)
 };
 
 FfnBwdScratch carve_ffn_bwd(const moe_layer_desc* d, int64_t max_pairs, void* base, size_t* bytes) {
@@ -727,13 +671,7 @@ FfnBwdScratch carve_ffn_bwd(const moe_layer_desc* d, int64_t max_pairs, void* ba
   w.dgu = take(size_t(max_pairs) * 2 * d->intermediate * dt);
   if (big_backward_supported(d, max_pairs)) {
     w.big = take(big_backward_scratch_bytes(d));
-    if (big_wgrad_supported(d, max_pairs)) {
-      const size_t q = size_t(max_pairs) + size_t(64) * d->local_count;
-      w.dysT = take(q * d->hidden * dt);
-      w.hT = take(q * d->intermediate * dt);
-      w.dguT = take(q * 2 * d->intermediate * dt);
-      w.xT = take(q * d->hidden * dt);
-    }
+    w.big_wgrad = big_wgrad_supported(d, max_pairs);
   }
   if (bytes) *bytes = o;
   return w;
@@ -788,36 +726,24 @@ moe_status ffn_bwd_t(const FfnBwdArgs& a) {
   }
   bool big_w = false;
   if constexpr (sizeof(T) == 2) {
-    if (w.dysT != nullptr) {
+    if (w.big_wgrad) {
+      // the weight gradients on the large tile, every operand read in place
       big_w = true;
-      // the row blocks actually present are not known on the host (no sync): a grid of
-      // about 4096 blocks strides over them
-      auto seg_t = [&](const void* X, int Cw, void* XT) -> moe_status {
-        const int64_t slots = std::min<int64_t>((a.max_pairs + 63) / 64 + L, std::max(1, 4096 / (Cw / 64)));
-        MOE_LAUNCH("ffn_bwd_seg_transpose", seg_transpose_kernel, dim3(unsigned(Cw / 64), unsigned(slots)), dim3(256), 0, a.s,
-                   static_cast<const bf16_t*>(X), Cw, a.offsets, L, static_cast<bf16_t*>(XT));
-        return MOE_OK;
-      };
-      const bf16_t* dysT = static_cast<const bf16_t*>(w.dysT);
-      const bf16_t* hT = static_cast<const bf16_t*>(w.hT);
-      const bf16_t* dguT = static_cast<const bf16_t*>(w.dguT);
-      const bf16_t* xT = static_cast<const bf16_t*>(w.xT);
-      moe_status st = seg_t(a.dy_sorted, H, w.dysT);
-      if (st == MOE_OK) st = seg_t(a.h, I, w.hT);
-      if (st == MOE_OK) st = seg_t(dgu, 2 * I, w.dguT);
-      if (st == MOE_OK) st = seg_t(a.x_sorted, H, w.xT);
+      const bf16_t* dys = static_cast<const bf16_t*>(a.dy_sorted);
+      const bf16_t* h = static_cast<const bf16_t*>(a.h);
+      const bf16_t* xs = static_cast<const bf16_t*>(a.x_sorted);
+      bf16_t* dwd = static_cast<bf16_t*>(a.dw_down);
+      bf16_t* dwg = static_cast<bf16_t*>(a.dw_gate);
+      bf16_t* dwu = static_cast<bf16_t*>(a.dw_up);
+      const bf16_t* g = reinterpret_cast<const bf16_t*>(dgu);
+      moe_status st = io ? launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, h, I, 0, dys, H, 0, dwd, nullptr,
+                                                     I, H, 1, a.max_pairs, a.s)
+                         : launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, dys, H, 0, h, I, 0, dwd, nullptr,
+                                                     H, I, 1, a.max_pairs, a.s);
       if (st == MOE_OK) {
-        st = io ? launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, hT, I, dysT, 0,
-                                            static_cast<bf16_t*>(a.dw_down), nullptr, I, H, 1, a.max_pairs, a.s)
-                : launch_big_backward_wgrad("ffn_down_wgrad", d, a.offsets, dysT, H, hT, 0,
-                                            static_cast<bf16_t*>(a.dw_down), nullptr, H, I, 1, a.max_pairs, a.s);
-      }
-      if (st == MOE_OK) {
-        st = io ? launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, xT, H, dguT, 2 * I,
-                                            static_cast<bf16_t*>(a.dw_gate), static_cast<bf16_t*>(a.dw_up), H, I, 2,
+        st = io ? launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, xs, H, 0, g, 2 * I, I, dwg, dwu, H, I, 2,
                                             a.max_pairs, a.s)
-                : launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, dguT, 2 * I, xT, 0,
-                                            static_cast<bf16_t*>(a.dw_gate), static_cast<bf16_t*>(a.dw_up), I, H, 2,
+                : launch_big_backward_wgrad("ffn_gate_up_wgrad", d, a.offsets, g, 2 * I, I, xs, H, 0, dwg, dwu, I, H, 2,
                                             a.max_pairs, a.s);
       }
       if (st != MOE_OK) return st;

@@ -552,7 +552,7 @@ constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true, 4>::kStage;  // 160
 // product's dgrad dh = dy_sorted Wd: reads the saved gate and up values Gs, Us
 // and writes dg and du side by side into C, rows of 2N).
 constexpr int kPlain = 0, kSave = 1, kSwigluBwd = 2;
-// the weight-gradient products (see wgrad_k): gemm_kernel decodes its own jobs
+// the weight-gradient products (wgrad_kernel); the epilogue treats them as kPlain
 constexpr int kWgrad = 3;
 
 template <int NMAT, bool WIDE, int NW, int EP>
@@ -733,19 +733,33 @@ __device__ __forceinline__ f32x4_t* part_ptr(float* __restrict__ parts, int pslo
   return reinterpret_cast<f32x4_t*>(parts + size_t(pslot) * (kPartBytes / sizeof(float)));
 }
 
-// One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
-//
-// The weight operand (Bg, and Bu for the up rows of gate/up) is stored one of two ways:
-//   BKN false: n-major, element (n, k) at B[n * kw + k] (a linear layer's [out, in]);
-//   BKN true:  k-major, element (k, n) at B[k * N + n] (the math form's [in, out]).
-// kw is K, or with kcat > 0 (one-matrix products only) 64 * kcat: the k steps from
-// kcat on then read Bu at step - kcat (a product over two matrices side by side
+// The operands of one tile.  Each is stored one of two ways, with rows of ld elements:
+//   A, AKM false: m-major, element (m, k) at A[m * lda + k]; the buffer holds a_rows rows
+//      of m (rows past them read zero);
+//   A, AKM true:  k-major, element (k, m) at A[k * lda + m]; a_rows rows of k;
+//   B, BKN false: n-major, element (n, k) at B[n * ldb + k] (a linear layer's [out, in]);
+//   B, BKN true:  k-major, element (k, n) at B[k * ldb + n] (the math form's [in, out]);
+//      b_rows rows (of n or k) either way.
+// Bg, and Bu for the up rows of gate/up; with kcat > 0 (one-matrix products only) the
+// k steps from kcat on read Bu at step - kcat (a product over two matrices side by side
 // along K, such as dg Wg + du Wu).
-template <int NMAT, bool WIDE, int NW, int EP, bool BKN>
-__device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_rows, const bf16_t* __restrict__ Bg,
-                                          const bf16_t* __restrict__ Bu, bf16_t* __restrict__ C, int N, int K,
-                                          int kcat, const Job& jb, float* __restrict__ parts, char* lds,
+struct Operands {
+  const bf16_t* A;
+  int a_rows, lda;
+  const bf16_t* Bg;
+  const bf16_t* Bu;
+  int b_rows, ldb;
+};
+
+// One tile (or one K piece of it): the main loop, then the epilogue or the piece write-out.
+template <int NMAT, bool WIDE, int NW, int EP, bool BKN, bool AKM>
+__device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict__ C, int N, int K, int kcat,
+                                          const Job& jb, float* __restrict__ parts, char* lds,
                                           bf16_t* __restrict__ Gs, bf16_t* __restrict__ Us) {
+  const bf16_t* __restrict__ A = op.A;
+  const bf16_t* __restrict__ Bg = op.Bg;
+  const bf16_t* __restrict__ Bu = op.Bu;
+  const int a_rows = op.a_rows, lda = op.lda, ldb = op.ldb;
   using S = Shape<WIDE, NW>;
   constexpr int NB = S::NB, kThreads = S::kThreads;
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;
@@ -763,15 +777,15 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
   const int c_odd = (lane & 7) ^ ((4 + (lane >> 4)) & 7);
   const int a_lrow = (S::kA / NW) * wave + (lane >> 3);
-  // buffer resources over the tile's rows of A and over the whole weight matrix
-  // (its extent is under 4 GiB); a read outside either returns zeros
-  const uint32_t a_bytes = uint32_t(min(int64_t(a_rows - row0) * K * 2, int64_t(0xFFFFFFFF)));
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(A + size_t(row0) * K), 0, a_bytes, kRsrcFlags);
+  // buffer resources over A (from the tile's first row when m-major) and over the whole
+  // weight matrix (its extent is under 4 GiB); a read outside either returns zeros
+  const int64_t a_span = AKM ? int64_t(a_rows) * lda : int64_t(a_rows - row0) * lda;
+  const uint32_t a_bytes = uint32_t(min(a_span * 2, int64_t(0xFFFFFFFF)));
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(AKM ? A : A + size_t(row0) * lda), 0, a_bytes, kRsrcFlags);
   // the first half of the waves loads gate rows (or the only matrix), the second half up rows;
   // b_rsrc2 is the second matrix of a product split along K
-  const int kw = kcat > 0 ? kcat * BK : K;
-  const uint32_t b_bytes = uint32_t(N) * uint32_t(kw) * 2u;
+  const uint32_t b_bytes = uint32_t(min(int64_t(op.b_rows) * ldb * 2, int64_t(0xFFFFFFFF)));
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(NMAT == 2 && wave >= NW / 2 ? Bu : Bg), 0, b_bytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t b_rsrc2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(Bu), 0, b_bytes,
@@ -784,12 +798,25 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
   // Each lane's byte offsets are fixed for the whole loop (A from the tile's
   // first row, B from the matrix); a step only moves the scalar offset by k0,
   // so a load costs no vector arithmetic.
-  const int a_lim = a_rows - 1 - row0;
   uint32_t a_vo[S::kLdA], b_vo[S::kLdB];
+  if constexpr (!AKM) {
+    const int a_lim = a_rows - 1 - row0;
 #pragma unroll
-  for (int j = 0; j < S::kLdA; ++j) {
-    const int cc = (j & 1) ? c_odd : c_even;
-    a_vo[j] = (uint32_t(min(a_lrow + 8 * j, a_lim)) * uint32_t(K) + uint32_t(cc * 8)) * 2u;
+    for (int j = 0; j < S::kLdA; ++j) {
+      const int cc = (j & 1) ? c_odd : c_even;
+      a_vo[j] = (uint32_t(min(a_lrow + 8 * j, a_lim)) * uint32_t(lda) + uint32_t(cc * 8)) * 2u;
+    }
+  } else {
+    // k-major stage, laid out as the k-major B stage below: regions of 128 m columns,
+    // 64 k rows of 256 bytes each, 64-byte units swizzled by row
+#pragma unroll
+    for (int j = 0; j < S::kLdA; ++j) {
+      const int gb = S::kLdA * wave + j;
+      const int krow = 4 * (gb & 15) + (lane >> 4);
+      const int u = ((lane & 15) >> 2) ^ ((lane >> 4) & 3);
+      // columns past the tile's rows read what follows (or zeros past the buffer): never stored
+      a_vo[j] = (uint32_t(krow) * uint32_t(lda) + uint32_t(row0 + 128 * (gb >> 4) + 32 * u + 8 * (lane & 3))) * 2u;
+    }
   }
   if constexpr (!BKN) {
     int b_lrow;
@@ -800,7 +827,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
       const int cc = (j & 1) ? c_odd : c_even;
       int r = n0 + b_lrow + 8 * j;
       if (r >= N) r %= N;
-      b_vo[j] = (uint32_t(r) * uint32_t(kw) + uint32_t(cc * 8)) * 2u;
+      b_vo[j] = (uint32_t(r) * uint32_t(ldb) + uint32_t(cc * 8)) * 2u;
     }
   } else {
     // k-major stage: the tile's B rows in regions of 128 columns (gate regions, then
@@ -816,7 +843,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
       const int u = ((lane & 15) >> 2) ^ ((lane >> 4) & 3);
       const int col = n0 + 128 * (NMAT == 2 ? reg % (S::kB / 256) : reg) + 32 * u + 8 * (lane & 3);
       // columns past N read what follows in memory (or zeros past the matrix): never stored
-      b_vo[j] = (uint32_t(krow) * uint32_t(N) + uint32_t(col)) * 2u;
+      b_vo[j] = (uint32_t(krow) * uint32_t(ldb) + uint32_t(col)) * 2u;
     }
   }
 // loads q0..q1-1 of stage kt_, in the order A0 B0 A1 B1 ... (then the B rows
@@ -826,9 +853,9 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
     char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
     char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
     const int s_ = kb + (kt_);                                                                              \
-    const uint32_t k0_ = uint32_t(s_) * (BK * 2);                                                           \
+    const uint32_t k0_ = uint32_t(s_) * (AKM ? uint32_t(BK * 2) * uint32_t(lda) : uint32_t(BK * 2));          \
     const bool sec_ = kcat > 0 && s_ >= kcat;                                                               \
-    const uint32_t kbo_ = uint32_t(sec_ ? s_ - kcat : s_) * (BKN ? uint32_t(BK * 2) * uint32_t(N) : uint32_t(BK * 2)); \
+    const uint32_t kbo_ = uint32_t(sec_ ? s_ - kcat : s_) * (BKN ? uint32_t(BK * 2) * uint32_t(ldb) : uint32_t(BK * 2)); \
     _Pragma("unroll") for (int q = (q0_); q < (q1_); ++q) {                                                 \
       const int j_ = q < 2 * S::kLdA ? q / 2 : q - S::kLdA;                                                 \
       if (q < 2 * S::kLdA && q % 2 == 0)                                                                    \
@@ -868,13 +895,24 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
                  32 * (G & 1) + 8 * (i & 3);
     }
   }
-  const int a_off = (wm * 128 + fr) * kRowBytes;
+  // A rows wm*128 + i*32: m-major, one row per lane; k-major, region wm, unit i
+  int aoffs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (!AKM) {
+      aoffs[i] = (wm * 128 + i * 32 + fr) * kRowBytes;
+    } else {
+      const int G = lane >> 4, il = lane & 15;
+      aoffs[i] = wm * 16384 + (8 * (G >> 1) + (il >> 2)) * 256 + 64 * (i ^ (il >> 2)) + 32 * (G & 1) + 8 * (il & 3);
+    }
+  }
   bf16x8_t fa[2][4], fb[2][NB];
 #define MOE_LOADF(buf_, st_, kc_)                                                                         \
   do {                                                                                                    \
     const int co_ = ((2 * (kc_) + g) ^ sw) * 16;                                                          \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
-      fa[buf_][i] = *reinterpret_cast<const bf16x8_t*>((st_) + a_off + i * 32 * kRowBytes + co_);          \
+      fa[buf_][i] = AKM ? read_kn_frag((st_) + aoffs[i] + (kc_) * 16 * 256)                                \
+                        : *reinterpret_cast<const bf16x8_t*>((st_) + aoffs[i] + co_);                      \
     _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                        \
       fb[buf_][j] = BKN ? read_kn_frag((st_) + boffs[j] + (kc_) * 16 * 256)                                \
                         : *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                      \
@@ -886,7 +924,7 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][i], acc[i][j], 0, 0, 0); \
   } while (0)
   // LDS reads per chunk (a k-major B fragment takes two transposing reads) and MFMAs per chunk
-  constexpr int kDs = 4 + NB * (BKN ? 2 : 1), kMf = 4 * NB;
+  constexpr int kDs = 4 * (AKM ? 2 : 1) + NB * (BKN ? 2 : 1), kMf = 4 * NB;
   // {MFMA, LDS read, MFMA} (or {MFMA, LDS read} when the reads outnumber half the
   // MFMAs): the next chunk's fragment reads spread over the whole group
 #define MOE_PIPE_DS()                                                                                     \
@@ -1002,16 +1040,48 @@ __device__ __forceinline__ void tile_body(const bf16_t* __restrict__ A, int a_ro
 }
 
 // ---- weight gradients on the large tile --------------------------------------
-// Expert e's dW = A_e B_e^T reduces over its rows.  The caller has copied the
-// operands transposed into per-expert blocks [rows, K_e] with K_e the segment
-// length rounded up to 64 (at least 64; the padding is zero), at element offset
-// rows * Q_e (Q_e = sum of K_e' over e' < e), so each expert's product has
-// the forward's operand layout with its own K.  In gemm_kernel's kWgrad mode:
-// blockIdx x = tile (m major), y = expert, z = which of up to two outputs (C, Gs);
-// A = the transposed blocks (a_rows of them per expert), B0 = B's blocks, K = M;
-// kcat = 0: output z takes A rows [z M, (z+1) M); kcat > 0: B's blocks have kcat
-// rows per expert and output z takes B rows [z N, (z+1) N).
-__device__ __forceinline__ int wgrad_k(int n) { return n <= 64 ? 64 : (n + 63) / 64 * 64; }
+// Expert e's dW = A_e^T B_e reduces over its rows [o_e, o_e + n_e): both operands are
+// read in place, k-major (row p of x_sorted, h, dy_sorted or dg | du is k = p), with the
+// buffer resources ending at the segment's end so the last, partial k step reads
+// zeros past it.  Grid: x = output tile (m major), y = expert, z = which of up to two
+// outputs (C0, C1), the z-th reading A and B at column offsets z * a_zoff, z * b_zoff.
+struct WgradOps {
+  const bf16_t* A;
+  int lda, a_zoff;
+  const bf16_t* B;
+  int ldb, b_zoff;
+  bf16_t* C0;
+  bf16_t* C1;
+  int M, N;
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void wgrad_kernel(WgradOps w, const int32_t* __restrict__ offsets) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int e = blockIdx.y, z = blockIdx.z;
+  const int o = offsets[e], n = offsets[e + 1] - o;
+  const int tn = (w.N + BNE - 1) / BNE;
+  Job jb;
+  jb.expert = e;
+  jb.row0 = (blockIdx.x / tn) * BM;
+  jb.rows = min(BM, w.M - jb.row0);
+  jb.n0 = blockIdx.x % tn;
+  jb.wide = false;
+  jb.kb = 0;
+  jb.nks = max(1, (n + BK - 1) / BK);  // an empty segment reads zeros and writes a zero gradient
+  jb.part = 0;
+  jb.nparts = 1;
+  jb.pslot = 0;
+  Operands op;
+  op.A = w.A + size_t(o) * w.lda + size_t(z) * w.a_zoff;
+  op.a_rows = n;
+  op.lda = w.lda;
+  op.Bg = op.Bu = w.B + size_t(o) * w.ldb + size_t(z) * w.b_zoff;
+  op.b_rows = n;
+  op.ldb = w.ldb;
+  bf16_t* Ce = (z ? w.C1 : w.C0) + size_t(e) * w.M * w.N;
+  tile_body<1, false, NW, kWgrad, true, true>(op, Ce, w.N, jb.nks * BK, 0, jb, nullptr, lds, nullptr, nullptr);
+}
 
 // BKN, kcat: the weight operand's layout and K split (see tile_body)
 template <int NMAT, int NW, int EP, bool BKN>
@@ -1022,32 +1092,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
                                                         float* __restrict__ parts, bf16_t* __restrict__ Gs,
                                                         bf16_t* __restrict__ Us) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  if constexpr (EP == kWgrad) {
-    const int e = blockIdx.y, z = blockIdx.z, M = K;
-    int64_t q = 0;
-    for (int i = 0; i < e; ++i) q += wgrad_k(offsets[i + 1] - offsets[i]);
-    const int Ke = wgrad_k(offsets[e + 1] - offsets[e]);
-    const int tn = (N + BNE - 1) / BNE;
-    Job jb;
-    jb.expert = e;
-    jb.row0 = (blockIdx.x / tn) * BM;
-    jb.rows = min(BM, M - jb.row0);
-    jb.n0 = blockIdx.x % tn;
-    jb.wide = false;
-    jb.kb = 0;
-    jb.nks = Ke / BK;
-    jb.part = 0;
-    jb.nparts = 1;
-    jb.pslot = 0;
-    const bool zb = kcat > 0;
-    const bf16_t* Ae = A + q * a_rows + (zb ? 0 : size_t(z) * M * Ke);
-    const bf16_t* Be = B0 + q * (zb ? kcat : N) + (zb ? size_t(z) * N * Ke : 0);
-    bf16_t* Ce = (z ? Gs : C) + size_t(e) * M * N;
-    // (EP, not kPlain, as the template argument: hipcc's host pass rejects the literal
-    // here; the epilogue treats kWgrad as kPlain)
-    tile_body<NMAT, false, NW, EP, false>(Ae, M, Be, Be, Ce, N, Ke, 0, jb, parts, lds, Us, Us);
-    return;
-  }
+  static_assert(EP != kWgrad, "the weight-gradient products run wgrad_kernel");
   constexpr int ON = NMAT == 2 ? BNE / 2 : BNE;  // output columns per regular tile
   const int NT = (N + ON - 1) / ON;
   const int nk = K / BK;
@@ -1062,13 +1107,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const bf16_t* __restrict_
   Job jb;
   unit_job(offsets, spre, L, NT, nk, cpx, xcd, xp, loc, jb);
   __syncthreads();  // every wave has its job before the first loads land in the LDS
-  const size_t boff = size_t(jb.expert) * N * (kcat > 0 ? kcat * BK : K);
-  const bf16_t* Bg = B0 + boff;
-  const bf16_t* Bu = (NMAT == 2 || kcat > 0 ? B1 : B0) + boff;
+  // K of one weight matrix: K, or 64 kcat for a product over two matrices side by side along K
+  const int kw = kcat > 0 ? kcat * BK : K;
+  const size_t boff = size_t(jb.expert) * N * kw;
+  Operands op;
+  op.A = A;
+  op.a_rows = a_rows;
+  op.lda = K;
+  op.Bg = B0 + boff;
+  op.Bu = (NMAT == 2 || kcat > 0 ? B1 : B0) + boff;
+  op.b_rows = BKN ? kw : N;
+  op.ldb = BKN ? N : kw;
   if (jb.wide)
-    tile_body<NMAT, true, NW, EP, BKN>(A, a_rows, Bg, Bu, C, N, K, kcat, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, true, NW, EP, BKN, false>(op, C, N, K, kcat, jb, parts, lds, Gs, Us);
   else
-    tile_body<NMAT, false, NW, EP, BKN>(A, a_rows, Bg, Bu, C, N, K, kcat, jb, parts, lds, Gs, Us);
+    tile_body<NMAT, false, NW, EP, BKN, false>(op, C, N, K, kcat, jb, parts, lds, Gs, Us);
 }
 
 
@@ -1213,18 +1266,15 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
 }
 
 template <int NW>
-moe_status launch_wgrad_nw(const char* name, const moe_layer_desc* d, const int32_t* offsets, const bf16_t* At,
-                           int a_rows_total, const bf16_t* Bt, int b_rows_total, bf16_t* C0, bf16_t* C1, int M, int N,
-                           int Z, hipStream_t s) {
-  auto kern = gemm_kernel<1, NW, kWgrad, false>;
+moe_status launch_wgrad_nw(const char* name, const moe_layer_desc* d, const int32_t* offsets, const WgradOps& w, int Z,
+                           hipStream_t s) {
+  auto kern = wgrad_kernel<NW>;
   constexpr size_t lds = lds_bytes<1>();
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      int(lds));
   if (e != hipSuccess) return set_error(MOE_ERR_HIP, "%s: LDS attribute: %s", name, hipGetErrorString(e));
-  const unsigned tiles = unsigned(((M + BM - 1) / BM) * ((N + BNE - 1) / BNE));
-  MOE_LAUNCH(name, kern, dim3(tiles, unsigned(d->local_count), unsigned(Z)), dim3(NW * 64), lds, s, At, offsets, Bt,
-             Bt, C0, d->local_count, N, M, b_rows_total, a_rows_total, static_cast<const int32_t*>(nullptr), 0, 1,
-             static_cast<float*>(nullptr), C1, static_cast<bf16_t*>(nullptr));
+  const unsigned tiles = unsigned(((w.M + BM - 1) / BM) * ((w.N + BNE - 1) / BNE));
+  MOE_LAUNCH(name, kern, dim3(tiles, unsigned(d->local_count), unsigned(Z)), dim3(NW * 64), lds, s, w, offsets);
   return MOE_OK;
 }
 
@@ -1556,19 +1606,22 @@ moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const bf16_t* dy_s
                         max_pairs, pre + L + 1, parts, s);
 }
 
+// The weight gradients read their operands in place, k-major, with 32-bit offsets
+// from a segment's first row: every segment must be addressable that way.
 bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs) {
-  const int64_t kmax = (max_pairs + 63) / 64 * 64 + 64;
-  return big_backward_supported(d, max_pairs) && big::addressable(std::max(d->hidden, 2 * d->intermediate), kmax);
+  return big_backward_supported(d, max_pairs) &&
+         big::addressable(max_pairs + 64, std::max<int64_t>(d->hidden, 2 * int64_t(d->intermediate)));
 }
 
+// dW_e = A_e^T B_e for each local expert e (Z outputs; see big::WgradOps).
 moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
-                                     const bf16_t* At, int a_rows_total, const bf16_t* Bt, int b_rows_total,
+                                     const bf16_t* A, int lda, int a_zoff, const bf16_t* B, int ldb, int b_zoff,
                                      bf16_t* C0, bf16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s) {
+  big::WgradOps w{A, lda, a_zoff, B, ldb, b_zoff, C0, C1, M, N};
   // eight waves when the average segment is under 64 k steps, as for the forward
   const int64_t avg = max_pairs / std::max(1, d->local_count);
-  if (avg / big::BK < big::kEightWaveSteps)
-    return big::launch_wgrad_nw<8>(name, d, offsets, At, a_rows_total, Bt, b_rows_total, C0, C1, M, N, Z, s);
-  return big::launch_wgrad_nw<4>(name, d, offsets, At, a_rows_total, Bt, b_rows_total, C0, C1, M, N, Z, s);
+  if (avg / big::BK < big::kEightWaveSteps) return big::launch_wgrad_nw<8>(name, d, offsets, w, Z, s);
+  return big::launch_wgrad_nw<4>(name, d, offsets, w, Z, s);
 }
 
 moe_status launch_grouped_ffn(const FfnArgs& a) {

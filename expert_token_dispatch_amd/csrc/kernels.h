@@ -156,13 +156,14 @@ moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const uint16_t* dy
                                      const uint16_t* w_down, const uint16_t* w_gate, const uint16_t* w_up,
                                      const uint16_t* gate, const uint16_t* up, uint16_t* dgu, uint16_t* dx_sorted,
                                      int64_t max_pairs, void* scratch, hipStream_t s);
-// dW on the large tile from per-expert transposed blocks (see grouped_gemm.hip)
+// dW_e = A_e^T B_e over each local expert's rows on the large tile, both operands read
+// in place (row p of A and B is k = p; rows of lda, ldb elements); Z outputs C0, C1,
+// the z-th reading A and B at column offsets z * a_zoff, z * b_zoff.
 bool big_wgrad_supported(const moe_layer_desc* d, int64_t max_pairs);
-// Z outputs; b_rows_total = 0: output z takes A rows [zM, (z+1)M), else B's blocks have
-// b_rows_total rows and output z takes B rows [zN, (z+1)N)
 moe_status launch_big_backward_wgrad(const char* name, const moe_layer_desc* d, const int32_t* offsets,
-                                     const uint16_t* At, int a_rows_total, const uint16_t* Bt, int b_rows_total,
-                                     uint16_t* C0, uint16_t* C1, int M, int N, int Z, int64_t max_pairs, hipStream_t s);
+                                     const uint16_t* A, int lda, int a_zoff, const uint16_t* B, int ldb, int b_zoff,
+                                     uint16_t* C0, uint16_t* C1, int M, int N, int Z, int64_t max_pairs,
+                                     hipStream_t s);
 
 struct RouteBwdScratch {
   void* dlogits;     // [T, Ep] in the layer's type (Ep = E rounded up to 8)
