@@ -3,265 +3,26 @@
 // Ultralytics glossary "Expert Parallelism", section "How tokens move between
 // GPUs", step 3: each GPU runs its local experts on the tokens it received.
 // The Transformers page names the expert kernel style "grouped_gemm" and says
-// the expert weights are split along the expert dimension, which is the
-// stacked [L, out, in] layout used here.  Expert i owns sorted rows
-// [offsets[i], offsets[i+1]) and computes the SwiGLU feed-forward
-//   h = silu(X Wg_i^T) * (X Wu_i^T)      (gate/up kernel, SwiGLU in its epilogue)
-//   y = h Wd_i^T                         (down kernel)
+// the expert weights are split along the expert dimension: they are stacked
+// per local expert.  Expert i owns sorted rows [offsets[i], offsets[i+1]) and
+// computes the SwiGLU feed-forward (math form)
+//   h = silu(X Wg_i) * (X Wu_i)      (gate/up product, SwiGLU in its epilogue)
+//   y = h Wd_i                       (down product)
 // with float32 accumulation; h is rounded to the storage type once.
 //
-// Work split: one block computes a BM x BN output tile (both the gate and the
-// up tile for the gate/up kernel, so SiLU(gate)*up is formed in registers).
-// grid.x enumerates m-tile slots: expert i contributes ceil(n_i / BM) of them,
-// found on the device from `offsets` (no host sync), and the grid is sized for
-// the worst case ceil(P_max / BM) + L so surplus blocks exit at once.
-// grid.y enumerates n-tiles.  Four waves split the tile 2 x 2; each wave owns
-// 64 x 64 per matrix as 2 x 2 MFMA 32x32 blocks (bf16: v_mfma 32x32x16, the
-// lane holds 8 consecutive k of its row/column; f32: eight 32x32x2 steps over
-// the same 8 values).  A and B k-slices are staged through double-buffered LDS
-// with rows padded to 80 bytes so the 16-byte fragment reads of eight lanes
-// fall in distinct banks.
+// Three kernels, picked from the largest segment the caller allows (P_max) and
+// the dtype: the large-tile bf16 kernel below for segments of hundreds of rows,
+// the skinny kernel (skinny_gemm.hip) for decode-sized batches, and the general
+// kernel (general_gemm.hip) for float32 and shapes off the large tile's grid.
 #include <math.h>
 
 #include <algorithm>
 
-#include "common.h"
+#include "ffn_common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
-
-constexpr int BM = 128, BN = 128, kThreads = 256;
-
-template <typename T> struct Gemm;
-template <> struct Gemm<bf16_t> {
-  static constexpr int BK = 32;       // k per LDS stage
-  static constexpr int kLd = BK + 8;  // LDS row stride in elements (80 bytes)
-  static constexpr int kFragVec = 1;  // uint4 per lane per 16-k chunk
-  __device__ static void mma(const uint4* a, const uint4* b, f32x16_t& c) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[0]), __builtin_bit_cast(bf16x8_t, b[0]),
-                                                c, 0, 0, 0);
-  }
-};
-template <> struct Gemm<float> {
-  static constexpr int BK = 16;
-  static constexpr int kLd = BK + 4;  // 80 bytes
-  static constexpr int kFragVec = 2;
-  __device__ static void mma(const uint4* a, const uint4* b, f32x16_t& c) {
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].x), __uint_as_float(b[v].x), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].y), __uint_as_float(b[v].y), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].z), __uint_as_float(b[v].z), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[v].w), __uint_as_float(b[v].w), c, 0, 0, 0);
-    }
-  }
-};
-
-// SiLU through the hardware reciprocal (1 ulp) rather than an IEEE division:
-// five instructions instead of about fifteen.  Every FFN kernel here uses this
-// one definition, so a token's result does not depend on which kernel ran it.
-// Both ends stay exact: exp(-z) overflowing gives -0, underflowing gives z.
-__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-
-// NMAT = 2: gate and up products with the SwiGLU epilogue; NMAT = 1: plain product.
-// Tiles of BMT (128 or 64) token rows x BN weight rows; the waves split them 2 x 2,
-// so a wave holds BMT/64 x 2 MFMA 32x32 blocks per matrix.  BKN: the weights are
-// k-major (element (k, n) at B[k * N + n]); thread t then loads k rows 2p and 2p+1
-// (p = t % (BK/2)) of 16-byte column chunk t / (BK/2) and stores them into the
-// [BN][BK] tile as (k, k+1) pairs, so the tile is the one n-major weights give.
-template <typename T, int NMAT, int BMT, bool BKN>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restrict__ A,
-                                                                const int32_t* __restrict__ offsets,
-                                                                const T* __restrict__ B0, const T* __restrict__ B1,
-                                                                T* __restrict__ C, int L, int N, int K,
-                                                                T* __restrict__ Gs, T* __restrict__ Us) {
-  using G = Gemm<T>;
-  constexpr int BK = G::BK, kLd = G::kLd, FV = G::kFragVec;
-  constexpr int EPV = 16 / int(sizeof(T));     // elements per 16-byte vector
-  constexpr int CPR = BK / EPV;                // 16-byte chunks per tile row (4)
-  constexpr int CPTA = BMT * CPR / kThreads;   // A chunks per thread (2 or 1)
-  constexpr int CPTB = BN * CPR / kThreads;    // B chunks per thread per matrix (2)
-  constexpr int MI = BMT / 64;                 // 32-row blocks per wave
-
-  // ---- which expert and rows this block owns --------------------------------
-  int g = blockIdx.x;
-  int expert = -1, row0 = 0, rows = 0;
-  {
-    int prev = offsets[0];
-    for (int i = 0; i < L; ++i) {
-      const int nxt = offsets[i + 1];
-      const int tiles = (nxt - prev + BMT - 1) / BMT;
-      if (g < tiles) {
-        expert = i;
-        row0 = prev + g * BMT;
-        rows = min(BMT, nxt - row0);
-        break;
-      }
-      g -= tiles;
-      prev = nxt;
-    }
-  }
-  if (expert < 0) return;
-  const int n0 = blockIdx.y * BN;
-  const size_t boff = size_t(expert) * N * K;
-  const T* Bm[2] = {B0 + boff, NMAT > 1 ? B1 + boff : B0 + boff};
-
-  __shared__ __attribute__((aligned(16))) T As[2][BMT * kLd];
-  __shared__ __attribute__((aligned(16))) T Bs[2][NMAT][BN * kLd];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-
-  uint4 ra[CPTA], rb[NMAT][CPTB];
-  constexpr int KP = BK / 2;  // k-major weights: (k, k+1) pairs per tile column
-  static_assert(!BKN || (KP * (BN / EPV) == kThreads && CPTB == 2), "one pair unit per thread");
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < CPTA; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / CPR, col = c % CPR;
-      const int kk = k0 + col * EPV;
-      const int ar = min(r, rows - 1);  // rows past the segment repeat its last row; never stored
-      ra[j] = kk < K ? *reinterpret_cast<const uint4*>(A + size_t(row0 + ar) * K + kk) : zero;
-    }
-    if constexpr (!BKN) {
-#pragma unroll
-      for (int j = 0; j < CPTB; ++j) {
-        const int c = tid + j * kThreads;
-        const int r = c / CPR, col = c % CPR;
-        const int kk = k0 + col * EPV;
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          const int nr = n0 + r;
-          rb[m][j] = (kk < K && nr < N) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(nr) * K + kk) : zero;
-        }
-      }
-    } else {
-      // N is a multiple of 8, so a chunk is wholly inside or wholly past column N
-      const int p = tid % KP, n = n0 + (tid / KP) * EPV, kk = k0 + 2 * p;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          rb[m][h] = (n < N && kk + h < K) ? *reinterpret_cast<const uint4*>(Bm[m] + size_t(kk + h) * N + n) : zero;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < CPTA; ++j) {
-      const int c = tid + j * kThreads;
-      const int r = c / CPR, col = c % CPR;
-      *reinterpret_cast<uint4*>(&As[buf][r * kLd + col * EPV]) = ra[j];
-    }
-    if constexpr (!BKN) {
-#pragma unroll
-      for (int j = 0; j < CPTB; ++j) {
-        const int c = tid + j * kThreads;
-        const int r = c / CPR, col = c % CPR;
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) *reinterpret_cast<uint4*>(&Bs[buf][m][r * kLd + col * EPV]) = rb[m][j];
-      }
-    } else {
-      const int p = tid % KP, c0 = (tid / KP) * EPV;
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const uint32_t a[4] = {rb[m][0].x, rb[m][0].y, rb[m][0].z, rb[m][0].w};
-        const uint32_t b[4] = {rb[m][1].x, rb[m][1].y, rb[m][1].z, rb[m][1].w};
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            // column 2w: the low halves of rows k and k+1, column 2w+1: the high halves
-            *reinterpret_cast<uint32_t*>(&Bs[buf][m][(c0 + 2 * w) * kLd + 2 * p]) = (a[w] & 0xFFFFu) | (b[w] << 16);
-            *reinterpret_cast<uint32_t*>(&Bs[buf][m][(c0 + 2 * w + 1) * kLd + 2 * p]) =
-                (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            *reinterpret_cast<uint2*>(&Bs[buf][m][(c0 + w) * kLd + 2 * p]) = make_uint2(a[w], b[w]);
-        }
-      }
-    }
-  };
-
-  f32x16_t acc[NMAT][MI][2];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.0f;
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int frow = lane & 31;            // row (A) / column (B) inside a 32-block
-  const int fk = 8 * (lane >> 5);        // first of the lane's 8 k values in a 16-k chunk
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int kc = 0; kc < BK / 16; ++kc) {
-      uint4 af[MI][FV], bfr[NMAT][2][FV];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const uint4* p =
-            reinterpret_cast<const uint4*>(&As[buf][(wm * (BMT / 2) + i * 32 + frow) * kLd + kc * 16 + fk]);
-#pragma unroll
-        for (int v = 0; v < FV; ++v) af[i][v] = p[v];
-      }
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint4* p =
-              reinterpret_cast<const uint4*>(&Bs[buf][m][(wn * 64 + j * 32 + frow) * kLd + kc * 16 + fk]);
-#pragma unroll
-          for (int v = 0; v < FV; ++v) bfr[m][j][v] = p[v];
-        }
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) G::mma(af[i], bfr[m][j], acc[m][i][j]);
-    }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: 32x32 accumulator layout, lane -> column (lane & 31),
-  // register r -> row 8*(r/4) + 4*(lane/32) + r%4 ------------------------------
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rt = wm * (BMT / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (rt < rows && col < N) {
-          float v;
-          if constexpr (NMAT == 2) {
-            v = silu(acc[0][i][j][r]) * acc[1][i][j][r];
-            if (Gs != nullptr) {  // training: keep the pre-activations for the backward
-              Gs[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(acc[0][i][j][r]);
-              Us[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(acc[1][i][j][r]);
-            }
-          } else {
-            v = acc[0][i][j][r];
-          }
-          C[size_t(row0 + rt) * N + col] = Elem<T>::from_f32(v);
-        }
-      }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Large-tile bf16 kernel for segments of hundreds of rows and more.
@@ -300,34 +61,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const T* __restr
 // activation tiles to several n-tiles.
 namespace big {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
-
 constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2;
 
-// A weight fragment from a tile stored k-major in LDS (rows of k, n contiguous).
-// gfx950's transposing read ds_read_b64_tr_b16 works on groups of 16 lanes:
-// lane i of a group receives element i % 4 of the 8-byte rows addressed by
-// lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4 of its group, in that order (checked
-// on the GPU).  With lane i of a group addressing row kb + i/4, columns
-// nb + 4(i%4) .. +3, lane i receives column nb + i at rows kb .. kb+3; a second
-// read four rows down gives kb+4 .. kb+7, so the lane holds eight consecutive k
-// of one column: the same register contents as the fragment read from an
-// n-major tile.
-__device__ __forceinline__ bf16x8_t read_kn_frag(const char* p) {
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p + 4 * 256));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// The same from the lane's two addresses (rows kb + i/4 and four rows down) of a
-// block with its own row placement.
-__device__ __forceinline__ bf16x8_t read_kn_frag2(const char* p0, const char* p1) {
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p1));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 constexpr int kRowBytes = BK * 2;              // 128
 constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
@@ -337,8 +72,6 @@ constexpr int kXcds = 8;
 #define MOE_LGKMCNT0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
 bool supported(int K) { return K % BK == 0; }
-// word 3 of a buffer descriptor on this family: 32-bit data format, raw byte addressing
-constexpr int kRsrcFlags = 0x00020000;
 // the direct loads address a weight matrix with 32-bit byte offsets
 bool addressable(int64_t rows, int64_t K) { return rows * K * 2 < (int64_t(1) << 32); }
 
@@ -1291,253 +1024,6 @@ moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, con
 
 }  // namespace big
 
-// ---------------------------------------------------------------------------
-// Skinny kernel for segments of a few rows (decode-sized batches).
-//
-// With a handful of rows per expert the product is bound by streaming the
-// expert weights from HBM, so the work is split over weight rows: one block
-// of four waves owns one expert and 64 consecutive output columns (each wave
-// 16 weight rows, or 16 gate + 16 up rows).  A wave multiplies up to 64 of the
-// expert's token rows at a time (four MFMA 16x16x32 row blocks) and streams
-// its weight rows straight from HBM into registers, eight k-steps of 32 in
-// flight per matrix (16-byte loads; two consecutive steps cover a 128-byte
-// line of each weight row).  The token rows come through the caches.  An
-// expert that received no rows returns before touching its weights.
-namespace skinny {
-
-constexpr int kThreads = 256, kMaxRowBlocks = 4;
-
-bool supported(int K) { return K % 32 == 0; }
-
-// Each wave streams two sets of 16 weight rows: for gate/up the gate and the
-// up rows of the same 16 output columns, for down two adjacent groups of 16
-// output columns.  So a block (four waves) covers 64 gate/up columns or 128
-// down columns.  The k loop is double-buffered in registers: the loads of the
-// next four 32-k steps are in flight while the MFMAs of the current four run.
-template <int NMAT>
-constexpr int cols_per_block() { return NMAT == 2 ? 64 : 128; }
-
-// SAVE (gate/up of the training forward): the gate and up pre-activations go to Gs, Us too.
-// BKN: the weights are k-major (element (k, n) at B[k * N + n]): each lane then loads
-// 16 bytes of one k row (a 32 x 16 block of a stream per step is 32 rows of 32 bytes),
-// the wave parks the block in its own 1 KB of LDS and reads the fragments back with
-// transposing reads, so the MFMAs see the same operands as with n-major weights.
-template <int NMAT, bool SAVE, bool BKN>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                        const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ C, int N, int K, bf16_t* __restrict__ Gs,
-                                                        bf16_t* __restrict__ Us) {
-  constexpr int kWaveCols = NMAT == 2 ? 16 : 32;
-  constexpr int kPipe = 4;
-  const int expert = blockIdx.y;
-  const int seg0 = offsets[expert];
-  const int seg_n = offsets[expert + 1] - seg0;
-  if (seg_n <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col0 = blockIdx.x * cols_per_block<NMAT>() + wave * kWaveCols;  // first output column of this wave
-  if (col0 >= N) return;
-  const size_t boff = size_t(expert) * N * K;
-  const int kg = (lane >> 4) * 8;  // the lane's 8 k values within a step
-  const bf16_t* bs0;
-  const bf16_t* bs1;
-  size_t kstride;  // elements between consecutive k of a lane's stream
-  if constexpr (!BKN) {
-    // stream 0 / 1 weight row of this lane (rows past N repeat row N-1; never stored)
-    const int wrow0 = min(col0 + (lane & 15), N - 1);
-    const int wrow1 = NMAT == 2 ? wrow0 : min(col0 + 16 + (lane & 15), N - 1);
-    bs0 = B0 + boff + size_t(wrow0) * K + kg;
-    bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(wrow1) * K + kg;
-    kstride = 1;
-  } else {
-    // lane l loads k row l/2 of the step, columns c + 8 (l % 2) .. +7 of its stream's 16
-    // (chunks past N re-read the last chunk of the row; never stored)
-    const int c0 = min(col0 + 8 * (lane & 1), N - 8);
-    const int c1 = NMAT == 2 ? c0 : min(col0 + 16 + 8 * (lane & 1), N - 8);
-    bs0 = B0 + boff + size_t(lane >> 1) * N + c0;
-    bs1 = (NMAT == 2 ? B1 : B0) + boff + size_t(lane >> 1) * N + c1;
-    kstride = size_t(N);
-  }
-  // the wave's LDS blocks (k-major weights only): [stream][step] 1 KB each; row r of a
-  // block at 32-byte slot r ^ 4 (r / 8 % 2), so a transposing read's two row quads per
-  // half wave fall in different bank halves
-  __shared__ __attribute__((aligned(1024))) char park[BKN ? 4 * 2 * kPipe * 1024 : 16];
-  char* wpark = park + (BKN ? wave * 2 * kPipe * 1024 : 0);
-  auto slot = [](int r) { return (r ^ (((r >> 3) & 1) << 2)) * 32; };
-  const int woff = slot(lane >> 1) + 16 * (lane & 1);  // this lane's store
-  // its transposing reads: k rows 8 (lane / 16) + (lane % 16) / 4 and four rows down
-  const int roff0 = slot(8 * (lane >> 4) + ((lane & 15) >> 2)) + 8 * (lane & 3);
-  const int roff1 = slot(8 * (lane >> 4) + ((lane & 15) >> 2) + 4) + 8 * (lane & 3);
-
-  for (int m0 = 0; m0 < seg_n; m0 += 16 * kMaxRowBlocks) {
-    const int nrb = min(kMaxRowBlocks, (seg_n - m0 + 15) / 16);
-    // token row of each row block for this lane (rows past the segment repeat its last row)
-    const bf16_t* arow[kMaxRowBlocks];
-#pragma unroll
-    for (int rb = 0; rb < kMaxRowBlocks; ++rb)
-      arow[rb] = A + size_t(seg0 + min(m0 + rb * 16 + (lane & 15), seg_n - 1)) * K + kg;
-    f32x4_t acc[2][kMaxRowBlocks];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int rb = 0; rb < kMaxRowBlocks; ++rb) acc[m][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // two register sets of kPipe k steps: the loads of the next set are in flight
-    // while the MFMAs of the current one run (four steps per set: fewer waves
-    // fit, but each keeps more in flight; same-box A/B on the decode-sized
-    // layer: 0 to -4% per layer against two steps, while capping registers for
-    // more waves per SIMD made it 12% slower)
-    bf16x8_t w0[2][kPipe], w1[2][kPipe], a0[2][kPipe];
-    const int nset = K / (32 * kPipe);
-    auto load_set = [&](int b, int k0) {
-#pragma unroll
-      for (int u = 0; u < kPipe; ++u) {
-        w0[b][u] = *reinterpret_cast<const bf16x8_t*>(bs0 + size_t(k0 + 32 * u) * kstride);
-        w1[b][u] = *reinterpret_cast<const bf16x8_t*>(bs1 + size_t(k0 + 32 * u) * kstride);
-        a0[b][u] = *reinterpret_cast<const bf16x8_t*>(arow[0] + k0 + 32 * u);
-      }
-    };
-    // k-major weights: park the loaded blocks, then read the fragments back transposed
-    auto transpose_set = [&](int b) {
-      if constexpr (BKN) {
-#pragma unroll
-        for (int u = 0; u < kPipe; ++u) {
-          *reinterpret_cast<bf16x8_t*>(wpark + u * 1024 + woff) = w0[b][u];
-          *reinterpret_cast<bf16x8_t*>(wpark + (kPipe + u) * 1024 + woff) = w1[b][u];
-        }
-#pragma unroll
-        for (int u = 0; u < kPipe; ++u) {
-          w0[b][u] = big::read_kn_frag2(wpark + u * 1024 + roff0, wpark + u * 1024 + roff1);
-          w1[b][u] = big::read_kn_frag2(wpark + (kPipe + u) * 1024 + roff0, wpark + (kPipe + u) * 1024 + roff1);
-        }
-      }
-    };
-    auto mma_set = [&](int b, int k0) {
-      transpose_set(b);
-#pragma unroll
-      for (int u = 0; u < kPipe; ++u) {
-#pragma unroll
-        for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-          if (rb < nrb) {
-            const bf16x8_t a = rb == 0 ? a0[b][u] : *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0 + 32 * u);
-            acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w0[b][u], acc[0][rb], 0, 0, 0);
-            acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w1[b][u], acc[1][rb], 0, 0, 0);
-          }
-        }
-      }
-    };
-    if (nset > 0) load_set(0, 0);
-    int set = 0;
-    for (; set + 2 <= nset; set += 2) {
-      load_set(1, (set + 1) * 32 * kPipe);
-      mma_set(0, set * 32 * kPipe);
-      if (set + 2 < nset) load_set(0, (set + 2) * 32 * kPipe);
-      mma_set(1, (set + 1) * 32 * kPipe);
-    }
-    if (set < nset) mma_set(0, set * 32 * kPipe);
-    int k0 = nset * 32 * kPipe;
-    for (; k0 < K; k0 += 32) {
-      bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(bs0 + size_t(k0) * kstride);
-      bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(bs1 + size_t(k0) * kstride);
-      if constexpr (BKN) {
-        *reinterpret_cast<bf16x8_t*>(wpark + woff) = v0;
-        *reinterpret_cast<bf16x8_t*>(wpark + kPipe * 1024 + woff) = v1;
-        v0 = big::read_kn_frag2(wpark + roff0, wpark + roff1);
-        v1 = big::read_kn_frag2(wpark + kPipe * 1024 + roff0, wpark + kPipe * 1024 + roff1);
-      }
-#pragma unroll
-      for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-        if (rb < nrb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow[rb] + k0);
-          acc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, v0, acc[0][rb], 0, 0, 0);
-          acc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, v1, acc[1][rb], 0, 0, 0);
-        }
-      }
-    }
-    // 16x16 layout: lane -> weight row (column of the output) lane & 15,
-    // register i -> token row 4*(lane/16) + i of the row block
-#pragma unroll
-    for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + rb * 16 + 4 * (lane >> 4) + i;
-        if (rb < nrb && r < seg_n) {
-          bf16_t* crow = C + size_t(seg0 + r) * N;
-          if (NMAT == 2) {
-            const int col = col0 + (lane & 15);
-            if (col < N) {
-              crow[col] = f32_to_bf16(silu(acc[0][rb][i]) * acc[1][rb][i]);
-              if constexpr (SAVE) {
-                Gs[size_t(seg0 + r) * N + col] = f32_to_bf16(acc[0][rb][i]);
-                Us[size_t(seg0 + r) * N + col] = f32_to_bf16(acc[1][rb][i]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const int col = col0 + 16 * s + (lane & 15);
-              if (col < N) crow[col] = f32_to_bf16(acc[s][rb][i]);
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
-// bkn: k-major weights (see gemm_kernel)
-template <int NMAT>
-moe_status launch(const char* name, const bf16_t* A, const int32_t* offsets, const bf16_t* B0, const bf16_t* B1,
-                  bf16_t* C, int L, int N, int K, bool bkn, hipStream_t s, bf16_t* Gs = nullptr, bf16_t* Us = nullptr) {
-  const dim3 grid(unsigned((N + cols_per_block<NMAT>() - 1) / cols_per_block<NMAT>()), unsigned(L));
-#define MOE_SKINNY(SAVE_)                                                                                          \
-  do {                                                                                                             \
-    if (bkn)                                                                                                       \
-      MOE_LAUNCH(name, (gemm_kernel<NMAT, SAVE_, true>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us); \
-    else                                                                                                           \
-      MOE_LAUNCH(name, (gemm_kernel<NMAT, SAVE_, false>), grid, dim3(kThreads), 0, s, A, offsets, B0, B1, C, N, K, Gs, Us); \
-  } while (0)
-  if (NMAT == 2 && Gs != nullptr) {
-    MOE_SKINNY(true);
-  } else {
-    MOE_SKINNY(false);
-  }
-#undef MOE_SKINNY
-  return MOE_OK;
-}
-
-}  // namespace skinny
-
-template <typename T, int BMT, bool BKN>
-moe_status launch_bm(const FfnArgs& a) {
-  const moe_layer_desc* d = a.d;
-  const int L = d->local_count, H = d->hidden, I = d->intermediate;
-  const unsigned mslots = unsigned((a.max_pairs + BMT - 1) / BMT + L);
-  MOE_LAUNCH("ffn_gate_up", (grouped_gemm_kernel<T, 2, BMT, BKN>), dim3(mslots, (I + BN - 1) / BN), dim3(kThreads), 0,
-             a.s, static_cast<const T*>(a.x_sorted), a.offsets, static_cast<const T*>(a.w_gate),
-             static_cast<const T*>(a.w_up), static_cast<T*>(a.h), L, I, H, static_cast<T*>(a.g_out),
-             static_cast<T*>(a.u_out));
-  MOE_LAUNCH("ffn_down", (grouped_gemm_kernel<T, 1, BMT, BKN>), dim3(mslots, (H + BN - 1) / BN), dim3(kThreads), 0,
-             a.s, static_cast<const T*>(a.h), a.offsets, static_cast<const T*>(a.w_down),
-             static_cast<const T*>(a.w_down), static_cast<T*>(a.y_sorted), L, H, I, static_cast<T*>(nullptr),
-             static_cast<T*>(nullptr));
-  return MOE_OK;
-}
-
-template <typename T, int BMT>
-moe_status launch_bm(const FfnArgs& a) {
-  return a.d->weight_layout == MOE_WEIGHTS_IN_OUT ? launch_bm<T, BMT, true>(a) : launch_bm<T, BMT, false>(a);
-}
-
-// 64-row tiles when 128-row tiles would leave fewer than two blocks per CU (the
-// fp32 layer's 8 experts x ~1024 rows x 256 columns: 144 blocks of 128 rows)
-template <typename T>
-moe_status launch_t(const FfnArgs& a) {
-  const moe_layer_desc* d = a.d;
-  const int64_t nb = std::min((d->intermediate + BN - 1) / BN, (d->hidden + BN - 1) / BN);
-  if (((a.max_pairs + BM - 1) / BM + d->local_count) * nb < 512) return launch_bm<T, 64>(a);
-  return launch_bm<T, 128>(a);
-}
-
 // large tiles pay off once segments hold a few hundred rows; decode-sized
 // batches (a handful of rows per expert) take the skinny kernel
 bool use_big(const moe_layer_desc* d, int64_t max_pairs) {
@@ -1546,20 +1032,9 @@ bool use_big(const moe_layer_desc* d, int64_t max_pairs) {
 }
 
 moe_status launch_small(const FfnArgs& a) {
-  const moe_layer_desc* d = a.d;
-  const int L = d->local_count, H = d->hidden, I = d->intermediate;
   // decode-sized batches: a few rows per expert, bound by streaming the weights
-  if (d->dtype == MOE_BF16 && a.max_pairs <= int64_t(32) * L && skinny::supported(H) && skinny::supported(I)) {
-    bf16_t* h = static_cast<bf16_t*>(a.h);
-    const bool kn = d->weight_layout == MOE_WEIGHTS_IN_OUT;
-    moe_status st = skinny::launch<2>("ffn_gate_up", static_cast<const bf16_t*>(a.x_sorted), a.offsets,
-                                      static_cast<const bf16_t*>(a.w_gate), static_cast<const bf16_t*>(a.w_up), h, L, I,
-                                      H, kn, a.s, static_cast<bf16_t*>(a.g_out), static_cast<bf16_t*>(a.u_out));
-    if (st != MOE_OK) return st;
-    return skinny::launch<1>("ffn_down", h, a.offsets, static_cast<const bf16_t*>(a.w_down),
-                             static_cast<const bf16_t*>(a.w_down), static_cast<bf16_t*>(a.y_sorted), L, H, I, kn, a.s);
-  }
-  return d->dtype == MOE_BF16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
+  if (skinny_ffn_fits(a.d, a.max_pairs)) return launch_skinny_ffn(a);
+  return launch_general_ffn(a);
 }
 
 }  // namespace

@@ -102,6 +102,10 @@ struct FfnArgs {
 // Scratch of the large-tile path (tile plan; split-K pieces when K is long), else 0.
 size_t ffn_scratch_bytes(const moe_layer_desc* d, int64_t max_pairs);
 moe_status launch_grouped_ffn(const FfnArgs& a);
+// the kernels launch_grouped_ffn picks from (skinny_gemm.hip, general_gemm.hip)
+bool skinny_ffn_fits(const moe_layer_desc* d, int64_t max_pairs);
+moe_status launch_skinny_ffn(const FfnArgs& a);
+moe_status launch_general_ffn(const FfnArgs& a);
 
 struct CombineArgs {
   const moe_layer_desc* d;
