@@ -205,3 +205,16 @@ def test_segment_tails_on_the_large_tile_path():
     err = row_error(y, ref, s.dtype)
     say(f"[parity] segment tails 257/128/129/0/256/384: grouped FFN row error {err:.3g}")
     assert err <= tol(s.dtype)
+
+
+@pytest.mark.parametrize("over", [dict(T=16256, H=128, I=128, E=4, k=2, L=4), dict(T=4096, H=512, I=256, E=8, k=2, L=8),
+                                  dict(T=300, H=136, I=200, E=8, k=2, L=8)],
+                         ids=["ring-128x128-tiles", "ring-64x64-tiles", "general-off-grid"])
+def test_fp32_tile_shapes(over):
+    # the float32 grouped GEMM's tile shapes: 128 x 128 tiles when they fill the CUs in
+    # whole rounds (32512 pairs over 4 experts, N = 128), 64 x 64 tiles for the tiny
+    # layer's shape, and the general kernel for k off the 16-element grid
+    s = synth.spec("tiny_fp32").replace(**over)
+    say(f"[edge] float32 {s}")
+    inp, layer, x, gpu = _run(s)
+    _check(s, inp, gpu)
