@@ -247,6 +247,46 @@ def routing_report(inp, ids_gpu, counts_gpu, dropped: int, P: int, with_oracle: 
     return out
 
 
+def copy_probe(s, P: int) -> dict:
+    """Library copy kernels with the byte mixes of the layer's memory-bound stages:
+    torch.index_select gathering P rows of [T, H] (reads T*H, writes P*H: dispatch_place's
+    mix) and torch.add of two [T, H] halves of a [P, H] buffer (reads P*H, writes T*H:
+    combine's mix, for k = 2).  Eight buffer sets rotate so the 256 MB Infinity Cache holds
+    none of the next call's inputs.  Timed with HIP events per call (median of 20)."""
+    import torch
+    dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    esz = 2 if s.dtype == "bf16" else 4
+    nset = 8
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    xs = [torch.empty((s.T, s.H), dtype=dt, device="cuda").normal_(generator=g) for _ in range(nset)]
+    idx = torch.randperm(P, device="cuda", generator=g) % s.T
+    outs = [torch.empty((P, s.H), dtype=dt, device="cuda") for _ in range(nset)]
+    res = {}
+    for name, fn, rd, wr in (
+            ("gather (dispatch_place mix)", lambda i: torch.index_select(xs[i], 0, idx, out=outs[i]), s.T, P),
+            ("add (combine mix)", lambda i: torch.add(outs[i][:P // 2], outs[i][P // 2:2 * (P // 2)],
+                                                       out=xs[i][:P // 2]), 2 * (P // 2), P // 2)):
+        for i in range(nset):
+            fn(i)
+        torch.cuda.synchronize()
+        ms = []
+        for r in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(r % nset)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        by = (rd + wr) * s.H * esz
+        res[name] = {"us": round(med * 1e3, 2), "bytes": by, "GB/s": round(by / (med * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(by / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del xs, outs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +307,11 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step of the layer: the forward that keeps its activations, "
                          "then the backward on a seeded upstream gradient")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the benchmark, time library copy kernels with the byte mix of dispatch_place "
+                         "(read the token rows once, write each kept pair's row) and of combine (read the "
+                         "pairs' rows, write the token rows) on this workload, buffers rotated past the "
+                         "Infinity Cache; reported under copy_probe")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES bytes (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -484,6 +529,8 @@ def main():
         "kernels": kern,
         "roofline": roof,
     }
+    if args.copy_probe:
+        out["copy_probe"] = copy_probe(s, P)
     out["routing"] = routing_report(inp, ids_h, cnt_h, int(dropped.item()), P, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")

@@ -52,7 +52,7 @@ size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   b += align_up(size_t(nblk) * d->num_experts * 4, 256);
   b += align_up(size_t(nblk) * d->local_count * 4, 256);
   b += align_up(size_t(d->local_count + 1) * 4, 256);
-  if (d->capacity_factor > 0) b += align_up(size_t(n) * 4, 256);
+  if (d->capacity_factor > 0) b += 3 * align_up(size_t(n) * 4, 256);
   return b;
 }
 
@@ -66,7 +66,14 @@ DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
   p += align_up(size_t(nblk) * d->local_count * 4, 256);
   s.pre_off = reinterpret_cast<int32_t*>(p);
   p += align_up(size_t(d->local_count + 1) * 4, 256);
-  s.tmp_sorted = d->capacity_factor > 0 ? reinterpret_cast<int32_t*>(p) : nullptr;
+  const int64_t n = d->num_tokens * d->top_k;
+  if (d->capacity_factor > 0) {
+    s.tmp_sorted = reinterpret_cast<int32_t*>(p);
+    p += align_up(size_t(n) * 4, 256);
+    s.tmp_key = reinterpret_cast<uint32_t*>(p);
+    p += align_up(size_t(n) * 4, 256);
+    s.tmp_final = reinterpret_cast<int32_t*>(p);
+  }
   return s;
 }
 
@@ -131,6 +138,7 @@ __global__ __launch_bounds__(kDispatchThreads) void count_kernel(const int32_t* 
 // ---- scan -------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
 constexpr int kScanGroups = 16;  // chunk ranges per column: short serial prefixes over the range sums
+constexpr int kScanCache = 32;   // chunk counts a thread keeps in registers between the two passes
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_all, int nblk, int E,
                                                             int begin, int L, int64_t cap, int32_t* __restrict__ counts,
@@ -146,9 +154,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   const int lane = tid & 63, wave = tid >> 6;
 
   __shared__ int rsum[kScanThreads];
+  // When every column fits one pass (E <= 1024) and a thread's range of chunks fits
+  // kScanCache registers, the thread loads its counts once, all in flight, and keeps
+  // them for the per-chunk bases below (the histogram was just written by another
+  // kernel, so each dependent round of loads costs a trip past this XCD's L2).
+  const int G1 = min(kScanGroups, kScanThreads / max(1, min(E, kScanThreads)));
+  const int per1 = (nblk + G1 - 1) / G1;
+  const bool cached = E <= kScanThreads && per1 <= kScanCache;
+  int v[kScanCache];
+  if (cached) {
+    const int e = tid % E, g = tid / E;
+    int sum = 0;
+    if (g < G1) {
+      const int b_lo = min(nblk, g * per1), b_hi = min(nblk, b_lo + per1);
+#pragma unroll
+      for (int u = 0; u < kScanCache; ++u) v[u] = b_lo + u < b_hi ? blk_all[size_t(b_lo + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanCache; ++u) sum += v[u];
+      rsum[tid] = sum;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int tot = 0;
+      for (int gg = 0; gg < G1; ++gg) tot += rsum[gg * E + tid];
+      cnt[tid] = tot;
+      counts[tid] = tot;
+    }
+    __syncthreads();
+  }
   // totals per expert: columns in groups of up to 1024; thread t sums column
   // t % Ec over a contiguous range of chunks (coalesced across the columns)
-  for (int c0 = 0; c0 < E; c0 += kScanThreads) {
+  for (int c0 = 0; !cached && c0 < E; c0 += kScanThreads) {
     const int Ec = min(kScanThreads, E - c0);
     const int G = min(kScanGroups, kScanThreads / Ec);
     const int per = (nblk + G - 1) / G;
@@ -205,6 +241,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
 
   // first pre-capacity row of every chunk's pairs of local expert i:
   // pre[i] + sum over earlier chunks of their count of expert begin+i.
+  if (cached) {
+    // the first pass's threads and registers: thread (column e, group g) of a local e
+    const int e = tid % E, g = tid / E;
+    if (g < G1 && e >= begin && e < begin + L) {
+      const int b_lo = min(nblk, g * per1), b_hi = min(nblk, b_lo + per1);
+      int run = pre[e - begin];
+      for (int gg = 0; gg < g; ++gg) run += rsum[gg * E + e];
+#pragma unroll
+      for (int u = 0; u < kScanCache; ++u) {
+        if (b_lo + u < b_hi) blk_base[size_t(b_lo + u) * L + e - begin] = run;
+        run += v[u];
+      }
+    }
+    return;
+  }
   // Columns in groups of up to 1024: thread t takes column t % Lc and a
   // contiguous range of chunks (group t / Lc); range sums go through LDS.
   for (int c0 = 0; c0 < L; c0 += kScanThreads) {
@@ -231,14 +282,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
 }
 
 // ---- scatter ----------------------------------------------------------------
-// CAP: the positions are pre-capacity rows in tmp_sorted; the capacity kernel
-// finishes pair_row for local pairs.
+// Order-preserving key of a float32 logit (larger logit -> larger key); -0.0
+// and +0.0 map to one key because they compare equal.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// CAP: the positions are pre-capacity rows in tmp_sorted, with each pair's logit
+// key beside it in tmp_key (so the capacity cut reads its segment's keys in
+// order); pair_row holds the pre-capacity row until the gather resolves it.
 template <bool CAP>
 __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t* __restrict__ ids, int64_t n_pairs,
                                                                    int begin, int L, int chunk,
                                                                    const int32_t* __restrict__ blk_base,
                                                                    int32_t* __restrict__ out_sorted,
-                                                                   int32_t* __restrict__ pair_row) {
+                                                                   int32_t* __restrict__ pair_row,
+                                                                   const float* __restrict__ topk_logit,
+                                                                   uint32_t* __restrict__ tmp_key) {
   extern __shared__ int32_t sh[];
   int32_t* run = sh;       // [L]      next row of each local expert for this block
   int32_t* cnt = sh + L;   // [4][L]   pairs of each expert in each wave of this round
@@ -264,7 +326,8 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
       int pos = run[li] + int(__popcll(lower));
       for (int w = 0; w < wave; ++w) pos += cnt[w * L + li];
       out_sorted[pos] = int32_t(p);
-      if (!CAP) pair_row[p] = pos;
+      pair_row[p] = pos;
+      if (CAP) tmp_key[pos] = logit_key(topk_logit[p]);
     } else if (valid) {
       pair_row[p] = -1;
     }
@@ -283,60 +346,56 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
 }
 
 // ---- capacity -----------------------------------------------------------------
-// Order-preserving key of a float32 logit (larger logit -> larger key); -0.0
-// and +0.0 map to one key because they compare equal.
-__device__ __forceinline__ uint32_t logit_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) == 0) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 constexpr int kCapThreads = 1024;
 constexpr int kCapPerThread = 32;  // register-resident keys per thread (segments up to 32768 pairs)
 constexpr int kCapWaves = kCapThreads / 64;
 constexpr int kCapSlots = kCapPerThread * kCapWaves;  // (register, wave) slots in segment order
+constexpr int kCapBins = 4096;                        // 12-bit radix digits
 
-// Finds the digit (bits [shift, shift+8) of keys matching `prefix` on `mask`)
-// at which the count from the largest digit down reaches `want`; the block's
-// histogram is in hist[256].  Returns the digit and leaves in *left how many
-// of the wanted keys still have to come from that digit.  Wave 0 does a
-// suffix scan over the 256 bins (4 per lane); the result goes through LDS.
-__device__ void pick_digit(const int* hist, int want, uint32_t* s_digit, int* s_want) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    // lane L owns bins 255-4L .. 252-4L (largest digits first)
-    int c[4];
-    int tot = 0;
+// The digit of a radix-select pass: hist[0..nbins) counts the candidate keys by
+// digit; the wanted key is the want-th largest of them.  Thread t owns bins
+// nbins-1-4t .. nbins-4-4t (largest digits first); a block scan of the owners'
+// sums finds the owner whose bins reach `want`.  Leaves the digit in *s_digit and,
+// in *s_want, how many of the wanted keys still have to come from it.  Every
+// thread of the block must call it.
+__device__ void pick_digit(const int* hist, int nbins, int want, int* wsum, uint32_t* s_digit, int* s_want) {
+  const int t = threadIdx.x;
+  int c[4], tot = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bin = nbins - 1 - 4 * t - q;
+    c[q] = bin >= 0 ? hist[bin] : 0;
+    tot += c[q];
+  }
+  int all;
+  int before = block_exclusive_scan(tot, wsum, &all);  // keys in larger digits than this thread's bins
+  if (before < want && before + tot >= want) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      c[q] = hist[255 - 4 * lane - q];
-      tot += c[q];
-    }
-    const int incl = wave_inclusive_scan(tot);
-    int before = incl - tot;  // keys in larger digits than this lane's bins
-    // the first lane whose range reaches `want` holds the digit
-    const uint64_t hit = __ballot(before < want && incl >= want);
-    if (hit != 0 && lane == __ffsll((unsigned long long)hit) - 1) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (before + c[q] >= want) {
-          *s_digit = uint32_t(255 - 4 * lane - q);
-          *s_want = want - before;
-          break;
-        }
-        before += c[q];
+      if (before + c[q] >= want) {
+        *s_digit = uint32_t(nbins - 1 - 4 * t - q);
+        *s_want = want - before;
+        break;
       }
+      before += c[q];
     }
   }
 }
 
+// One block per local expert.  The pre-capacity segment of expert i is rows
+// [pre_off[i], pre_off[i+1]) of tmp_sorted (pair ids, in pair order) and tmp_key
+// (their logit keys).  An expert within capacity keeps every pair; otherwise the
+// cap pairs with the largest keys are kept, equal keys in segment (= token) order.
+// Writes sorted_pairs for the kept pairs (in segment order from offsets[i]) and,
+// for every pre-capacity row, its final row or -1 in tmp_final: every access is in
+// segment order, and the gather resolves pair_row through tmp_final.
 __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ tmp_sorted,
+                                                               const uint32_t* __restrict__ tmp_key,
                                                                const int32_t* __restrict__ pre_off,
-                                                               const int32_t* __restrict__ offsets,
-                                                               const float* __restrict__ topk_logit, int cap,
+                                                               const int32_t* __restrict__ offsets, int cap,
                                                                int32_t* __restrict__ sorted_pairs,
-                                                               int32_t* __restrict__ pair_row) {
-  __shared__ int hist[256];
+                                                               int32_t* __restrict__ tmp_final) {
+  __shared__ int hist[kCapBins];
   __shared__ int wsum[kCapThreads / 64];
   __shared__ int slot_cnt[kCapSlots];
   __shared__ uint32_t s_digit;
@@ -350,46 +409,49 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
 
   if (n <= cap) {
     for (int r = tid; r < n; r += kCapThreads) {
-      const int p = seg[r];
-      sorted_pairs[out0 + r] = p;
-      pair_row[p] = out0 + r;
+      sorted_pairs[out0 + r] = seg[r];
+      tmp_final[a + r] = out0 + r;
     }
     return;
   }
 
   if (cap == 0) {  // nothing is kept
-    for (int r = tid; r < n; r += kCapThreads) pair_row[seg[r]] = -1;
+    for (int r = tid; r < n; r += kCapThreads) tmp_final[a + r] = -1;
     return;
   }
 
   // element r = j*1024 + tid of the segment sits in this thread's register j
   // (coalesced loads; segment order is j-major, then wave, then lane)
   const int lane = tid & 63, wave = tid >> 6;
-  int pid[kCapPerThread];
+  bool in[kCapPerThread];
   uint32_t key[kCapPerThread];
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
     const int r = j * kCapThreads + tid;
-    pid[j] = r < n ? seg[r] : -1;
+    in[j] = r < n;
+    key[j] = in[j] ? tmp_key[a + r] : 0u;
   }
-#pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j) key[j] = pid[j] >= 0 ? logit_key(topk_logit[pid[j]]) : 0u;
 
-  // radix select, most significant byte first: threshold key thr of the cap-th
-  // largest key, and how many keys equal to thr are still wanted
+  // radix select of the cap-th largest key, 12-bit digits (bits 31..20, 19..8) then
+  // 8 bits: float logits share a few exponents, and 12-bit leading digits spread
+  // them over tens of bins where 8-bit ones leave a handful (and every lane of a
+  // wave adding to the same bin)
   uint32_t prefix = 0, mask = 0;
   int want = cap;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += kCapThreads) hist[b] = 0;
+  const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
+#pragma unroll
+  for (int ps = 0; ps < 3; ++ps) {
+    const int shift = shifts[ps], nbins = 1 << widths[ps];
+    for (int b = tid; b < nbins; b += kCapThreads) hist[b] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kCapPerThread; ++j)
-      if (pid[j] >= 0 && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 0xFFu], 1);
+      if (in[j] && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & uint32_t(nbins - 1)], 1);
     __syncthreads();
-    pick_digit(hist, want, &s_digit, &s_want);
+    pick_digit(hist, nbins, want, wsum, &s_digit, &s_want);
     __syncthreads();
     prefix |= s_digit << shift;
-    mask |= 0xFFu << shift;
+    mask |= uint32_t(nbins - 1) << shift;
     want = s_want;
     __syncthreads();
   }
@@ -401,7 +463,7 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
   uint64_t eqm[kCapPerThread];
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    eqm[j] = __ballot(pid[j] >= 0 && key[j] == thr);
+    eqm[j] = __ballot(in[j] && key[j] == thr);
     if (lane == 0) slot_cnt[j * kCapWaves + wave] = int(__popcll(eqm[j]));
   }
   __syncthreads();
@@ -416,10 +478,9 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
   const uint64_t below = lanemask_lt();
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    const bool in = pid[j] >= 0;
-    const bool eq = in && key[j] == thr;
+    const bool eq = in[j] && key[j] == thr;
     const int eq_before = slot_cnt[j * kCapWaves + wave] + int(__popcll(eqm[j] & below));
-    keepm[j] = __ballot(in && (key[j] > thr || (eq && eq_before < need_eq)));
+    keepm[j] = __ballot(in[j] && (key[j] > thr || (eq && eq_before < need_eq)));
   }
   __syncthreads();
 #pragma unroll
@@ -434,13 +495,14 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    if (pid[j] < 0) continue;
+    if (!in[j]) continue;
+    const int r = j * kCapThreads + tid;
     if ((keepm[j] >> lane) & 1u) {
       const int pos = out0 + slot_cnt[j * kCapWaves + wave] + int(__popcll(keepm[j] & below));
-      sorted_pairs[pos] = pid[j];
-      pair_row[pid[j]] = pos;
+      sorted_pairs[pos] = seg[r];
+      tmp_final[a + r] = pos;
     } else {
-      pair_row[pid[j]] = -1;
+      tmp_final[a + r] = -1;
     }
   }
 }
@@ -451,12 +513,18 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
 // however many experts a token picked.
 constexpr int kGatherTokensPerBlock = 4;
 
-__global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__ x, const int32_t* __restrict__ pair_row,
-                                                     int64_t ntok, int k, int vec_per_row, u32x4_t* __restrict__ xs) {
+// After the capacity cut pair_row holds each local pair's pre-capacity row; the
+// gather first resolves it through tmp_final (final row, or -1 if the pair was cut)
+// and writes the final pair_row.
+__global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__ x, int32_t* __restrict__ pair_row,
+                                                     const int32_t* __restrict__ tmp_final, int64_t ntok, int k,
+                                                     int vec_per_row, u32x4_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * kGatherTokensPerBlock + (threadIdx.x >> 6);
   if (t >= ntok) return;
-  const int my_row = lane < k ? pair_row[t * k + lane] : -1;
+  int my_row = lane < k ? pair_row[t * k + lane] : -1;
+  if (my_row >= 0) my_row = tmp_final[my_row];
+  if (lane < k) pair_row[t * k + lane] = my_row;
   // destinations as a bit mask over slots (k <= 32)
   const uint64_t kept = __ballot(my_row >= 0);
   if (kept == 0) return;
@@ -692,12 +760,12 @@ moe_status launch_dispatch(const DispatchArgs& a) {
   if (cap) {
     const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
     MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
-               begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row);
-    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), 0, a.s, a.scr.tmp_sorted, a.scr.pre_off,
-               a.offsets, a.topk_logit, int(a.capacity), a.sorted_pairs, a.pair_row);
+               begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
+    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), 0, a.s, a.scr.tmp_sorted,
+               a.scr.tmp_key, a.scr.pre_off, a.offsets, int(a.capacity), a.sorted_pairs, a.scr.tmp_final);
     const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
     MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const u32x4_t*>(a.x), a.pair_row,
-               d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
+               a.scr.tmp_final, d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
   } else {
     const size_t lds = (size_t(L) * (1 + kDispatchThreads / 64) + size_t(chunk)) * 4;
     auto kern = fused ? place_kernel<true> : place_kernel<false>;
