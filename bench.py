@@ -123,13 +123,19 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
     return 0.0, 0.0
 
 
-def source_digest(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    """First 16 hex digits of the SHA-256 of the named files' bytes, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str, training: bool = False):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they still match the source
-    (training-step runs are recorded under their own keys: their kernels are other instantiations)."""
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel's source file and
+    the local headers it builds on still match the recorded digest (training-step runs are recorded
+    under their own keys: their kernels are other instantiations)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -137,10 +143,10 @@ def traffic_for(kernel: str, workload: str, training: bool = False):
         rec = json.load(open(p)).get(f"{workload}:{kernel}" + (":training" if training else ""))
     except (OSError, ValueError):
         return None
-    if not rec:
+    if not rec or not isinstance(rec.get("sources"), list):
         return None
-    src = os.path.join(ROOT, "expert_token_dispatch_amd", "csrc", rec["source"])
-    if not os.path.exists(src) or source_digest(src) != rec["source_sha"]:
+    srcs = [os.path.join(ROOT, "expert_token_dispatch_amd", "csrc", f) for f in rec["sources"]]
+    if not all(os.path.exists(f) for f in srcs) or source_digest(srcs) != rec["source_sha"]:
         return None
     return rec["bytes_per_launch"]
 
