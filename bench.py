@@ -293,6 +293,73 @@ def copy_probe(s, P: int) -> dict:
     return res
 
 
+def gemm_probe(s, P: int) -> dict:
+    """The library's grouped FFN and the vendor library on the dense products with the grouped
+    products' flops: one expert holding all P rows ([P, H] through gate/up [2I, H] and down
+    [H, I]), first through this library (offsets [0, P]; its gate/up also applies SwiGLU and
+    writes [P, I]), then torch.matmul (hipBLASLt) on the same shapes ([P, H] x [H, 2I] and
+    [P, I] x [I, H], bf16 out, float32 accumulation).  A dense product has no segment tails
+    and reads one weight matrix instead of L.  Timed with HIP events per call (median of 10)."""
+    import torch
+    import synth
+    import expert_token_dispatch_amd as etd
+    from expert_token_dispatch_amd.layer import MoELayer
+    if s.dtype != "bf16":
+        return {}
+    res = {}
+    d1 = synth.spec(s.name, T=P, E=1, k=1, local_begin=0, L=1, capacity_factor=0.0)
+    lay = MoELayer.from_host(etd.make_desc(d1.T, d1.H, d1.I, 1, 1, 0, 1, 0.0, "bf16"), synth.make_layer(d1))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    xs = torch.empty((P, s.H), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    offs = torch.tensor([0, P], dtype=torch.int32, device="cuda")
+    hip = HipEvents()
+    for _ in range(2):
+        lay.grouped_ffn(xs, offs)
+    torch.cuda.synchronize()
+    per = {}
+    for _ in range(10):
+        ev = hip.create(16)
+        etd.moe_profile_events(ev)
+        lay.grouped_ffn(xs, offs)
+        etd.moe_profile_events(None)
+        torch.cuda.synchronize()
+        for i in range(etd.moe_profile_kernel_count()):
+            per.setdefault(etd.moe_profile_kernel_name(i), []).append(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]))
+        hip.destroy(ev)
+    flops = {"ffn_gate_up": 4.0 * P * s.H * s.I, "ffn_down": 2.0 * P * s.H * s.I}
+    for n, ts in per.items():
+        med = sorted(ts)[len(ts) // 2]
+        e = {"us": round(med * 1e3, 2)}
+        if n in flops:
+            tf = flops[n] / (med * 1e-3) / 1e12
+            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)})
+        res[f"library {n}, one expert of {P} rows"] = e
+    del lay, xs
+    for name, M, N, K in (("gate_up", P, 2 * s.I, s.H), ("down", P, s.H, s.I)):
+        a = torch.empty((M, K), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+        w = torch.empty((N, K), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            torch.matmul(a, w.t(), out=c)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, w.t(), out=c)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        tf = 2.0 * M * N * K / (med * 1e-3) / 1e12
+        res[f"hipBLASLt {name} [{M}x{K}]x[{K}x{N}]"] = {"us": round(med * 1e3, 2), "TFLOP/s": round(tf, 1),
+                                                        "mfma_frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        del a, w, c
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +385,10 @@ def main():
                          "(read the token rows once, write each kept pair's row) and of combine (read the "
                          "pairs' rows, write the token rows) on this workload, buffers rotated past the "
                          "Infinity Cache; reported under copy_probe")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="after the benchmark, time the library's grouped FFN on one expert holding all the "
+                         "pairs' rows and torch.matmul (hipBLASLt) on the same dense products; reported under "
+                         "gemm_probe")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES bytes (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -537,6 +608,8 @@ def main():
     }
     if args.copy_probe:
         out["copy_probe"] = copy_probe(s, P)
+    if args.gemm_probe:
+        out["gemm_probe"] = gemm_probe(s, P)
     out["routing"] = routing_report(inp, ids_h, cnt_h, int(dropped.item()), P, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
