@@ -36,11 +36,16 @@ def log(*a):
 
 
 class HipEvents:
-    """hipEvent_t handles through the HIP runtime that torch already loaded."""
+    """hipEvent_t handles through the HIP runtime that torch already loaded.  They are created
+    timing-only (hipEventDisableSystemFence): recording one does not write back and invalidate
+    the caches, which would otherwise add a few microseconds to every kernel the events bracket
+    (most for kernels that leave much dirty data in L2)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
@@ -48,8 +53,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
 
