@@ -559,10 +559,15 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4_t* __restrict__
 // mixtral-like layer 36.6 us against 36.8 and 37.8) and large enough that a small
 // batch still spreads its row copies over ~256 CUs (a decode batch of one
 // chunk: 64 blocks of one token each).
-constexpr int kMinPlaceSplit = 8, kMaxPlaceSplit = kDispatchTokens;
-int place_split(int nblk) {  // power of two, kDispatchTokens divisible by it
+constexpr int kMinPlaceSplit = 2, kMaxPlaceSplit = kDispatchTokens;
+// Blocks per chunk: a power of two (kDispatchTokens divisible by it) giving about 1024 blocks.
+// More blocks copy in smaller pieces and, fused, each re-reads the chunk histograms for its
+// bases; fewer leave the copy too few loads in flight (measured on the gpt-oss-like share,
+// 256 chunks: 2048 blocks 24.4 us, 1024 21.8, 512 23.2; mixtral_like, 128 chunks: 1024
+// blocks 35.1 us, 512 35.6, 2048 37.0).
+int place_split(int nblk) {
   int s = kMinPlaceSplit;
-  while (s < kMaxPlaceSplit && int64_t(nblk) * s < 256) s *= 2;
+  while (s < kMaxPlaceSplit && int64_t(nblk) * s < 1024) s *= 2;
   return s;
 }
 // With few chunks and experts the place blocks find their own bases: every
@@ -573,7 +578,7 @@ constexpr int kFuseEntries = 65536;  // chunks x experts up to which the scan is
 // FUSED: run[i] = (pairs of local experts before i) + (pairs of local expert i
 // in earlier chunks), from the chunk histograms; block 0 also writes counts,
 // offsets and the (zero) drop count.  Otherwise blk_base holds them.
-template <bool FUSED>
+template <bool FUSED, int kUnroll>
 __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* __restrict__ ids, int64_t ntok, int k,
                                                                  int begin, int L, const int32_t* __restrict__ blk_base,
                                                                  const int32_t* __restrict__ blk_all, int nblk, int E,
@@ -637,29 +642,20 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
       }
       carry += all;
     }
-    if (blockIdx.x == 0) {
-      if (tid == 0) {
-        offsets[L] = carry;
-        if (num_dropped != nullptr) *num_dropped = 0;
-      }
-      // experts outside the local range (their totals were not needed above), grouped like the local ones
-      for (int e0 = 0; e0 < E; e0 += kDispatchThreads) {
-        const int Eg = min(kDispatchThreads, E - e0);
-        const int G = kDispatchThreads / Eg;
-        const int el = tid % Eg, g = tid / Eg;
-        const int e = e0 + el;
-        const bool outside = e < begin || e >= begin + L;
-        int tot = 0;
-        if (g < G && outside) tot = column_sum(blk_all + e, size_t(E), g, nblk, G);
-        __syncthreads();
-        ptot[tid] = tot;
-        __syncthreads();
-        if (tid < Eg && (e0 + tid < begin || e0 + tid >= begin + L)) {
-          int s = 0;
-          for (int gg = 0; gg < G; ++gg) s += ptot[gg * Eg + tid];
-          counts[e0 + tid] = s;
-        }
-      }
+    if (blockIdx.x == 0 && tid == 0) {
+      offsets[L] = carry;
+      if (num_dropped != nullptr) *num_dropped = 0;
+    }
+    // the totals of the experts outside the local range (not needed above): one expert per
+    // block, the block's threads splitting its column of chunk counts (one block summing
+    // them all would be the last to finish)
+    for (int e = int(blockIdx.x); e < E; e += int(gridDim.x)) {
+      if (e >= begin && e < begin + L) continue;
+      int tot = 0;
+      for (int b = tid; b < nblk; b += kDispatchThreads) tot += blk_all[size_t(b) * E + e];
+      int all;
+      (void)block_exclusive_scan(tot, wsum, &all);
+      if (tid == 0) counts[e] = all;
     }
   } else {
     for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
@@ -709,7 +705,6 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
   const int tw0 = part * tpp + (tpp >= kWaves ? wave * tpw : wave / wpt);
   const int cper = (vec_per_row + wpt - 1) / wpt;
   const int c_lo = (wave % wpt) * cper, c_hi = min(vec_per_row, c_lo + cper);
-  constexpr int kUnroll = 4;
   for (int tt = tw0; tt < tw0 + tpw && tt < ntk; ++tt) {
     const int my_row = lane < k ? pos[tt * k + lane] : -1;
     const uint64_t kept = __ballot(my_row >= 0);
@@ -768,13 +763,22 @@ moe_status launch_dispatch(const DispatchArgs& a) {
                a.scr.tmp_final, d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));
   } else {
     const size_t lds = (size_t(L) * (1 + kDispatchThreads / 64) + size_t(chunk)) * 4;
-    auto kern = fused ? place_kernel<true> : place_kernel<false>;
+    // 16-byte slices per lane and pass over a row: 4, or 6 when the row then fits fewer, fuller
+    // passes (a 2880-wide bf16 row: one pass of 384 instead of two of 256; 21.6 -> 20.2 us on the
+    // gpt-oss-like share)
+    const int split = place_split(nblk);
+    const int tpp = kDispatchTokens / split, waves = kDispatchThreads / 64;
+    const int wpt = tpp >= waves ? 1 : waves / tpp;  // waves per token, as in the kernel
+    const int cper = (vec_per_row + wpt - 1) / wpt;
+    const auto waste = [&](int u) { return (cper + 64 * u - 1) / (64 * u) * 64 * u - cper; };
+    const bool six = waste(6) < waste(4);
+    auto kern = fused ? (six ? place_kernel<true, 6> : place_kernel<true, 4>)
+                      : (six ? place_kernel<false, 6> : place_kernel<false, 4>);
     if (lds > 65536) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
       if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_place: LDS attribute: %s", hipGetErrorString(e));
     }
-    const int split = place_split(nblk);
     MOE_LAUNCH("dispatch_place", kern, dim3(unsigned(nblk) * split), dim3(kDispatchThreads), lds, a.s,
                a.topk_ids, d->num_tokens, d->top_k, begin, L, a.scr.blk_base, a.scr.blk_all, nblk, E, a.counts,
                a.offsets, a.num_dropped, a.sorted_pairs, a.pair_row, static_cast<const u32x4_t*>(a.x), vec_per_row,
