@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstring>
 
 #include "ffn_common.h"
 #include "kernels.h"
@@ -991,7 +992,10 @@ moe_status launch_nws(const char* name, const bf16_t* A, const int32_t* offsets,
   MOE_LAUNCH(name, kern, dim3(unsigned(per_xcd * kXcds)), dim3(kThreads), lds, s, A, offsets, B0, B1, C, L, N, K, kcat,
              int(max_pairs), tpre, cpx, smax, parts, Gs, Us);
   if (smax > 1) {
-    const char* fname = NMAT == 2 ? "ffn_gate_up_fixup" : "ffn_down_fixup";
+    const char* fname = std::strcmp(name, "ffn_gate_up") == 0         ? "ffn_gate_up_fixup"
+                        : std::strcmp(name, "ffn_gate_up_dgrad") == 0 ? "ffn_gate_up_dgrad_fixup"
+                        : std::strcmp(name, "ffn_down") == 0          ? "ffn_down_fixup"
+                                                                       : "ffn_fixup";
     MOE_LAUNCH(fname, (fixup_kernel<NMAT, NW, EP>), dim3(unsigned(kXcds * kMaxTail * kFixSub)), dim3(kThreads), 0, s,
                offsets, C, L, N, K, tpre, cpx, smax, static_cast<const float*>(parts), Gs, Us);
   }
