@@ -266,6 +266,7 @@ struct Shape {
   static constexpr int kA = WIDE ? BM / 2 : BM;          // A rows
   static constexpr int kB = WIDE ? 2 * BNE : BNE;        // B rows
   static constexpr int kStageA = kA * kRowBytes;
+  static constexpr int kStageB = kB * kRowBytes;
   static constexpr int kStage = (kA + kB) * kRowBytes;   // 64 KB regular, 80 KB wide
   static constexpr int kLdA = kA / (8 * NW), kLdB = kB / (8 * NW);  // 1 KB direct loads per wave per stage
   static constexpr int kLd = kLdA + kLdB;
@@ -273,6 +274,8 @@ struct Shape {
   __device__ static int wn(int wave) { return WIDE ? wave : wave % (NW / 2); }
 };
 constexpr size_t kLoopLdsMax = size_t(kStages) * Shape<true, 4>::kStage;  // 160 KB
+// a regular tile's two A slots and three B slots fit in the same space
+static_assert(2 * Shape<false, 4>::kStageA + 3 * Shape<false, 4>::kStageB <= int(kLoopLdsMax), "regular ring");
 
 // ---- epilogue.  The products were formed as (weight rows) x (token rows), so
 // in the 32x32 accumulator layout lane l holds token row l & 31 and register
@@ -580,12 +583,25 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
       b_vo[j] = (uint32_t(krow) * uint32_t(ldb) + uint32_t(col)) * 2u;
     }
   }
+  // LDS stages.  A wide tile keeps two whole stages (A and B rows of a step together).
+  // A regular tile keeps its A rows in two slots and its B rows in three (2 x 32 + 3 x
+  // 32 KB): the weight rows, which miss L2 far more often than the activation rows,
+  // are asked for two steps before they are used instead of one.  a_slot(s) is where
+  // stage s's A rows start; b_slot(s) + kStageA is where its B rows start (the B
+  // fragment offsets count from a whole stage's base).
+  constexpr bool kRing3 = !WIDE;
+  const auto a_slot = [&](int st) -> char* {
+    return kRing3 ? lds + (st & 1) * S::kStageA : lds + (st % kStages) * S::kStage;
+  };
+  const auto b_slot = [&](int st) -> char* {
+    return kRing3 ? lds + S::kStageA + (st % 3) * S::kStageB : lds + (st % kStages) * S::kStage;
+  };
 // loads q0..q1-1 of stage kt_, in the order A0 B0 A1 B1 ... (then the B rows
 // past the last A block)
 #define MOE_ISSUE(kt_, q0_, q1_)                                                                            \
   do {                                                                                                      \
-    char* sa_ = lds + ((kt_) % kStages) * S::kStage + (S::kLdA * wave) * 1024;                              \
-    char* sb_ = lds + ((kt_) % kStages) * S::kStage + S::kStageA + (S::kLdB * wave) * 1024;                 \
+    char* sa_ = a_slot(kt_) + (S::kLdA * wave) * 1024;                                                      \
+    char* sb_ = b_slot(kt_) + S::kStageA + (S::kLdB * wave) * 1024;                                         \
     const int s_ = kb + (kt_);                                                                              \
     const uint32_t k0_ = uint32_t(s_) * (AKM ? uint32_t(BK * 2) * uint32_t(lda) : uint32_t(BK * 2));          \
     const bool sec_ = kcat > 0 && s_ >= kcat;                                                               \
@@ -598,6 +614,25 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sec_ ? b_rsrc2 : b_rsrc, (lds_ptr_t)(sb_ + j_ * 1024), 16, b_vo[j_], \
                                                  kbo_, 0, 0);                                              \
     }                                                                                                       \
+  } while (0)
+
+// all A loads (MOE_ISSUE_A) or all B loads (MOE_ISSUE_B) of stage kt_
+#define MOE_ISSUE_A(kt_)                                                                                    \
+  do {                                                                                                      \
+    char* sa_ = a_slot(kt_) + (S::kLdA * wave) * 1024;                                                      \
+    const uint32_t k0_ = uint32_t(kb + (kt_)) * (AKM ? uint32_t(BK * 2) * uint32_t(lda) : uint32_t(BK * 2)); \
+    _Pragma("unroll") for (int j_ = 0; j_ < S::kLdA; ++j_)                                                  \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + j_ * 1024), 16, a_vo[j_], k0_, 0, 0);  \
+  } while (0)
+#define MOE_ISSUE_B(kt_)                                                                                    \
+  do {                                                                                                      \
+    char* sb_ = b_slot(kt_) + S::kStageA + (S::kLdB * wave) * 1024;                                         \
+    const int s_ = kb + (kt_);                                                                              \
+    const bool sec_ = kcat > 0 && s_ >= kcat;                                                               \
+    const uint32_t kbo_ = uint32_t(sec_ ? s_ - kcat : s_) * (BKN ? uint32_t(BK * 2) * uint32_t(ldb) : uint32_t(BK * 2)); \
+    _Pragma("unroll") for (int j_ = 0; j_ < S::kLdB; ++j_)                                                  \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sec_ ? b_rsrc2 : b_rsrc, (lds_ptr_t)(sb_ + j_ * 1024), 16, b_vo[j_], \
+                                               kbo_, 0, 0);                                                 \
   } while (0)
 
   f32x16_t acc[4][NB];
@@ -641,15 +676,15 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
     }
   }
   bf16x8_t fa[2][4], fb[2][NB];
-#define MOE_LOADF(buf_, st_, kc_)                                                                         \
+#define MOE_LOADF(buf_, sta_, stb_, kc_)                                                                  \
   do {                                                                                                    \
     const int co_ = ((2 * (kc_) + g) ^ sw) * 16;                                                          \
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                         \
-      fa[buf_][i] = AKM ? read_kn_frag((st_) + aoffs[i] + (kc_) * 16 * 256)                                \
-                        : *reinterpret_cast<const bf16x8_t*>((st_) + aoffs[i] + co_);                      \
+      fa[buf_][i] = AKM ? read_kn_frag((sta_) + aoffs[i] + (kc_) * 16 * 256)                               \
+                        : *reinterpret_cast<const bf16x8_t*>((sta_) + aoffs[i] + co_);                     \
     _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                        \
-      fb[buf_][j] = BKN ? read_kn_frag((st_) + boffs[j] + (kc_) * 16 * 256)                                \
-                        : *reinterpret_cast<const bf16x8_t*>((st_) + boffs[j] + co_);                      \
+      fb[buf_][j] = BKN ? read_kn_frag((stb_) + boffs[j] + (kc_) * 16 * 256)                               \
+                        : *reinterpret_cast<const bf16x8_t*>((stb_) + boffs[j] + co_);                     \
   } while (0)
 #define MOE_MMA(buf_)                                                                                     \
   do {                                                                                                    \
@@ -686,6 +721,7 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
   // of an XCD hit L2 together, and the second half still has three chunks to
   // land before the barrier that waits for it.
   constexpr int kHalf = S::kLd / 2;
+  static_assert(!kRing3 || (S::kLdA == kHalf && S::kLdB == kHalf), "a regular tile's A and B loads are the halves");
   // a chunk that also issues half a refill: its fragment reads first, then the loads
   // spread over its 4 * NB MFMAs
 #define MOE_CHUNK_LOADS()                                                                                 \
@@ -704,52 +740,72 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
       }                                                                                                   \
     }                                                                                                     \
   } while (0)
-  MOE_ISSUE(0, 0, S::kLd);
-  if (nks > 1) {
-    MOE_ISSUE(1, 0, kHalf);
-    MOE_VMCNT(kHalf);  // stage 0 landed
+  // Load order (the vector-memory counter retires loads in issue order).  Wide tile:
+  // stage 0, the first half of stage 1; each iteration kt then issues the second half of
+  // stage kt+1 at its top and the first half of stage kt+2 after its barrier, and the
+  // barrier waits for everything (stage kt+1).  Regular tile: A0 B0 B1 A1; iteration kt
+  // issues B(kt+2) at its top and A(kt+2) after its barrier, so at the barrier only
+  // B(kt+2) may still be in flight (A(kt+1) went out before it, B(kt+1) an iteration
+  // earlier).  Near the end a stage past the last repeats the last one (same bytes
+  // into the same slot).
+  if constexpr (kRing3) {
+    MOE_ISSUE_A(0);
+    MOE_ISSUE_B(0);
+    MOE_ISSUE_B(min(1, nks - 1));
+    MOE_ISSUE_A(min(1, nks - 1));
+    MOE_VMCNT(S::kLdA + S::kLdB);  // stage 0 landed
   } else {
-    MOE_VMCNT(0);
+    MOE_ISSUE(0, 0, S::kLd);
+    if (nks > 1) {
+      MOE_ISSUE(1, 0, kHalf);
+      MOE_VMCNT(kHalf);  // stage 0 landed
+    } else {
+      MOE_VMCNT(0);
+    }
   }
   block_barrier();
-  MOE_LOADF(0, lds, 0);
-  // every iteration has a next stage; the refill issued in it is stage kt+2,
-  // or (near the end) a repeat of the last stage into the free slot
+  MOE_LOADF(0, a_slot(0), b_slot(0), 0);
   for (int kt = 0; kt + 1 < nks; ++kt) {
-    const char* st = lds + (kt % kStages) * S::kStage;
-    MOE_LOADF(1, st, 1);
-    MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
+    const char* sta = a_slot(kt);
+    const char* stb = b_slot(kt);
+    MOE_LOADF(1, sta, stb, 1);
+    if constexpr (kRing3) MOE_ISSUE_B(min(kt + 2, nks - 1));
+    else MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
     MOE_MMA(0);
     MOE_CHUNK_LOADS();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_LOADF(0, st, 2);
+    MOE_LOADF(0, sta, stb, 2);
     MOE_MMA(1);
-    MOE_LOADF(1, st, 3);
+    MOE_LOADF(1, sta, stb, 3);
     MOE_MMA(0);
     MOE_PIPE_DS();
     MOE_PIPE_DS();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_VMCNT(0);     // this wave's loads of stage kt+1 have landed
-    MOE_LGKMCNT0();   // and its reads of stage kt are done
+    MOE_VMCNT(kRing3 ? S::kLdB : 0);  // this wave's loads of stage kt+1 have landed
+    MOE_LGKMCNT0();                   // and its reads of stage kt are done
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_LOADF(0, lds + ((kt + 1) % kStages) * S::kStage, 0);
-    MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
+    MOE_LOADF(0, a_slot(kt + 1), b_slot(kt + 1), 0);
+    if constexpr (kRing3) MOE_ISSUE_A(min(kt + 2, nks - 1));
+    else MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
     MOE_MMA(1);
     MOE_CHUNK_LOADS();
   }
   {
-    const char* st = lds + ((nks - 1) % kStages) * S::kStage;
-    MOE_LOADF(1, st, 1);
+    const char* sta = a_slot(nks - 1);
+    const char* stb = b_slot(nks - 1);
+    MOE_LOADF(1, sta, stb, 1);
     MOE_MMA(0);
-    MOE_LOADF(0, st, 2);
+    MOE_LOADF(0, sta, stb, 2);
     MOE_MMA(1);
-    MOE_LOADF(1, st, 3);
+    MOE_LOADF(1, sta, stb, 3);
     MOE_MMA(0);
     MOE_MMA(1);
   }
   MOE_VMCNT(0);  // the last refill repeated a stage; let it land before the block ends
 #undef MOE_ISSUE
+#undef MOE_ISSUE_A
+#undef MOE_ISSUE_B
 #undef MOE_LOADF
 #undef MOE_MMA
 #undef MOE_PIPE_DS
