@@ -30,7 +30,7 @@
 //   place     without a capacity cut, scatter and row copy in one kernel:
 //             ranks as in scatter, then token-major copies (one read of x[t],
 //             one write per kept local pair, 16-byte vectors); when the chunk
-//             histogram table is small (chunks x experts <= 16384) every place
+//             histogram table is small (chunks x experts <= 65536) every place
 //             block also sums the columns it needs itself, so no scan launch
 //             sits between the router and the copy;
 //   gather    with a capacity cut, the same token-major copy after it.
