@@ -58,6 +58,11 @@ class HipEvents:
             out.append(e.value)
         return out
 
+    def record(self, e, stream) -> None:
+        """Record event e on the hipStream_t stream (an int handle, e.g. a torch stream's cuda_stream)."""
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
         st = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
@@ -263,7 +268,8 @@ def copy_probe(s, P: int) -> dict:
     torch.index_select gathering P rows of [T, H] (reads T*H, writes P*H: dispatch_place's
     mix) and torch.add of two [T, H] halves of a [P, H] buffer (reads P*H, writes T*H:
     combine's mix, for k = 2).  Eight buffer sets rotate so the 256 MB Infinity Cache holds
-    none of the next call's inputs.  Timed with HIP events per call (median of 20)."""
+    none of the next call's inputs.  Timed per call with the same timing-only HIP events as
+    the library's kernels (median of 20)."""
     import torch
     dt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     esz = 2 if s.dtype == "bf16" else 4
@@ -282,13 +288,16 @@ def copy_probe(s, P: int) -> dict:
             fn(i)
         torch.cuda.synchronize()
         ms = []
+        hip = HipEvents()
+        st = torch.cuda.current_stream().cuda_stream
         for r in range(20):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            ev = hip.create(2)
+            hip.record(ev[0], st)
             fn(r % nset)
-            b.record()
+            hip.record(ev[1], st)
             torch.cuda.synchronize()
-            ms.append(a.elapsed_time(b))
+            ms.append(hip.elapsed_ms(ev[0], ev[1]))
+            hip.destroy(ev)
         ms.sort()
         med = ms[len(ms) // 2]
         by = (rd + wr) * s.H * esz
@@ -304,7 +313,8 @@ def gemm_probe(s, P: int) -> dict:
     [H, I]), first through this library (offsets [0, P]; its gate/up also applies SwiGLU and
     writes [P, I]), then torch.matmul (hipBLASLt) on the same shapes ([P, H] x [H, 2I] and
     [P, I] x [I, H], bf16 out, float32 accumulation).  A dense product has no segment tails
-    and reads one weight matrix instead of L.  Timed with HIP events per call (median of 10)."""
+    and reads one weight matrix instead of L.  Timed per call with the same timing-only HIP events
+    as the library's kernels (median of 10)."""
     import torch
     import synth
     import expert_token_dispatch_amd as etd
@@ -349,13 +359,15 @@ def gemm_probe(s, P: int) -> dict:
             torch.matmul(a, w.t(), out=c)
         torch.cuda.synchronize()
         ms = []
+        st = torch.cuda.current_stream().cuda_stream
         for _ in range(10):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            ev = hip.create(2)
+            hip.record(ev[0], st)
             torch.matmul(a, w.t(), out=c)
-            e1.record()
+            hip.record(ev[1], st)
             torch.cuda.synchronize()
-            ms.append(e0.elapsed_time(e1))
+            ms.append(hip.elapsed_ms(ev[0], ev[1]))
+            hip.destroy(ev)
         ms.sort()
         med = ms[len(ms) // 2]
         tf = 2.0 * M * N * K / (med * 1e-3) / 1e12
@@ -550,13 +562,16 @@ def main():
 
     # per-step durations (median and minimum), from K more steps each between two events
     # of its own, after the timed region
-    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    cur = torch.cuda.current_stream().cuda_stream
+    pev = [hip.create(2) for _ in range(args.steps)]
     for a_, b_ in pev:
-        a_.record()
+        hip.record(a_, cur)
         step()
-        b_.record()
+        hip.record(b_, cur)
     torch.cuda.synchronize()
-    per_step = sorted(a_.elapsed_time(b_) for a_, b_ in pev)
+    per_step = sorted(hip.elapsed_ms(a_, b_) for a_, b_ in pev)
+    for e in pev:
+        hip.destroy(e)
     step_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
     step_min = per_step[0]
 
