@@ -35,21 +35,24 @@ namespace {
 // (256 registers, kept in AGPRs), so every fragment read from LDS feeds four
 // MFMAs.
 //
-// K advances 64 at a time through two 64 KB LDS stages filled by direct
-// global->LDS loads (global_load_lds_dwordx4: lane i of a load writes bytes
-// [16i, 16i+16) of a 1 KB block, no staging registers).  Rows are 128 bytes;
-// 16-byte chunk c of row r sits at physical chunk c ^ ((r/2) % 8), so the
-// fragment reads of 16 lanes (16 rows, one chunk) cover all 64 banks.
+// K advances 64 at a time through LDS filled by direct global->LDS loads
+// (buffer_load_dwordx4 ... lds: lane i of a load writes bytes [16i, 16i+16) of
+// a 1 KB block, no staging registers): the 256 activation rows of a step in
+// two 32 KB slots, the 256 weight rows in three, so the weight rows (which
+// miss L2 far more often) are asked for two steps ahead (a wide tile keeps two
+// whole stages).  Rows are 128 bytes; 16-byte chunk c of row r sits at physical
+// chunk c ^ ((r/2) % 8), so the fragment reads of 16 lanes (16 rows, one
+// chunk) cover all 64 banks.
 //
-// Schedule of one stage (per wave): for each 16-k chunk, the fragments of the
+// Schedule of one step (per wave): for each 16-k chunk, the fragments of the
 // next chunk are read while this chunk's 16 MFMAs issue, one read between
 // every two MFMAs (pinned with sched_group_barrier); reads bunched at the
-// start of the group left the LDS and the matrix core taking turns.  Before the last chunk the wave waits for its own
-// loads of the next stage and for its own reads of this stage, then a block
-// barrier makes both true for every wave: the next stage's first fragments
-// are read and this stage's slot is refilled (stage kt+2) while the last 16
-// MFMAs run.  The barrier is a bare s_barrier: __syncthreads() would also
-// drain every load in flight.
+// start of the group left the LDS and the matrix core taking turns.  Before
+// the last chunk the wave waits for its own loads of the next step and for its
+// own reads of this one, then a block barrier makes both true for every wave:
+// the next step's first fragments are read and the freed slots are refilled
+// while the last 16 MFMAs run.  The barrier is a bare s_barrier:
+// __syncthreads() would also drain every load in flight.
 //
 // The MFMAs take the weight fragment as the left operand, so each lane ends
 // with four adjacent output columns of one token row; the epilogue parks the
