@@ -619,6 +619,21 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
     }                                                                                                       \
   } while (0)
 
+#define MOE_ISSUE_A1(kt_, j_)                                                                               \
+  do {                                                                                                      \
+    char* sa_ = a_slot(kt_) + (S::kLdA * wave) * 1024;                                                      \
+    const uint32_t k0_ = uint32_t(kb + (kt_)) * (AKM ? uint32_t(BK * 2) * uint32_t(lda) : uint32_t(BK * 2)); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(sa_ + (j_) * 1024), 16, a_vo[j_], k0_, 0, 0);   \
+  } while (0)
+#define MOE_ISSUE_B1(kt_, j_)                                                                               \
+  do {                                                                                                      \
+    char* sb_ = b_slot(kt_) + S::kStageA + (S::kLdB * wave) * 1024;                                         \
+    const int s_ = kb + (kt_);                                                                              \
+    const bool sec_ = kcat > 0 && s_ >= kcat;                                                               \
+    const uint32_t kbo_ = uint32_t(sec_ ? s_ - kcat : s_) * (BKN ? uint32_t(BK * 2) * uint32_t(ldb) : uint32_t(BK * 2)); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sec_ ? b_rsrc2 : b_rsrc, (lds_ptr_t)(sb_ + (j_) * 1024), 16, b_vo[j_], \
+                                             kbo_, 0, 0);                                                   \
+  } while (0)
 // all A loads (MOE_ISSUE_A) or all B loads (MOE_ISSUE_B) of stage kt_
 #define MOE_ISSUE_A(kt_)                                                                                    \
   do {                                                                                                      \
@@ -695,6 +710,20 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                      \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][i], acc[i][j], 0, 0, 0); \
   } while (0)
+#define MOE_LOADF_Q(buf_, sta_, stb_, kc_, q_)                                                            \
+  do {                                                                                                    \
+    const int co_ = ((2 * (kc_) + g) ^ sw) * 16;                                                          \
+    fa[buf_][q_] = AKM ? read_kn_frag((sta_) + aoffs[q_] + (kc_) * 16 * 256)                                \
+                       : *reinterpret_cast<const bf16x8_t*>((sta_) + aoffs[q_] + co_);                      \
+    if ((q_) < NB)                                                                                        \
+      fb[buf_][(q_) % NB] = BKN ? read_kn_frag((stb_) + boffs[(q_) % NB] + (kc_) * 16 * 256)                \
+                                : *reinterpret_cast<const bf16x8_t*>((stb_) + boffs[(q_) % NB] + co_);      \
+  } while (0)
+#define MOE_MMA_Q(buf_, q_)                                                                               \
+  do {                                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                                                        \
+      acc[q_][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf_][j], fa[buf_][q_], acc[q_][j], 0, 0, 0); \
+  } while (0)
   // LDS reads per chunk (a k-major B fragment takes two transposing reads) and MFMAs per chunk
   constexpr int kDs = 4 * (AKM ? 2 : 1) + NB * (BKN ? 2 : 1), kMf = 4 * NB;
   // {MFMA, LDS read, MFMA} (or {MFMA, LDS read} when the reads outnumber half the
@@ -746,17 +775,68 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
   // Load order (the vector-memory counter retires loads in issue order).  Wide tile:
   // stage 0, the first half of stage 1; each iteration kt then issues the second half of
   // stage kt+1 at its top and the first half of stage kt+2 after its barrier, and the
-  // barrier waits for everything (stage kt+1).  Regular tile: A0 B0 B1 A1; iteration kt
-  // issues B(kt+2) at its top and A(kt+2) after its barrier, so at the barrier only
-  // B(kt+2) may still be in flight (A(kt+1) went out before it, B(kt+1) an iteration
-  // earlier).  Near the end a stage past the last repeats the last one (same bytes
-  // into the same slot).
+  // barrier waits for everything (stage kt+1).  Regular tile: A0 B0 B1 and the first
+  // half of A1; iteration kt issues the second half of A(kt+1) in its chunk 0, B(kt+2)
+  // in chunks 1 and 2, and the first half of A(kt+2) in chunk 3 (after its barrier), so
+  // at the barrier only B(kt+2) may still be in flight.  One load per quarter chunk
+  // keeps the texture addresser's queue from filling (with a chunk's loads issued
+  // together it was full several times as often as the vendor library's; spreading
+  // them: mixtral_like down −2 to −3%, gate/up −0.3%).  Near the end a stage past the
+  // last repeats the last one (same bytes into the same slot).
   if constexpr (kRing3) {
+    // within a chunk, per quarter: one row of MFMAs, the next chunk's fragments of that
+    // quarter, at most one load; the fences pin the order
+    constexpr int hA = S::kLdA / 2, hB = S::kLdB / 2;
+    static_assert(hA <= 4 && hB <= 4 && 4 % hA == 0 && 4 % hB == 0, "loads per quarter");
     MOE_ISSUE_A(0);
     MOE_ISSUE_B(0);
     MOE_ISSUE_B(min(1, nks - 1));
-    MOE_ISSUE_A(min(1, nks - 1));
-    MOE_VMCNT(S::kLdA + S::kLdB);  // stage 0 landed
+    _Pragma("unroll") for (int j = 0; j < hA; ++j) MOE_ISSUE_A1(min(1, nks - 1), j);
+    MOE_VMCNT(S::kLdB + hA);  // stage 0 landed
+    block_barrier();
+    MOE_LOADF(0, a_slot(0), b_slot(0), 0);
+    for (int kt = 0; kt + 1 < nks; ++kt) {
+      const char* sta = a_slot(kt);
+      const char* stb = b_slot(kt);
+      const int sa1 = min(kt + 1, nks - 1), s2 = min(kt + 2, nks - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // chunk 0 (fragments of chunk 1 into buffer 1)
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {
+        MOE_MMA_Q(0, q);
+        MOE_LOADF_Q(1, sta, stb, 1, q);
+        if (q % (4 / hA) == 4 / hA - 1) MOE_ISSUE_A1(sa1, hA + q / (4 / hA));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // chunk 1
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {
+        MOE_MMA_Q(1, q);
+        MOE_LOADF_Q(0, sta, stb, 2, q);
+        if (q % (4 / hB) == 4 / hB - 1) MOE_ISSUE_B1(s2, q / (4 / hB));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // chunk 2
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {
+        MOE_MMA_Q(0, q);
+        MOE_LOADF_Q(1, sta, stb, 3, q);
+        if (q % (4 / hB) == 4 / hB - 1) MOE_ISSUE_B1(s2, hB + q / (4 / hB));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      MOE_VMCNT(S::kLdB);  // all but B(kt+2)
+      MOE_LGKMCNT0();
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // chunk 3 (fragments of the next stage's chunk 0 into buffer 0)
+      {
+        const char* nta = a_slot(kt + 1);
+        const char* ntb = b_slot(kt + 1);
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {
+          MOE_MMA_Q(1, q);
+          MOE_LOADF_Q(0, nta, ntb, 0, q);
+          if (q % (4 / hA) == 4 / hA - 1) MOE_ISSUE_A1(s2, q / (4 / hA));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
   } else {
     MOE_ISSUE(0, 0, S::kLd);
     if (nks > 1) {
@@ -765,34 +845,32 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
     } else {
       MOE_VMCNT(0);
     }
-  }
-  block_barrier();
-  MOE_LOADF(0, a_slot(0), b_slot(0), 0);
-  for (int kt = 0; kt + 1 < nks; ++kt) {
-    const char* sta = a_slot(kt);
-    const char* stb = b_slot(kt);
-    MOE_LOADF(1, sta, stb, 1);
-    if constexpr (kRing3) MOE_ISSUE_B(min(kt + 2, nks - 1));
-    else MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
-    MOE_MMA(0);
-    MOE_CHUNK_LOADS();
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_LOADF(0, sta, stb, 2);
-    MOE_MMA(1);
-    MOE_LOADF(1, sta, stb, 3);
-    MOE_MMA(0);
-    MOE_PIPE_DS();
-    MOE_PIPE_DS();
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_VMCNT(kRing3 ? S::kLdB : 0);  // this wave's loads of stage kt+1 have landed
-    MOE_LGKMCNT0();                   // and its reads of stage kt are done
     block_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_LOADF(0, a_slot(kt + 1), b_slot(kt + 1), 0);
-    if constexpr (kRing3) MOE_ISSUE_A(min(kt + 2, nks - 1));
-    else MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
-    MOE_MMA(1);
-    MOE_CHUNK_LOADS();
+    MOE_LOADF(0, a_slot(0), b_slot(0), 0);
+    for (int kt = 0; kt + 1 < nks; ++kt) {
+      const char* sta = a_slot(kt);
+      const char* stb = b_slot(kt);
+      MOE_LOADF(1, sta, stb, 1);
+      MOE_ISSUE(min(kt + 1, nks - 1), kHalf, S::kLd);
+      MOE_MMA(0);
+      MOE_CHUNK_LOADS();
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_LOADF(0, sta, stb, 2);
+      MOE_MMA(1);
+      MOE_LOADF(1, sta, stb, 3);
+      MOE_MMA(0);
+      MOE_PIPE_DS();
+      MOE_PIPE_DS();
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_VMCNT(0);
+      MOE_LGKMCNT0();
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      MOE_LOADF(0, a_slot(kt + 1), b_slot(kt + 1), 0);
+      MOE_ISSUE(min(kt + 2, nks - 1), 0, kHalf);
+      MOE_MMA(1);
+      MOE_CHUNK_LOADS();
+    }
   }
   {
     const char* sta = a_slot(nks - 1);
@@ -808,6 +886,10 @@ __device__ __forceinline__ void tile_body(const Operands& op, bf16_t* __restrict
   MOE_VMCNT(0);  // the last refill repeated a stage; let it land before the block ends
 #undef MOE_ISSUE
 #undef MOE_ISSUE_A
+#undef MOE_ISSUE_A1
+#undef MOE_ISSUE_B1
+#undef MOE_LOADF_Q
+#undef MOE_MMA_Q
 #undef MOE_ISSUE_B
 #undef MOE_LOADF
 #undef MOE_MMA
