@@ -24,9 +24,9 @@
 //             earlier rounds -- no atomics, so the order is deterministic;
 //   capacity  (only with a limit) one block per local expert: the expert's
 //             keys sit in registers (element j*1024 + thread); radix select of
-//             the C-th largest key (logit desc, then token asc), then a stable
-//             compaction from per-wave ballots and two scans over the 512
-//             (register, wave) slots;
+//             the C-th largest key (logit desc, then token asc) in two 16-bit
+//             passes over packed 16-bit counters, then a stable compaction from
+//             per-wave ballots and one scan over the 512 (register, wave) slots;
 //   place     without a capacity cut, scatter and row copy in one kernel:
 //             ranks as in scatter, then token-major copies (one read of x[t],
 //             one write per kept local pair, 16-byte vectors); when the chunk
@@ -94,25 +94,50 @@ __device__ __forceinline__ int column_sum(const int32_t* __restrict__ col, size_
   return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
-// Exclusive scan over the block; *total receives the block sum.  `wsum` holds
-// one int per wave.  Every thread of the block must call it.
-__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+// Inclusive prefix sum over the wave (modulo 2^32) by DPP lane moves, no LDS
+// round trips: Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8; a
+// lane shifted in from outside its row reads 0), then the last lane of row 0 is
+// added to row 1 and that of row 2 to row 3 (row_bcast:15), then the last lane of
+// row 1 to rows 2 and 3 (row_bcast:31).  The cross-lane operations are those of
+// AMD's GCN3/Vega ISA documents (DPP_CTRL row_shr, row_bcast15, row_bcast31).
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  int x = int(v);
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true)));  // row_shr:1
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true)));  // row_shr:2
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true)));  // row_shr:4
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true)));  // row_shr:8
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false)));  // row_bcast:15
+  x = int(uint32_t(x) + uint32_t(__builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false)));  // row_bcast:31
+  return uint32_t(x);
+}
+
+// Exclusive scan over the block (modulo 2^32); *total receives the block sum.
+// `wsum` holds one word per wave.  Every thread of the block must call it.
+__device__ uint32_t block_exclusive_scan_u32(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const int incl = wave_inclusive_scan(v);
+  const uint32_t incl = wave_scan_u32(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int s = lane < nw ? wsum[lane] : 0;
-    s = wave_inclusive_scan(s);
+    uint32_t s = lane < nw ? wsum[lane] : 0u;
+    s = wave_scan_u32(s);
     if (lane < nw) wsum[lane] = s;
   }
   __syncthreads();
-  const int before = wave > 0 ? wsum[wave - 1] : 0;
+  const uint32_t before = wave > 0 ? wsum[wave - 1] : 0u;
   *total = wsum[nw - 1];
   __syncthreads();
   return before + incl - v;
+}
+
+// The same for non-negative int sums that fit an int.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  uint32_t t;
+  const uint32_t ex = block_exclusive_scan_u32(uint32_t(v), reinterpret_cast<uint32_t*>(wsum), &t);
+  *total = int(t);
+  return int(ex);
 }
 
 // ---- count ------------------------------------------------------------------
@@ -351,30 +376,42 @@ constexpr int kCapPerThread = 32;  // register-resident keys per thread (segment
 constexpr int kCapWaves = kCapThreads / 64;
 constexpr int kCapSlots = kCapPerThread * kCapWaves;  // (register, wave) slots in segment order
 constexpr int kCapBins = 4096;                        // 12-bit radix digits
+constexpr int kCapCopies = 8;                         // counter copies per digit (lane mod 8)
+constexpr int kCapWords = kCapBins * kCapCopies;      // 128 KB of LDS
+constexpr size_t kCapLds = size_t(kCapWords + kCapSlots + kCapWaves + 2) * 4;
+static_assert(kCapWords >= kCapPerThread * kCapThreads, "the counters' space holds every row's final row");
 
-// The digit of a radix-select pass: hist[0..nbins) counts the candidate keys by
-// digit; the wanted key is the want-th largest of them.  Thread t owns bins
-// nbins-1-4t .. nbins-4-4t (largest digits first); a block scan of the owners'
-// sums finds the owner whose bins reach `want`.  Leaves the digit in *s_digit and,
-// in *s_want, how many of the wanted keys still have to come from it.  Every
-// thread of the block must call it.
-__device__ void pick_digit(const int* hist, int nbins, int want, int* wsum, uint32_t* s_digit, int* s_want) {
+// The digit of a radix-select pass: hist[8 d + c] counts, in copy c, the candidate
+// keys of digit d (lane l adds to copy l mod 8, so the lanes of a wave that share a
+// digit spread over eight words); the wanted key is the want-th largest candidate.
+// `pad` keys counted in digit 0 are not candidates (padding) and are taken off.
+// Thread t owns digits nbins-1-4t .. nbins-4-4t (largest first); a block scan of the
+// owners' sums finds the owner whose digits reach `want`.  Leaves the digit in
+// *s_digit and, in *s_want, how many of the wanted keys still have to come from it.
+// Every thread of the block must call it.
+__device__ void pick_digit(const uint32_t* hist, int nbins, int want, uint32_t pad, uint32_t* wsum,
+                           uint32_t* s_digit, int* s_want) {
   const int t = threadIdx.x;
-  int c[4], tot = 0;
+  uint32_t c[4], tot = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int bin = nbins - 1 - 4 * t - q;
-    c[q] = bin >= 0 ? hist[bin] : 0;
+    const int d = nbins - 1 - 4 * t - q;
+    c[q] = 0;
+    if (d >= 0) {
+      const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hist + d * kCapCopies);
+      const u32x4_t x = h4[0], y = h4[1];
+      c[q] = (x[0] + x[1]) + (x[2] + x[3]) + (y[0] + y[1]) + (y[2] + y[3]) - (d == 0 ? pad : 0u);
+    }
     tot += c[q];
   }
-  int all;
-  int before = block_exclusive_scan(tot, wsum, &all);  // keys in larger digits than this thread's bins
-  if (before < want && before + tot >= want) {
+  uint32_t all;
+  uint32_t before = block_exclusive_scan_u32(tot, wsum, &all);  // keys in larger digits
+  if (before < uint32_t(want) && before + tot >= uint32_t(want)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (before + c[q] >= want) {
+      if (before + c[q] >= uint32_t(want)) {
         *s_digit = uint32_t(nbins - 1 - 4 * t - q);
-        *s_want = want - before;
+        *s_want = int(uint32_t(want) - before);
         break;
       }
       before += c[q];
@@ -389,17 +426,27 @@ __device__ void pick_digit(const int* hist, int nbins, int want, int* wsum, uint
 // Writes sorted_pairs for the kept pairs (in segment order from offsets[i]) and,
 // for every pre-capacity row, its final row or -1 in tmp_final: every access is in
 // segment order, and the gather resolves pair_row through tmp_final.
+// After the radix select of the cap-th largest key, one scan over the 512
+// (register, wave) slots of packed counts -- keys above the threshold in the low
+// half, keys equal to it in the high half -- gives every kept key its row: (keys
+// above before it) + min(equal keys before it, equal keys kept).  An expert's whole
+// segment is one block on one CU, so the kernel is bound by vector issue there (a
+// wave64 instruction takes four cycles of a 16-lane SIMD; 16 waves, ~20 instructions
+// per key and phase) and by LDS atomics on the few digits that similar logits share.
 __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ tmp_sorted,
                                                                const uint32_t* __restrict__ tmp_key,
                                                                const int32_t* __restrict__ pre_off,
                                                                const int32_t* __restrict__ offsets, int cap,
                                                                int32_t* __restrict__ sorted_pairs,
                                                                int32_t* __restrict__ tmp_final) {
-  __shared__ int hist[kCapBins];
-  __shared__ int wsum[kCapThreads / 64];
-  __shared__ int slot_cnt[kCapSlots];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_want;
+  // all of the block's LDS is dynamic (no static arrays), so the counters start at
+  // offset 0 and their 16-byte reads and writes are aligned
+  extern __shared__ int32_t sh[];
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sh);  // [kCapWords]
+  uint32_t* slot_cnt = hist + kCapWords;             // [kCapSlots]
+  uint32_t* wsum = slot_cnt + kCapSlots;             // [kCapWaves]
+  uint32_t& s_digit = wsum[kCapWaves];
+  int& s_want = reinterpret_cast<int*>(wsum)[kCapWaves + 1];
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
   const int a = pre_off[i];
@@ -407,10 +454,19 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
   const int out0 = offsets[i];
   const int32_t* seg = tmp_sorted + a;
 
-  if (n <= cap) {
-    for (int r = tid; r < n; r += kCapThreads) {
-      sorted_pairs[out0 + r] = seg[r];
-      tmp_final[a + r] = out0 + r;
+  if (n <= cap) {  // rows in batches of four per thread, the loads issued together
+    for (int r0 = tid; r0 < n; r0 += 4 * kCapThreads) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = r0 + u * kCapThreads < n ? seg[r0 + u * kCapThreads] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u * kCapThreads;
+        if (r < n) {
+          sorted_pairs[out0 + r] = v[u];
+          tmp_final[a + r] = out0 + r;
+        }
+      }
     }
     return;
   }
@@ -422,33 +478,43 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
 
   // element r = j*1024 + tid of the segment sits in this thread's register j
   // (coalesced loads; segment order is j-major, then wave, then lane)
+  // Rows past the segment hold key 0 as padding.  The histograms skip registers
+  // with no row of the segment (j*1024 >= n, a wave-uniform test); the rest's npad
+  // padding keys are candidates while the digits chosen so far are all 0, always in
+  // digit 0, which the digit pick takes off.  A padding key is never above a
+  // threshold and comes after every real row in segment order, so it never takes a
+  // kept row.
   const int lane = tid & 63, wave = tid >> 6;
-  bool in[kCapPerThread];
+  const int nreg = (n + kCapThreads - 1) / kCapThreads;
+  const uint32_t npad = uint32_t(nreg * kCapThreads - n);
+  const uint32_t* kseg = tmp_key + a;
   uint32_t key[kCapPerThread];
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    const int r = j * kCapThreads + tid;
-    in[j] = r < n;
-    key[j] = in[j] ? tmp_key[a + r] : 0u;
+    const uint32_t r = uint32_t(j * kCapThreads + tid);
+    key[j] = r < uint32_t(n) ? kseg[r] : 0u;
   }
+  u32x4_t* hist4 = reinterpret_cast<u32x4_t*>(hist);
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  const int copy = lane & (kCapCopies - 1);
 
   // radix select of the cap-th largest key, 12-bit digits (bits 31..20, 19..8) then
   // 8 bits: float logits share a few exponents, and 12-bit leading digits spread
-  // them over tens of bins where 8-bit ones leave a handful (and every lane of a
-  // wave adding to the same bin)
+  // them over tens of bins where 8-bit ones leave a handful
   uint32_t prefix = 0, mask = 0;
   int want = cap;
   const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
 #pragma unroll
   for (int ps = 0; ps < 3; ++ps) {
     const int shift = shifts[ps], nbins = 1 << widths[ps];
-    for (int b = tid; b < nbins; b += kCapThreads) hist[b] = 0;
+    for (int q = tid; q < nbins * kCapCopies / 4; q += kCapThreads) hist4[q] = zero4;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kCapPerThread; ++j)
-      if (in[j] && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & uint32_t(nbins - 1)], 1);
+      if (j < nreg && (key[j] & mask) == prefix)
+        atomicAdd(&hist[((key[j] >> shift) & uint32_t(nbins - 1)) * kCapCopies + copy], 1u);
     __syncthreads();
-    pick_digit(hist, nbins, want, wsum, &s_digit, &s_want);
+    pick_digit(hist, nbins, want, prefix == 0 ? npad : 0u, wsum, &s_digit, &s_want);
     __syncthreads();
     prefix |= s_digit << shift;
     mask |= uint32_t(nbins - 1) << shift;
@@ -456,53 +522,55 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
     __syncthreads();
   }
   const uint32_t thr = prefix;
-  const int need_eq = want;  // keys equal to thr kept: the first need_eq in segment (= token) order
+  const uint32_t need_eq = uint32_t(want);  // keys equal to thr kept: the first need_eq in segment order
 
-  // rank of each key equal to thr among the equal keys before it, in segment order:
-  // per (j, wave) counts from ballots, one exclusive scan over the 512 (j, wave) slots
-  uint64_t eqm[kCapPerThread];
-#pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j) {
-    eqm[j] = __ballot(in[j] && key[j] == thr);
-    if (lane == 0) slot_cnt[j * kCapWaves + wave] = int(__popcll(eqm[j]));
-  }
-  __syncthreads();
-  int tot;
-  {
-    const int v = tid < kCapSlots ? slot_cnt[tid] : 0;
-    const int ex = block_exclusive_scan(v, wsum, &tot);
-    if (tid < kCapSlots) slot_cnt[tid] = ex;
-  }
-  __syncthreads();
-  uint64_t keepm[kCapPerThread];
+  // per (register, wave) slot: keys above thr (low half) and equal to it (high half);
+  // per key, the same counts over the lanes below it in its slot
   const uint64_t below = lanemask_lt();
+  uint32_t lcnt[kCapPerThread];
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    const bool eq = in[j] && key[j] == thr;
-    const int eq_before = slot_cnt[j * kCapWaves + wave] + int(__popcll(eqm[j] & below));
-    keepm[j] = __ballot(in[j] && (key[j] > thr || (eq && eq_before < need_eq)));
+    const uint64_t gm = __ballot(key[j] > thr), em = __ballot(key[j] == thr);
+    lcnt[j] = uint32_t(__popcll(gm & below)) | (uint32_t(__popcll(em & below)) << 16);
+    if (lane == 0) slot_cnt[j * kCapWaves + wave] = uint32_t(__popcll(gm)) | (uint32_t(__popcll(em)) << 16);
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j)
-    if (lane == 0) slot_cnt[j * kCapWaves + wave] = int(__popcll(keepm[j]));
-  __syncthreads();
   {
-    const int v = tid < kCapSlots ? slot_cnt[tid] : 0;
-    const int ex = block_exclusive_scan(v, wsum, &tot);
+    const uint32_t v = tid < kCapSlots ? slot_cnt[tid] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan_u32(v, wsum, &tot);
     if (tid < kCapSlots) slot_cnt[tid] = ex;
   }
   __syncthreads();
+  // every row's final row (or -1) into LDS, where the counters were (so that no row
+  // address stays live in registers across the kernel)
+  int32_t* fin = reinterpret_cast<int32_t*>(hist);
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    if (!in[j]) continue;
-    const int r = j * kCapThreads + tid;
-    if ((keepm[j] >> lane) & 1u) {
-      const int pos = out0 + slot_cnt[j * kCapWaves + wave] + int(__popcll(keepm[j] & below));
-      sorted_pairs[pos] = seg[r];
-      tmp_final[a + r] = pos;
-    } else {
-      tmp_final[a + r] = -1;
+    const bool gt = key[j] > thr, eq = key[j] == thr;
+    const uint32_t c = slot_cnt[j * kCapWaves + wave] + lcnt[j];  // no carry: halves stay below 2^16
+    const uint32_t gb = c & 0xffffu, eb = c >> 16;
+    fin[j * kCapThreads + tid] = (gt || (eq && eb < need_eq)) ? out0 + int(gb + min(eb, need_eq)) : -1;
+  }
+  __syncthreads();
+  // every pair-id load in flight at once, then the stores (a kept row always lands in
+  // [out0, out_end); the test only keeps this kernel and the gather in bounds)
+  const int out_end = offsets[i + 1];
+  int32_t* tfin = tmp_final + a;
+  int32_t f[kCapPerThread], v[kCapPerThread];
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    const uint32_t r = uint32_t(j * kCapThreads + tid);
+    f[j] = r < uint32_t(n) ? fin[r] : -1;
+    v[j] = f[j] >= 0 ? seg[r] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j) {
+    const uint32_t r = uint32_t(j * kCapThreads + tid);
+    if (r < uint32_t(n)) {
+      const bool kept = f[j] >= out0 && f[j] < out_end;
+      if (kept) sorted_pairs[f[j]] = v[j];
+      tfin[r] = kept ? f[j] : -1;
     }
   }
 }
@@ -756,7 +824,13 @@ moe_status launch_dispatch(const DispatchArgs& a) {
     const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
     MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
                begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
-    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), 0, a.s, a.scr.tmp_sorted,
+    const size_t cap_lds = kCapLds;
+    {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(capacity_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(cap_lds));
+      if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_capacity: LDS attribute: %s", hipGetErrorString(e));
+    }
+    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), cap_lds, a.s, a.scr.tmp_sorted,
                a.scr.tmp_key, a.scr.pre_off, a.offsets, int(a.capacity), a.sorted_pairs, a.scr.tmp_final);
     const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
     MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const u32x4_t*>(a.x), a.pair_row,
