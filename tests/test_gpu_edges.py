@@ -113,6 +113,43 @@ def test_capacity_drops_everything_for_some_tokens():
     assert np.all(gpu["y"][C:] == 0)
 
 
+@pytest.mark.parametrize("case", ["max_segment", "ragged_clustered"])
+def test_capacity_cut_large_segments(case):
+    # The capacity cut keeps a segment's keys 32 per thread of a 1024-thread block: a
+    # segment of the most tokens a call takes (32768, every register full, no padding),
+    # and segments of several thousand keys that are not multiples of 1024 (padding
+    # rows) whose logits share a handful of values (many keys per radix digit, ties
+    # ranked by token).
+    if case == "max_segment":
+        s = synth.spec("skewed_capacity", T=32768, H=64, I=64, E=8, k=1, L=8, capacity_factor=0.5)
+        rng = np.random.default_rng(11)
+        lg = np.zeros((s.T, s.E), dtype=np.float32)
+        lg[:, 0] = rng.choice(np.array([1.0, 1.5, 2.0], dtype=np.float32), size=s.T)
+    else:
+        s = synth.spec("skewed_capacity", T=9001, H=64, I=64, E=4, k=2, L=4, capacity_factor=0.9)
+        rng = np.random.default_rng(12)
+        lg = (3.0 + 1e-3 * np.round(rng.standard_normal((s.T, s.E)) * 3)).astype(np.float32)
+        lg[:, 1] += 0.5   # expert 1 in nearly every token's top 2
+    say(f"[edge] capacity cut {case}: {s}")
+    inp, layer, x, gpu = _run(s, logits=lg)
+    ref = _check(s, inp, gpu, logits=lg)
+    C = oracle.capacity_limit(s.capacity_factor, s.T, s.k, s.E)
+    assert int(np.max(ref["counts"])) > C and ref["num_dropped"] > 0
+
+
+def test_zero_capacity_drops_every_pair():
+    # a capacity factor so small that C = floor(cf * T * k / E) = 0: every pair is cut
+    # and every output row is zero
+    s = synth.spec("skewed_capacity", T=1000, H=64, I=64, E=8, k=2, L=8, capacity_factor=0.001)
+    assert oracle.capacity_limit(s.capacity_factor, s.T, s.k, s.E) == 0
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    y = np_of(layer.forward(x))
+    ref = oracle.layer_forward(inp)
+    assert ref["num_dropped"] == s.T * s.k
+    assert np.all(y == 0) and np.all(ref["y"] == 0)
+
+
 def test_expert_ranges_sum_to_all_local():
     base = synth.spec("gptoss_ep8_share", T=512, H=128, I=96, E=16, k=4, L=16, dtype="f32", bias="none")
     inp = synth.make_layer(base)
