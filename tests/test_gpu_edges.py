@@ -150,6 +150,37 @@ def test_zero_capacity_drops_every_pair():
     assert np.all(y == 0) and np.all(ref["y"] == 0)
 
 
+@pytest.mark.parametrize("E,L,begin,cf", [(2048, 2048, 0, 0.0), (4096, 1500, 100, 0.0), (4096, 3000, 1000, 2.0)],
+                         ids=lambda v: str(v))
+def test_dispatch_with_thousands_of_experts(E, L, begin, cf):
+    # Dispatch on given top-k ids with more experts than the router takes (up to the 4096
+    # the descriptor allows, up to 3000 local): the chunk histogram table is past the
+    # size the place kernel sums itself, so the scan runs as its own launch over column
+    # groups of 1024 experts; with a capacity factor, the cut runs one block per local
+    # expert over segments of a few pairs.
+    s = synth.spec("gptoss_ep8_share", T=3000, H=64, I=32, E=E, k=4, local_begin=begin, L=L, capacity_factor=cf)
+    inp = synth.make_layer(s)
+    layer, x = layer_of(inp)
+    rng = np.random.default_rng(E + L)
+    ids = np.argsort(rng.random((s.T, E)), axis=1)[:, : s.k].astype(np.int32)   # k distinct experts per token
+    crowd = (np.arange(s.T) < s.T // 3) & ~(ids[:, 1:] == begin + 7).any(axis=1)
+    ids[crowd, 0] = begin + 7                                                     # one crowded local expert
+    lgt = np.round(rng.standard_normal((s.T, s.k)) * 4).astype(np.float32) / 4   # many equal scores
+    say(f"[edge] dispatch E={E} L={L} begin={begin} cf={cf}")
+    g = layer.dispatch(x, torch.from_numpy(ids).cuda(), torch.from_numpy(lgt).cuda() if cf > 0 else None)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(ids.astype(np.int64), lgt.astype(np.float64), E, begin, L, cf)
+    np.testing.assert_array_equal(np_of(g["counts"]), d["counts"])
+    np.testing.assert_array_equal(np_of(g["offsets"]), d["offsets"])
+    P = int(d["offsets"][-1])
+    np.testing.assert_array_equal(np_of(g["sorted_pairs"])[:P], d["sorted_pairs"])
+    np.testing.assert_array_equal(np_of(g["pair_row"]), d["pair_row"])
+    assert int(np_of(g["num_dropped"])[0]) == d["num_dropped"]
+    np.testing.assert_array_equal(np_of(g["x_sorted"])[:P], np_of(x)[d["sorted_pairs"] // s.k])
+    if cf > 0:
+        assert d["num_dropped"] > 0
+
+
 def test_expert_ranges_sum_to_all_local():
     base = synth.spec("gptoss_ep8_share", T=512, H=128, I=96, E=16, k=4, L=16, dtype="f32", bias="none")
     inp = synth.make_layer(base)
