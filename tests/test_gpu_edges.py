@@ -181,6 +181,18 @@ def test_dispatch_with_thousands_of_experts(E, L, begin, cf):
         assert d["num_dropped"] > 0
 
 
+@pytest.mark.parametrize("H,I", [(128, 512), (512, 128)], ids=["gate_up_128", "down_128"])
+def test_float32_layer_on_128_tiles(H, I):
+    # A float32 layer whose 64 x 64 tiles would fill the CUs unevenly takes 128 x 128
+    # tiles (six-slot ring) for the product with 512 output columns: gate/up for
+    # H=128, I=512; down for H=512, I=128 (the tile picker's cost: rounds of 256 CUs x
+    # tile area, 64 x 64 only when 10% cheaper).
+    s = synth.spec("tiny_fp32", T=3000, H=H, I=I, E=8, k=2, L=8)
+    say(f"[edge] float32 128x128 tiles: {s}")
+    inp, layer, x, gpu = _run(s)
+    _check(s, inp, gpu)
+
+
 def test_expert_ranges_sum_to_all_local():
     base = synth.spec("gptoss_ep8_share", T=512, H=128, I=96, E=16, k=4, L=16, dtype="f32", bias="none")
     inp = synth.make_layer(base)
