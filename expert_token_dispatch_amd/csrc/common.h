@@ -17,8 +17,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // (HIP's uint4 is a struct, which a conditional expression can push to scratch)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWave = 64;
-
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
 // float32 -> bfloat16, round to nearest, ties to even, by the hardware
@@ -94,17 +92,6 @@ __device__ __forceinline__ uint64_t match_any(uint32_t key, int bits, uint64_t a
     m &= ((key >> b) & 1u) ? set : ~set;
   }
   return m;
-}
-
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
 }
 
 }  // namespace moe
