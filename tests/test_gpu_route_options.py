@@ -60,6 +60,43 @@ def test_route_with_options_bit_exact(E, k, G, M, bs, tied):
     np.testing.assert_allclose(np_of(r["topk_w"]), ref["topk_w"], rtol=0, atol=2e-7)
 
 
+def test_route_options_random_draws():
+    # seeded random draws: E up to 256, k, a group count dividing E (up to 16), the most
+    # groups a token may use (enough to hold k), a selection bias of random scale (or none),
+    # and logits from the router or rounded so that many tie
+    rng = np.random.default_rng(31337)
+    for it in range(120):
+        E = int(rng.choice([2, 4, 6, 8, 12, 16, 32, 48, 64, 96, 128, 160, 192, 256]))
+        divs = [g for g in range(2, 17) if E % g == 0]
+        G = int(rng.choice(divs)) if divs and rng.random() < 0.7 else 0
+        k = int(rng.integers(1, min(E, 32) + 1))
+        M = 0
+        if G:
+            M = int(rng.integers(1, G + 1))
+            while M * (E // G) < k:
+                M += 1
+        bs = float(rng.choice([0.0, 0.25, 1.0, 4.0]))
+        tied = bool(rng.random() < 0.4)
+        T = int(rng.choice([1, 5, 64, 65, 257]))
+        s = synth.spec("mixtral_like", T=T, H=64, I=64, E=E, k=k, L=E, seed=70000 + it)
+        inp = synth.make_layer(s)
+        layer, x = layer_of(inp)
+        bias = (np.round(rng.standard_normal(E) * bs * 4) / 4).astype(np.float32) if bs else None
+        bt = None if bias is None else torch.from_numpy(bias).cuda()
+        o = etd.make_route_opts(bt, G, M)
+        if tied:
+            lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+            r = layer.route(x, logits_in=torch.from_numpy(lg).cuda(), want_topk_logit=True, opts=o)
+        else:
+            r = layer.route(x, want_logits=True, want_topk_logit=True, opts=o)
+            lg = np_of(r["logits"])
+        say(f"[options] draw {it}: T={T} E={E} k={k} groups {G}/{M} bias {bs} tied {tied}")
+        ref = oracle.route_with_options(lg.astype(np.float64), k, bias, G, M)
+        np.testing.assert_array_equal(np_of(r["topk_ids"]), ref["topk_ids"], err_msg=f"draw {it}")
+        np.testing.assert_array_equal(np_of(r["topk_logit"]), ref["topk_logit"].astype(np.float32))
+        np.testing.assert_allclose(np_of(r["topk_w"]), ref["topk_w"], rtol=0, atol=2e-7)
+
+
 def test_layer_forward_with_options():
     s = synth.spec("gptoss_ep8_share", T=700, H=128, I=160, E=32, k=4, L=16, local_begin=8)
     inp = synth.make_layer(s)
