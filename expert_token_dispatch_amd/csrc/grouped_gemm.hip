@@ -60,16 +60,21 @@ namespace {
 //
 // Tile order: the blocks that run at once on one XCD (blocks are dealt to
 // the 8 XCDs round robin) get consecutive tile numbers, and tile numbers run
-// over (expert, group of kGroupN n-tiles, m-tile, n-tile in group), so one
-// XCD's L2 serves a few weight tiles to all m-tiles of an expert and a few
-// activation tiles to several n-tiles.
+// over (expert, group of gn n-tiles, m-tile, n-tile in group), so one XCD's L2
+// serves a few weight tiles to all m-tiles of an expert and a few activation
+// tiles to several n-tiles.
 namespace big {
 
 constexpr int BM = 256, BNE = 256, BK = 64, kStages = 2;
 
 constexpr int kRowBytes = BK * 2;              // 128
-constexpr int kGroupN = 4;
 constexpr int kXcds = 8;
+
+// n-tiles per group of the tile order (gn): 2 for products of fewer than 8192 k, 4 for
+// longer ones (same-box interleaved runs: with 2 instead of 4, mixtral_like's gate/up
+// (K = 4096) -2.2% and the gpt-oss-like share's products (K = 2880) -1.4 to -2.4%, but
+// mixtral_like's down (K = 14336) +1.7 to +2.7%; groups of 1 or 8 were slower).
+__host__ __device__ constexpr int group_width(int K) { return K >= 8192 ? 4 : 2; }
 
 // s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at their maxima)
 #define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
@@ -80,7 +85,7 @@ bool supported(int K) { return K % BK == 0; }
 bool addressable(int64_t rows, int64_t K) { return rows * K * 2 < (int64_t(1) << 32); }
 
 // ---- work plan -------------------------------------------------------------
-// Tiles are numbered over (expert, group of kGroupN n-tiles, m-tile, n-tile
+// Tiles are numbered over (expert, group of gn n-tiles, m-tile, n-tile
 // in group) and dealt to the XCDs in contiguous ranges (block b runs on XCD
 // b % 8).  An XCD with q tiles runs them in rounds of `cpx` (its CU count);
 // when the last round is only partly filled, its r tiles may be cut into s
@@ -120,16 +125,16 @@ struct Job {
   int part, nparts, pslot;
 };
 
-// Tiles of one expert with n rows: in every group of up to kGroupN n-tiles,
-// the full 256-row m-tiles, then the tail m-tile: a regular tile per n-tile
-// when the tail has more than 128 rows, else one wide tile per two n-tiles.
+// Tiles of one expert with n rows: in every group of up to gn n-tiles, the
+// full 256-row m-tiles, then the tail m-tile: a regular tile per n-tile when
+// the tail has more than 128 rows, else one wide tile per two n-tiles.
 __device__ __forceinline__ int tail_tiles(int tail, int gsz) {
   return tail == 0 ? 0 : (tail <= BM / 2 ? (gsz + 1) / 2 : gsz);
 }
-__device__ __forceinline__ int expert_tiles(int n, int NT) {
+__device__ __forceinline__ int expert_tiles(int n, int NT, int gn) {
   const int mf = n / BM, tail = n - mf * BM;
-  const int nfull = NT / kGroupN, last = NT - nfull * kGroupN;
-  return nfull * (mf * kGroupN + tail_tiles(tail, kGroupN)) + (last ? mf * last + tail_tiles(tail, last) : 0);
+  const int nfull = NT / gn, last = NT - nfull * gn;
+  return nfull * (mf * gn + tail_tiles(tail, gn)) + (last ? mf * last + tail_tiles(tail, last) : 0);
 }
 
 // One XCD's share of the work: tiles [base, base + qx) in rounds of cpx; the r
@@ -153,15 +158,16 @@ __device__ __forceinline__ XcdPlan plan_xcd(int R, int nk, int cpx, int smax, in
 // Per-expert tile counts of both products, as exclusive prefix sums
 // (pre[0..L] for gate/up, pre[L+1..2L+1] for down), so that a GEMM block
 // finds the total and its tile's expert without walking all the offsets.
+// K_gu, K_dn: each product's K (its group width follows from it).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int L, int NT_gu, int NT_dn,
-                                                    int32_t* __restrict__ pre) {
+                                                    int K_gu, int K_dn, int32_t* __restrict__ pre) {
   __shared__ int wa[16], wb[16];  // per-wave totals
   int carry_gu = 0, carry_dn = 0;
   for (int i0 = 0; i0 < L; i0 += 1024) {
     const int i = i0 + threadIdx.x;
     const int n = i < L ? offsets[i + 1] - offsets[i] : 0;
-    const int a = i < L ? expert_tiles(n, NT_gu) : 0;
-    const int b = i < L ? expert_tiles(n, NT_dn) : 0;
+    const int a = i < L ? expert_tiles(n, NT_gu, group_width(K_gu)) : 0;
+    const int b = i < L ? expert_tiles(n, NT_dn, group_width(K_dn)) : 0;
     // two block scans (inclusive within waves, then over the wave totals)
     int va = a, vb = b;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -200,9 +206,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
-// expert, rows and columns of tile t; tpre = the product's tile prefix (L + 1 entries)
-__device__ __forceinline__ void tile_of(const int32_t* __restrict__ offsets, const int32_t* tpre, int L, int NT, int t,
-                                        Job& jb) {
+// expert, rows and columns of tile t; tpre = the product's tile prefix (L + 1 entries),
+// gn its group width
+__device__ __forceinline__ void tile_of(const int32_t* __restrict__ offsets, const int32_t* tpre, int L, int NT, int gn,
+                                        int t, Job& jb) {
   // the expert: the last i with tpre[i] <= t (experts with no tiles have tpre[i] == tpre[i+1])
   int lo = 0, hi = L - 1;
   while (lo < hi) {
@@ -214,15 +221,15 @@ __device__ __forceinline__ void tile_of(const int32_t* __restrict__ offsets, con
   const int seg0 = offsets[lo];
   const int seg_n = offsets[lo + 1] - seg0;
   const int mf = seg_n / BM, tl = seg_n - mf * BM;
-  const int nfull = NT / kGroupN;
-  const int per_group = mf * kGroupN + tail_tiles(tl, kGroupN);
+  const int nfull = NT / gn;
+  const int per_group = mf * gn + tail_tiles(tl, gn);
   int ng = t / per_group;
   if (ng > nfull) ng = nfull;  // past the full groups: the last, partial group
   const int rem = t - ng * per_group;
-  const int gsz = ng < nfull ? kGroupN : NT - nfull * kGroupN;
+  const int gsz = ng < nfull ? gn : NT - nfull * gn;
   if (rem < mf * gsz) {
     const int mt = rem / gsz;
-    jb.n0 = ng * kGroupN + (rem - mt * gsz);
+    jb.n0 = ng * gn + (rem - mt * gsz);
     jb.row0 = seg0 + mt * BM;
     jb.rows = BM;
     jb.wide = false;
@@ -231,7 +238,7 @@ __device__ __forceinline__ void tile_of(const int32_t* __restrict__ offsets, con
     jb.row0 = seg0 + mf * BM;
     jb.rows = tl;
     jb.wide = tl <= BM / 2;
-    jb.n0 = ng * kGroupN + (jb.wide ? 2 * r2 : r2);
+    jb.n0 = ng * gn + (jb.wide ? 2 * r2 : r2);
   }
 }
 
@@ -252,7 +259,7 @@ __device__ __forceinline__ void unit_job(const int32_t* __restrict__ offsets, co
     jb.nparts = xp.s;
     jb.pslot = xcd * kMaxParts + v;
   }
-  tile_of(offsets, tpre, L, NT, t, jb);
+  tile_of(offsets, tpre, L, NT, group_width(nk * BK), t, jb);
   jb.kb = (jb.part * nk) / jb.nparts;
   jb.nks = ((jb.part + 1) * nk) / jb.nparts - jb.kb;
 }
@@ -1043,7 +1050,7 @@ __global__ __launch_bounds__(NW * 64) void fixup_kernel(const int32_t* __restric
   const XcdPlan xp = plan_xcd(tpre[L], K / BK, cpx, smax, xcd);
   if (xp.s == 1 || w >= xp.r) return;
   Job jb;
-  tile_of(offsets, tpre, L, NT, xp.base + xp.F * cpx + w, jb);
+  tile_of(offsets, tpre, L, NT, group_width(K), xp.base + xp.F * cpx + w, jb);
   jb.nparts = xp.s;
   jb.pslot = xcd * kMaxParts + w * xp.s;
   const int n0 = jb.n0 * ON;
@@ -1238,7 +1245,7 @@ moe_status launch_big_backward_dgrad(const moe_layer_desc* d, const bf16_t* dy_s
                                                                align_up(size_t(2) * (L + 1) * sizeof(int32_t), 256))
                                     : nullptr;
   MOE_LAUNCH("ffn_bwd_plan", big::plan_kernel, dim3(1), dim3(1024), 0, s, offsets, L, (I + big::BNE - 1) / big::BNE,
-             (H + big::BNE - 1) / big::BNE, pre);
+             (H + big::BNE - 1) / big::BNE, H, 2 * I, pre);
   moe_status st = big::launch<1>("ffn_down_dgrad", dy_sorted, offsets, w_down, w_down, dgu, L, I, H, 0, kn, max_pairs,
                                  pre, nullptr, s, const_cast<bf16_t*>(gate), const_cast<bf16_t*>(up), big::kSwigluBwd);
   if (st != MOE_OK) return st;
@@ -1278,7 +1285,7 @@ moe_status launch_grouped_ffn(const FfnArgs& a) {
                                                 align_up(size_t(2) * (L + 1) * sizeof(int32_t), 256))
                      : nullptr;
   MOE_LAUNCH("ffn_plan", big::plan_kernel, dim3(1), dim3(1024), 0, a.s, a.offsets, L, (I + big::BNE / 2 - 1) / (big::BNE / 2),
-             (H + big::BNE - 1) / big::BNE, pre);
+             (H + big::BNE - 1) / big::BNE, H, I, pre);
   // the math-form layout stores the weights k-major
   const bool kn = d->weight_layout == MOE_WEIGHTS_IN_OUT;
   moe_status st = big::launch<2>("ffn_gate_up", x, a.offsets, static_cast<const bf16_t*>(a.w_gate),
