@@ -90,8 +90,10 @@ def kernel_work(name: str, s, P: int, touched_tokens: int, touched_experts: int,
         return T * k * 4 + nblk * E * 4, 0.0
     if name == "dispatch_scan":
         return nblk * E * 4 * 2, 0.0
-    if name == "dispatch_scatter":
-        return T * k * 4 * 2 + P * 4, 0.0
+    if name == "dispatch_scatter":  # ids, logits, chunk counts in; pair_row, pre-capacity permutation and keys out
+        return T * k * 4 * 5 + nblk * E * 4, 0.0
+    if name == "dispatch_cap_hist":  # the keys of the experts over capacity (at most all of them)
+        return T * k * 4, 0.0
     if name == "dispatch_capacity":
         return T * k * 4 * 3, 0.0
     if name == "dispatch_gather":

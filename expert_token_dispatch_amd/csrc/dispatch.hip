@@ -45,6 +45,14 @@
 
 namespace moe {
 
+// The capacity cut works on slices of kCapSlice consecutive pre-capacity rows of
+// one expert's segment; an upper bound on their number over all local experts.
+constexpr int kCapSlice = 4096;
+constexpr int kCapBins = 4096;  // 12-bit radix digits
+int64_t cap_slices_max(const moe_layer_desc* d) {
+  return (d->num_tokens * d->top_k + kCapSlice - 1) / kCapSlice + d->local_count;
+}
+
 size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   const int64_t n = d->num_tokens * d->top_k;
   const int64_t nblk = dispatch_blocks(d->num_tokens);
@@ -52,7 +60,11 @@ size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   b += align_up(size_t(nblk) * d->num_experts * 4, 256);
   b += align_up(size_t(nblk) * d->local_count * 4, 256);
   b += align_up(size_t(d->local_count + 1) * 4, 256);
-  if (d->capacity_factor > 0) b += 3 * align_up(size_t(n) * 4, 256);
+  if (d->capacity_factor > 0) {
+    b += 3 * align_up(size_t(n) * 4, 256);
+    b += align_up(size_t(d->local_count + 1) * 4, 256);
+    b += align_up(size_t(cap_slices_max(d)) * kCapBins * 4, 256);
+  }
   return b;
 }
 
@@ -73,6 +85,10 @@ DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
     s.tmp_key = reinterpret_cast<uint32_t*>(p);
     p += align_up(size_t(n) * 4, 256);
     s.tmp_final = reinterpret_cast<int32_t*>(p);
+    p += align_up(size_t(n) * 4, 256);
+    s.slice_off = reinterpret_cast<int32_t*>(p);
+    p += align_up(size_t(d->local_count + 1) * 4, 256);
+    s.slice_hist = reinterpret_cast<uint32_t*>(p);
   }
   return s;
 }
@@ -82,7 +98,9 @@ namespace {
 __device__ __forceinline__ int bits_for(int maxval) { return 32 - __clz(maxval); }
 
 // Sum of col[b * stride] for b = b_lo, b_lo + step, ... < b_hi, eight loads in flight
-// (integer sums: the grouping does not change the result).
+// (integer sums: the grouping does not change the result).  Sixteen in flight was
+// slower (the capacity path's fused scatter: 15.9 -> 25.5 us; every block reads the
+// same rows, so more requests only queue at the same L2 channels).
 __device__ __forceinline__ int column_sum(const int32_t* __restrict__ col, size_t stride, int b_lo, int b_hi, int step) {
   int s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int b = b_lo;
@@ -169,6 +187,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
                                                             int begin, int L, int64_t cap, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ pre_off,
                                                             int32_t* __restrict__ blk_base,
+                                                            int32_t* __restrict__ slice_off,
                                                             int64_t* __restrict__ num_dropped) {
   extern __shared__ int32_t sh[];
   int32_t* cnt = sh;          // [E]
@@ -230,29 +249,34 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     __syncthreads();
   }
 
-  // segment offsets before (pre) and after (offsets) the capacity cut
-  int carry_pre = 0, carry_post = 0;
+  // segment offsets before (pre) and after (offsets) the capacity cut; with a cut,
+  // also the first capacity slice of each expert
+  int carry_pre = 0, carry_post = 0, carry_sl = 0;
   long long dropped = 0;
   for (int i0 = 0; i0 < L; i0 += kScanThreads) {
     const int i = i0 + tid;
     const int n = i < L ? cnt[begin + i] : 0;
     const int kept = cap < 0 ? n : int(min<int64_t>(n, cap));
     dropped += n - kept;
-    int tot_n, tot_k;
+    int tot_n, tot_k, tot_s = 0, ex_s = 0;
     const int ex_n = block_exclusive_scan(n, wsum, &tot_n);
     const int ex_k = block_exclusive_scan(kept, wsum, &tot_k);
+    if (cap >= 0) ex_s = block_exclusive_scan((n + kCapSlice - 1) / kCapSlice, wsum, &tot_s);
     if (i < L) {
       pre[i] = carry_pre + ex_n;
       pre_off[i] = carry_pre + ex_n;
       offsets[i] = carry_post + ex_k;
+      if (cap >= 0) slice_off[i] = carry_sl + ex_s;
     }
     carry_pre += tot_n;
     carry_post += tot_k;
+    carry_sl += tot_s;
   }
   if (tid == 0) {
     pre[L] = carry_pre;
     pre_off[L] = carry_pre;
     offsets[L] = carry_post;
+    if (cap >= 0) slice_off[L] = carry_sl;
   }
   // dropped pairs: sum over threads
   for (int d = 1; d < 64; d <<= 1) dropped += __shfl_xor(dropped, d, 64);
@@ -306,6 +330,96 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
 }
 
+// ---- bases of one chunk without a scan launch ----------------------------------
+// For small chunk-histogram tables a block finds the bases of its own chunk:
+// run[i] = (pairs of the local experts before i) + (pairs of local expert i in
+// the chunks before this one), in pre-capacity rows.  Experts go in groups of up
+// to 256; within a group thread t takes expert t % Lg and every G-th chunk row from
+// t / Lg (rows read coalesced), and the partial sums meet in LDS.  Block 0 also
+// writes counts [E] (the experts outside the local range one per block, its threads
+// splitting the column: one block summing them all would be the last to finish),
+// the segment offsets (after the cut when cap >= 0) and the drop count; with a cut,
+// also the pre-capacity offsets and the first capacity slice of each expert.
+// Every thread of the block must call it.
+__device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E, int begin, int L, int chunk,
+                            int64_t cap, int32_t* run, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ pre_off, int32_t* __restrict__ slice_off,
+                            int64_t* __restrict__ num_dropped) {
+  constexpr int kWaves = kDispatchThreads / 64;
+  __shared__ int wsum[kWaves];
+  __shared__ int ptot[kDispatchThreads], pbef[kDispatchThreads];
+  const int tid = threadIdx.x;
+  const bool first = blockIdx.x == 0;
+  int carry = 0, carry_post = 0, carry_sl = 0, dropped = 0;
+  for (int i0 = 0; i0 < L; i0 += kDispatchThreads) {
+    const int Lg = min(kDispatchThreads, L - i0);
+    const int G = kDispatchThreads / Lg;
+    const int il = tid % Lg, g = tid / Lg;
+    int tot = 0, before = 0;
+    if (g < G) {
+      // chunks g, g + G, ...: those before this chunk, then the rest
+      const int32_t* col = blk_all + begin + i0 + il;
+      const int split = g < chunk ? g + (chunk - g + G - 1) / G * G : g;  // first of this group's chunks >= chunk
+      before = column_sum(col, size_t(E), g, min(split, nblk), G);
+      tot = before + column_sum(col, size_t(E), split, nblk, G);
+    }
+    ptot[tid] = tot;
+    pbef[tid] = before;
+    __syncthreads();
+    tot = 0;
+    before = 0;
+    if (tid < Lg) {
+      for (int gg = 0; gg < G; ++gg) {
+        tot += ptot[gg * Lg + tid];
+        before += pbef[gg * Lg + tid];
+      }
+    }
+    int all;
+    const int ex = carry + block_exclusive_scan(tid < Lg ? tot : 0, wsum, &all);
+    if (tid < Lg) {
+      run[i0 + tid] = ex + before;
+      if (first) counts[begin + i0 + tid] = tot;
+    }
+    if (cap < 0) {
+      if (first && tid < Lg) offsets[i0 + tid] = ex;
+    } else {
+      const int kept = int(min<int64_t>(tot, cap));
+      dropped += tot - kept;
+      int all_k, all_s;
+      const int ex_k = carry_post + block_exclusive_scan(kept, wsum, &all_k);
+      const int ex_s = carry_sl + block_exclusive_scan((tot + kCapSlice - 1) / kCapSlice, wsum, &all_s);
+      if (first && tid < Lg) {
+        pre_off[i0 + tid] = ex;
+        offsets[i0 + tid] = ex_k;
+        slice_off[i0 + tid] = ex_s;
+      }
+      carry_post += all_k;
+      carry_sl += all_s;
+    }
+    carry += all;
+  }
+  if (first) {
+    int all_d = 0;
+    if (cap >= 0) (void)block_exclusive_scan(dropped, wsum, &all_d);
+    if (tid == 0) {
+      offsets[L] = cap < 0 ? carry : carry_post;
+      if (cap >= 0) {
+        pre_off[L] = carry;
+        slice_off[L] = carry_sl;
+      }
+      if (num_dropped != nullptr) *num_dropped = all_d;
+    }
+  }
+  for (int e = int(blockIdx.x); e < E; e += int(gridDim.x)) {
+    if (e >= begin && e < begin + L) continue;
+    int tot = 0;
+    for (int b = tid; b < nblk; b += kDispatchThreads) tot += blk_all[size_t(b) * E + e];
+    int all;
+    (void)block_exclusive_scan(tot, wsum, &all);
+    if (tid == 0) counts[e] = all;
+  }
+}
+
 // ---- scatter ----------------------------------------------------------------
 // Order-preserving key of a float32 logit (larger logit -> larger key); -0.0
 // and +0.0 map to one key because they compare equal.
@@ -315,13 +429,21 @@ __device__ __forceinline__ uint32_t logit_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// CAP: the positions are pre-capacity rows in tmp_sorted, with each pair's logit
-// key beside it in tmp_key (so the capacity cut reads its segment's keys in
-// order); pair_row holds the pre-capacity row until the gather resolves it.
-template <bool CAP>
+// With a capacity limit: the positions are pre-capacity rows in tmp_sorted, with
+// each pair's logit key beside it in tmp_key (so the capacity cut reads its
+// segment's keys in order); pair_row holds the pre-capacity row until the gather
+// resolves it.  FUSED: the block finds its own bases (chunk_bases), else blk_base
+// holds them.
+template <bool FUSED>
 __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t* __restrict__ ids, int64_t n_pairs,
                                                                    int begin, int L, int chunk,
                                                                    const int32_t* __restrict__ blk_base,
+                                                                   const int32_t* __restrict__ blk_all, int nblk, int E,
+                                                                   int64_t cap, int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ pre_off,
+                                                                   int32_t* __restrict__ slice_off,
+                                                                   int64_t* __restrict__ num_dropped,
                                                                    int32_t* __restrict__ out_sorted,
                                                                    int32_t* __restrict__ pair_row,
                                                                    const float* __restrict__ topk_logit,
@@ -332,7 +454,12 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
   constexpr int kWaves = kDispatchThreads / 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  for (int i = tid; i < L; i += kDispatchThreads) run[i] = blk_base[size_t(blockIdx.x) * L + i];
+  if (FUSED) {
+    chunk_bases(blk_all, nblk, E, begin, L, int(blockIdx.x), cap, run, counts, offsets, pre_off, slice_off,
+                num_dropped);
+  } else {
+    for (int i = tid; i < L; i += kDispatchThreads) run[i] = blk_base[size_t(blockIdx.x) * L + i];
+  }
   for (int i = tid; i < kWaves * L; i += kDispatchThreads) cnt[i] = 0;
   __syncthreads();
   const int64_t p0 = int64_t(blockIdx.x) * chunk;
@@ -352,7 +479,7 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
       for (int w = 0; w < wave; ++w) pos += cnt[w * L + li];
       out_sorted[pos] = int32_t(p);
       pair_row[p] = pos;
-      if (CAP) tmp_key[pos] = logit_key(topk_logit[p]);
+      tmp_key[pos] = logit_key(topk_logit[p]);
     } else if (valid) {
       pair_row[p] = -1;
     }
@@ -371,119 +498,205 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
 }
 
 // ---- capacity -----------------------------------------------------------------
+// The cut keeps the cap pairs with the largest keys of each expert over capacity
+// (logit descending, equal keys in segment = token order).  Its blocks each take
+// one slice of kCapSlice consecutive pre-capacity rows of one expert (the slice
+// table comes with the offsets), so a hot expert's segment is spread over several
+// CUs:
+//   cap_hist    per slice of an expert over capacity, the histogram of the keys'
+//               leading 12-bit digit (bits 31..20);
+//   cap_select  per slice: an expert within capacity copies its rows; otherwise the
+//               block takes the whole segment's keys into registers, sums the
+//               slices' histograms, and finishes the radix select of the cap-th
+//               largest key from them (two 10-bit digits over the few keys that
+//               share the leading one), redundantly in every block of the expert
+//               (no grid-wide wait); then it ranks the rows of its own slice from
+//               a ballot scan over the (register, wave) slots of the slices up to
+//               its own.
 constexpr int kCapThreads = 1024;
 constexpr int kCapPerThread = 32;  // register-resident keys per thread (segments up to 32768 pairs)
 constexpr int kCapWaves = kCapThreads / 64;
-constexpr int kCapSlots = kCapPerThread * kCapWaves;  // (register, wave) slots in segment order
-constexpr int kCapBins = 4096;                        // 12-bit radix digits
+constexpr int kSliceRegs = kCapSlice / kCapThreads;   // a slice is registers [4s, 4s + 4) of the segment
 constexpr int kCapCopies = 8;                         // counter copies per digit (lane mod 8)
 constexpr int kCapWords = kCapBins * kCapCopies;      // 128 KB of LDS
-constexpr size_t kCapLds = size_t(kCapWords + kCapSlots + kCapWaves + 2) * 4;
-static_assert(kCapWords >= kCapPerThread * kCapThreads, "the counters' space holds every row's final row");
+constexpr size_t kCapLds = size_t(kCapWords + 1) * 4;  // cap_hist: the counters and one word
+constexpr int kLowBins = 1024;                          // 10-bit digits of the select's last two passes
+constexpr int kRankSlots = kCapWaves + kSliceRegs * kCapWaves;  // earlier-slice sums per wave, then the slice's slots
+constexpr size_t kSelLds = size_t(kCapBins + 2 * kLowBins + kRankSlots + kCapWaves + 3) * 4;
+static_assert(kCapSlice % kCapThreads == 0 && kCapPerThread % kSliceRegs == 0, "slices are whole register groups");
+static_assert(kCapBins == 4 * kCapThreads, "each thread owns four digits of a pass");
 
-// The digit of a radix-select pass: hist[8 d + c] counts, in copy c, the candidate
-// keys of digit d (lane l adds to copy l mod 8, so the lanes of a wave that share a
-// digit spread over eight words); the wanted key is the want-th largest candidate.
-// `pad` keys counted in digit 0 are not candidates (padding) and are taken off.
-// Thread t owns digits nbins-1-4t .. nbins-4-4t (largest first); a block scan of the
-// owners' sums finds the owner whose digits reach `want`.  Leaves the digit in
-// *s_digit and, in *s_want, how many of the wanted keys still have to come from it.
-// Every thread of the block must call it.
-__device__ void pick_digit(const uint32_t* hist, int nbins, int want, uint32_t pad, uint32_t* wsum,
-                           uint32_t* s_digit, int* s_want) {
-  const int t = threadIdx.x;
-  uint32_t c[4], tot = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int d = nbins - 1 - 4 * t - q;
-    c[q] = 0;
-    if (d >= 0) {
-      const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hist + d * kCapCopies);
-      const u32x4_t x = h4[0], y = h4[1];
-      c[q] = (x[0] + x[1]) + (x[2] + x[3]) + (y[0] + y[1]) + (y[2] + y[3]) - (d == 0 ? pad : 0u);
-    }
-    tot += c[q];
-  }
-  uint32_t all;
-  uint32_t before = block_exclusive_scan_u32(tot, wsum, &all);  // keys in larger digits
-  if (before < uint32_t(want) && before + tot >= uint32_t(want)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (before + c[q] >= uint32_t(want)) {
-        *s_digit = uint32_t(nbins - 1 - 4 * t - q);
-        *s_want = int(uint32_t(want) - before);
-        break;
-      }
-      before += c[q];
-    }
+// Digit counts of a radix-select pass are gathered in hist[8 d + c]: copy c of
+// digit d (lane l adds to copy l mod 8, so the lanes of a wave that share a digit
+// spread over eight words).  compact_counts sums the copies into cnt[d]: lanes take
+// consecutive 16-byte chunks (chunk q holds four copies of digit q / 2, so a wave's
+// reads cover the banks without conflicts; per-thread runs of 128 bytes made every
+// read a 32-way bank conflict, ~7k cycles per pass) and neighbouring lanes add their
+// halves.  nbins is a multiple of 32, so whole waves run each round.
+__device__ void compact_counts(const uint32_t* hist, int nbins, uint32_t* cnt) {
+  const u32x4_t* h4 = reinterpret_cast<const u32x4_t*>(hist);
+  for (int q = threadIdx.x; q < 2 * nbins; q += blockDim.x) {
+    const u32x4_t x = h4[q];
+    uint32_t v = (x[0] + x[1]) + (x[2] + x[3]);
+    v += uint32_t(__shfl_xor(int(v), 1, 64));
+    if ((q & 1) == 0) cnt[q >> 1] = v;
   }
 }
 
-// One block per local expert.  The pre-capacity segment of expert i is rows
-// [pre_off[i], pre_off[i+1]) of tmp_sorted (pair ids, in pair order) and tmp_key
-// (their logit keys).  An expert within capacity keeps every pair; otherwise the
-// cap pairs with the largest keys are kept, equal keys in segment (= token) order.
-// Writes sorted_pairs for the kept pairs (in segment order from offsets[i]) and,
-// for every pre-capacity row, its final row or -1 in tmp_final: every access is in
-// segment order, and the gather resolves pair_row through tmp_final.
-// After the radix select of the cap-th largest key, one scan over the 512
-// (register, wave) slots of packed counts -- keys above the threshold in the low
-// half, keys equal to it in the high half -- gives every kept key its row: (keys
-// above before it) + min(equal keys before it, equal keys kept).  An expert's whole
-// segment is one block on one CU, so the kernel is bound by vector issue there (a
-// wave64 instruction takes four cycles of a 16-lane SIMD; 16 waves, ~20 instructions
-// per key and phase) and by LDS atomics on the few digits that similar logits share.
-__global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ tmp_sorted,
-                                                               const uint32_t* __restrict__ tmp_key,
+// The digit of a radix-select pass from cnt[d], the candidate keys of digit d: the
+// wanted key is the want-th largest candidate.  `pad` keys counted in digit 0 are not
+// candidates (padding) and are taken off.  One wave walks the digits from the top,
+// 256 per step (lane l holds digits top-1-4l .. top-4-4l: one 16-byte read, lanes
+// contiguous), with a DPP scan of the lanes' sums; the lane whose digits reach `want`
+// leaves the digit in *s_digit and, in *s_want, how many of the wanted keys still have
+// to come from it.  nbins is a multiple of 256.  Called by one whole wave; the block
+// waits at a barrier meanwhile (a block-wide scan here cost three barriers a pass).
+__device__ void wave_pick_digit(const uint32_t* cnt, int nbins, int want, uint32_t pad, uint32_t* s_digit,
+                                int* s_want) {
+  const int lane = threadIdx.x & 63;
+  uint32_t before = 0;  // candidates in larger digits (the same in every lane)
+  for (int top = nbins; top > 0; top -= 256) {
+    const u32x4_t x = reinterpret_cast<const u32x4_t*>(cnt + top - 4 - 4 * lane)[0];
+    uint32_t c[4] = {x[3], x[2], x[1], x[0]};  // digits top-1-4l, ..., top-4-4l
+    if (top - 4 - 4 * lane == 0) c[3] -= pad;
+    const uint32_t tot = (c[0] + c[1]) + (c[2] + c[3]);
+    const uint32_t incl = wave_scan_u32(tot);
+    const uint32_t all = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    if (before + all >= uint32_t(want)) {
+      uint32_t ex = before + incl - tot;
+      if (ex < uint32_t(want) && ex + tot >= uint32_t(want)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (ex + c[q] >= uint32_t(want)) {
+            *s_digit = uint32_t(top - 1 - 4 * lane - q);
+            *s_want = int(uint32_t(want) - ex);
+            break;
+          }
+          ex += c[q];
+        }
+      }
+      return;
+    }
+    before += all;
+  }
+}
+
+// The local expert whose slices hold capacity block b (slice_off[i] <= b <
+// slice_off[i+1]; an expert with no rows has no slice), or -1 when b is past the
+// last slice: one round of loads, every thread testing some experts.  Every thread
+// of the block must call it.
+__device__ int slice_expert(const int32_t* __restrict__ slice_off, int L, int b, int* s_exp) {
+  if (threadIdx.x == 0) *s_exp = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < L; i += blockDim.x)
+    if (slice_off[i] <= b && b < slice_off[i + 1]) *s_exp = i;
+  __syncthreads();
+  return *s_exp;
+}
+
+// Leading-digit histogram of one slice of an expert over capacity:
+// slice_hist[b][d] = keys of slice b whose bits 31..20 are d.
+__global__ __launch_bounds__(kCapThreads) void cap_hist_kernel(const uint32_t* __restrict__ tmp_key,
                                                                const int32_t* __restrict__ pre_off,
-                                                               const int32_t* __restrict__ offsets, int cap,
-                                                               int32_t* __restrict__ sorted_pairs,
-                                                               int32_t* __restrict__ tmp_final) {
-  // all of the block's LDS is dynamic (no static arrays), so the counters start at
-  // offset 0 and their 16-byte reads and writes are aligned
+                                                               const int32_t* __restrict__ slice_off, int L, int cap,
+                                                               uint32_t* __restrict__ slice_hist) {
+  // all of the block's LDS is dynamic, so the counters start at offset 0 (aligned 16-byte accesses)
   extern __shared__ int32_t sh[];
   uint32_t* hist = reinterpret_cast<uint32_t*>(sh);  // [kCapWords]
-  uint32_t* slot_cnt = hist + kCapWords;             // [kCapSlots]
-  uint32_t* wsum = slot_cnt + kCapSlots;             // [kCapWaves]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int i = slice_expert(slice_off, L, b, sh + kCapWords);
+  if (i < 0) return;
+  const int a = pre_off[i];
+  const int n = pre_off[i + 1] - a;
+  if (n <= cap) return;
+  const int r0 = (b - slice_off[i]) * kCapSlice;
+  uint32_t key[kSliceRegs];
+#pragma unroll
+  for (int u = 0; u < kSliceRegs; ++u) {
+    const int r = r0 + u * kCapThreads + tid;
+    key[u] = r < n ? tmp_key[a + r] : 0u;
+  }
+  u32x4_t* hist4 = reinterpret_cast<u32x4_t*>(hist);
+  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  for (int q = tid; q < kCapWords / 4; q += kCapThreads) hist4[q] = zero4;
+  __syncthreads();
+  const int copy = tid & (kCapCopies - 1);
+#pragma unroll
+  for (int u = 0; u < kSliceRegs; ++u)
+    if (r0 + u * kCapThreads + tid < n) atomicAdd(&hist[(key[u] >> 20) * kCapCopies + copy], 1u);
+  __syncthreads();
+  compact_counts(hist, kCapBins, slice_hist + size_t(b) * kCapBins);
+}
+
+// One slice of an expert's pre-capacity segment, rows [r0, r0 + kCapSlice) of
+// tmp_sorted (pair ids, in pair order) and tmp_key (their logit keys), segment
+// [pre_off[i], pre_off[i+1]).  Writes sorted_pairs for the slice's kept pairs (at
+// their rows from offsets[i]) and, for every row of the slice, its final row or -1
+// in tmp_final; the gather resolves pair_row through tmp_final.
+// A kept key's row is (keys above the threshold before it) + min(keys equal to it
+// before it, equal keys kept), from one scan over the (register, wave) slots of the
+// slices up to this one, of packed counts (keys above the threshold in the low half,
+// equal in the high half), and the lanes below the key in its slot.
+__global__ __launch_bounds__(kCapThreads) void cap_select_kernel(const int32_t* __restrict__ tmp_sorted,
+                                                                 const uint32_t* __restrict__ tmp_key,
+                                                                 const int32_t* __restrict__ pre_off,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 const int32_t* __restrict__ slice_off,
+                                                                 const uint32_t* __restrict__ slice_hist, int L,
+                                                                 int cap, int32_t* __restrict__ sorted_pairs,
+                                                                 int32_t* __restrict__ tmp_final) {
+  extern __shared__ int32_t sh[];
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(sh);   // [kCapBins]   leading-digit counts
+  uint32_t* low = cnt + kCapBins;                    // [2][kLowBins] counts of the two 10-bit passes
+  uint32_t* slot_cnt = low + 2 * kLowBins;           // [kRankSlots]
+  uint32_t* wsum = slot_cnt + kRankSlots;            // [kCapWaves]
   uint32_t& s_digit = wsum[kCapWaves];
   int& s_want = reinterpret_cast<int*>(wsum)[kCapWaves + 1];
   const int tid = threadIdx.x;
-  const int i = blockIdx.x;
+  const int b = blockIdx.x;
+  const int i = slice_expert(slice_off, L, b, reinterpret_cast<int*>(wsum) + kCapWaves + 2);
+  if (i < 0) return;
   const int a = pre_off[i];
   const int n = pre_off[i + 1] - a;
   const int out0 = offsets[i];
+  const int sl = b - slice_off[i];
+  const int r0 = sl * kCapSlice;
   const int32_t* seg = tmp_sorted + a;
 
-  if (n <= cap) {  // rows in batches of four per thread, the loads issued together
-    for (int r0 = tid; r0 < n; r0 += 4 * kCapThreads) {
-      int32_t v[4];
+  if (n <= cap) {  // every row kept, in place
+    int32_t v[kSliceRegs];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = r0 + u * kCapThreads < n ? seg[r0 + u * kCapThreads] : 0;
+    for (int u = 0; u < kSliceRegs; ++u) {
+      const int r = r0 + u * kCapThreads + tid;
+      v[u] = r < n ? seg[r] : 0;
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = r0 + u * kCapThreads;
-        if (r < n) {
-          sorted_pairs[out0 + r] = v[u];
-          tmp_final[a + r] = out0 + r;
-        }
+    for (int u = 0; u < kSliceRegs; ++u) {
+      const int r = r0 + u * kCapThreads + tid;
+      if (r < n) {
+        sorted_pairs[out0 + r] = v[u];
+        tmp_final[a + r] = out0 + r;
       }
     }
     return;
   }
-
   if (cap == 0) {  // nothing is kept
-    for (int r = tid; r < n; r += kCapThreads) tmp_final[a + r] = -1;
+#pragma unroll
+    for (int u = 0; u < kSliceRegs; ++u) {
+      const int r = r0 + u * kCapThreads + tid;
+      if (r < n) tmp_final[a + r] = -1;
+    }
     return;
   }
 
   // element r = j*1024 + tid of the segment sits in this thread's register j
-  // (coalesced loads; segment order is j-major, then wave, then lane)
-  // Rows past the segment hold key 0 as padding.  The histograms skip registers
-  // with no row of the segment (j*1024 >= n, a wave-uniform test); the rest's npad
-  // padding keys are candidates while the digits chosen so far are all 0, always in
-  // digit 0, which the digit pick takes off.  A padding key is never above a
-  // threshold and comes after every real row in segment order, so it never takes a
-  // kept row.
+  // (coalesced loads; segment order is j-major, then wave, then lane).  Rows past the
+  // segment hold key 0 as padding; the digit passes skip registers with no row of the
+  // segment (j*1024 >= n, a wave-uniform test), and the rest's npad padding keys are
+  // candidates while the digits chosen so far are all 0, always in digit 0, which the
+  // digit pick takes off.  A padding key is never above a threshold and comes after
+  // every real row in segment order, so it never takes a kept row.
   const int lane = tid & 63, wave = tid >> 6;
   const int nreg = (n + kCapThreads - 1) / kCapThreads;
   const uint32_t npad = uint32_t(nreg * kCapThreads - n);
@@ -494,83 +707,101 @@ __global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __
     const uint32_t r = uint32_t(j * kCapThreads + tid);
     key[j] = r < uint32_t(n) ? kseg[r] : 0u;
   }
-  u32x4_t* hist4 = reinterpret_cast<u32x4_t*>(hist);
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-  const int copy = lane & (kCapCopies - 1);
 
-  // radix select of the cap-th largest key, 12-bit digits (bits 31..20, 19..8) then
-  // 8 bits: float logits share a few exponents, and 12-bit leading digits spread
-  // them over tens of bins where 8-bit ones leave a handful
-  uint32_t prefix = 0, mask = 0;
-  int want = cap;
-  const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
+  // leading digit: the slices' histograms summed (thread t takes digits 4t .. 4t+3),
+  // no padding counted; the counters of the later passes cleared meanwhile
+  {
+    const int s0 = slice_off[i], s1 = slice_off[i + 1];
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+    for (int s = s0; s < s1; ++s) {
+      const u32x4_t h = reinterpret_cast<const u32x4_t*>(slice_hist + size_t(s) * kCapBins)[tid];
+      acc[0] += h[0];
+      acc[1] += h[1];
+      acc[2] += h[2];
+      acc[3] += h[3];
+    }
+    reinterpret_cast<u32x4_t*>(cnt)[tid] = acc;
+    for (int q = tid; q < 2 * kLowBins; q += kCapThreads) low[q] = 0u;
+  }
+  __syncthreads();
+  if (wave == 0) wave_pick_digit(cnt, kCapBins, cap, 0u, &s_digit, &s_want);
+  __syncthreads();
+  uint32_t prefix = s_digit << 20, mask = 0xFFF00000u;
+  int want = s_want;
+  // the remaining 20 bits in two 10-bit digits over the keys that share the digits so
+  // far.  Those are few, so each pass counts into one word per digit (ties of many
+  // equal keys only make their atomics queue); the next pass has counters of its own,
+  // so the digit and count read here are not overwritten before every wave has them.
 #pragma unroll
-  for (int ps = 0; ps < 3; ++ps) {
-    const int shift = shifts[ps], nbins = 1 << widths[ps];
-    for (int q = tid; q < nbins * kCapCopies / 4; q += kCapThreads) hist4[q] = zero4;
-    __syncthreads();
+  for (int ps = 0; ps < 2; ++ps) {
+    const int shift = 10 - 10 * ps;
+    uint32_t* h = low + ps * kLowBins;
 #pragma unroll
     for (int j = 0; j < kCapPerThread; ++j)
-      if (j < nreg && (key[j] & mask) == prefix)
-        atomicAdd(&hist[((key[j] >> shift) & uint32_t(nbins - 1)) * kCapCopies + copy], 1u);
+      if (j < nreg && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> shift) & uint32_t(kLowBins - 1)], 1u);
     __syncthreads();
-    pick_digit(hist, nbins, want, prefix == 0 ? npad : 0u, wsum, &s_digit, &s_want);
+    if (wave == 0) wave_pick_digit(h, kLowBins, want, prefix == 0 ? npad : 0u, &s_digit, &s_want);
     __syncthreads();
     prefix |= s_digit << shift;
-    mask |= uint32_t(nbins - 1) << shift;
+    mask |= uint32_t(kLowBins - 1) << shift;
     want = s_want;
-    __syncthreads();
   }
   const uint32_t thr = prefix;
   const uint32_t need_eq = uint32_t(want);  // keys equal to thr kept: the first need_eq in segment order
 
-  // per (register, wave) slot: keys above thr (low half) and equal to it (high half);
-  // per key, the same counts over the lanes below it in its slot
+  // One scan over packed counts (keys above thr in the low half, equal to it in the high
+  // half; halves stay below 2^16, so no carry): first, per wave, its threads' keys in the
+  // slices before this one (every element there is a row of the segment), then per
+  // (register, wave) slot of this slice; per key of the slice, the same counts over the
+  // lanes below it in its slot.
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kCapPerThread; ++j)
+    if (j < kSliceRegs * sl) mine += (key[j] > thr ? 1u : 0u) + (key[j] == thr ? 0x10000u : 0u);
+  mine = wave_scan_u32(mine);
+  if (lane == 63) slot_cnt[wave] = mine;
   const uint64_t below = lanemask_lt();
-  uint32_t lcnt[kCapPerThread];
+  uint32_t lcnt[kSliceRegs], skey[kSliceRegs];
 #pragma unroll
   for (int j = 0; j < kCapPerThread; ++j) {
-    const uint64_t gm = __ballot(key[j] > thr), em = __ballot(key[j] == thr);
-    lcnt[j] = uint32_t(__popcll(gm & below)) | (uint32_t(__popcll(em & below)) << 16);
-    if (lane == 0) slot_cnt[j * kCapWaves + wave] = uint32_t(__popcll(gm)) | (uint32_t(__popcll(em)) << 16);
+    if (j / kSliceRegs == sl) {  // wave-uniform
+      const int jj = j % kSliceRegs;
+      const uint64_t gm = __ballot(key[j] > thr), em = __ballot(key[j] == thr);
+      lcnt[jj] = uint32_t(__popcll(gm & below)) | (uint32_t(__popcll(em & below)) << 16);
+      skey[jj] = key[j];
+      if (lane == 0)
+        slot_cnt[kCapWaves + jj * kCapWaves + wave] = uint32_t(__popcll(gm)) | (uint32_t(__popcll(em)) << 16);
+    }
   }
   __syncthreads();
   {
-    const uint32_t v = tid < kCapSlots ? slot_cnt[tid] : 0u;
+    const uint32_t v = tid < kRankSlots ? slot_cnt[tid] : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan_u32(v, wsum, &tot);
-    if (tid < kCapSlots) slot_cnt[tid] = ex;
-  }
-  __syncthreads();
-  // every row's final row (or -1) into LDS, where the counters were (so that no row
-  // address stays live in registers across the kernel)
-  int32_t* fin = reinterpret_cast<int32_t*>(hist);
-#pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j) {
-    const bool gt = key[j] > thr, eq = key[j] == thr;
-    const uint32_t c = slot_cnt[j * kCapWaves + wave] + lcnt[j];  // no carry: halves stay below 2^16
-    const uint32_t gb = c & 0xffffu, eb = c >> 16;
-    fin[j * kCapThreads + tid] = (gt || (eq && eb < need_eq)) ? out0 + int(gb + min(eb, need_eq)) : -1;
+    if (tid < kRankSlots) slot_cnt[tid] = ex;
   }
   __syncthreads();
   // every pair-id load in flight at once, then the stores (a kept row always lands in
   // [out0, out_end); the test only keeps this kernel and the gather in bounds)
   const int out_end = offsets[i + 1];
-  int32_t* tfin = tmp_final + a;
-  int32_t f[kCapPerThread], v[kCapPerThread];
+  int32_t f[kSliceRegs], v[kSliceRegs];
 #pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j) {
-    const uint32_t r = uint32_t(j * kCapThreads + tid);
-    f[j] = r < uint32_t(n) ? fin[r] : -1;
-    v[j] = f[j] >= 0 ? seg[r] : 0;
+  for (int jj = 0; jj < kSliceRegs; ++jj) {
+    const int r = r0 + jj * kCapThreads + tid;
+    const bool gt = skey[jj] > thr, eq = skey[jj] == thr;
+    const uint32_t c = slot_cnt[kCapWaves + jj * kCapWaves + wave] + lcnt[jj];
+    const uint32_t gb = c & 0xffffu, eb = c >> 16;
+    f[jj] = (r < n && (gt || (eq && eb < need_eq))) ? out0 + int(gb + min(eb, need_eq)) : -1;
+    v[jj] = f[jj] >= 0 ? seg[r] : 0;
   }
 #pragma unroll
-  for (int j = 0; j < kCapPerThread; ++j) {
-    const uint32_t r = uint32_t(j * kCapThreads + tid);
-    if (r < uint32_t(n)) {
-      const bool kept = f[j] >= out0 && f[j] < out_end;
-      if (kept) sorted_pairs[f[j]] = v[j];
-      tfin[r] = kept ? f[j] : -1;
+  for (int jj = 0; jj < kSliceRegs; ++jj) {
+    const int r = r0 + jj * kCapThreads + tid;
+    if (r < n) {
+      const bool kept = f[jj] >= out0 && f[jj] < out_end;
+      if (kept) sorted_pairs[f[jj]] = v[jj];
+      tmp_final[a + r] = kept ? f[jj] : -1;
     }
   }
 }
@@ -669,62 +900,7 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
   const int64_t p0 = t0 * k;
 
   if (FUSED) {
-    // per local expert i: total over all chunks and over the chunks before this one;
-    // run[i] = (exclusive scan of the totals)[i] + (this expert's pairs in earlier chunks).
-    // Experts in groups of up to 256; within a group, thread t takes expert t % Lg and
-    // every G-th chunk row from t / Lg (rows read coalesced), partial sums meet in LDS.
-    __shared__ int wsum[kWaves];
-    __shared__ int ptot[kDispatchThreads], pbef[kDispatchThreads];
-    int carry = 0;
-    for (int i0 = 0; i0 < L; i0 += kDispatchThreads) {
-      const int Lg = min(kDispatchThreads, L - i0);
-      const int G = kDispatchThreads / Lg;
-      const int il = tid % Lg, g = tid / Lg;
-      int tot = 0, before = 0;
-      if (g < G) {
-        // chunks g, g + G, ...: those before this chunk, then the rest
-        const int32_t* col = blk_all + begin + i0 + il;
-        const int split = g < chunk ? g + (chunk - g + G - 1) / G * G : g;  // first of this group's chunks >= chunk
-        before = column_sum(col, size_t(E), g, min(split, nblk), G);
-        tot = before + column_sum(col, size_t(E), split, nblk, G);
-      }
-      ptot[tid] = tot;
-      pbef[tid] = before;
-      __syncthreads();
-      tot = 0;
-      before = 0;
-      if (tid < Lg) {
-        for (int gg = 0; gg < G; ++gg) {
-          tot += ptot[gg * Lg + tid];
-          before += pbef[gg * Lg + tid];
-        }
-      }
-      int all;
-      const int ex = carry + block_exclusive_scan(tid < Lg ? tot : 0, wsum, &all);
-      if (tid < Lg) {
-        run[i0 + tid] = ex + before;
-        if (blockIdx.x == 0) {
-          offsets[i0 + tid] = ex;
-          counts[begin + i0 + tid] = tot;
-        }
-      }
-      carry += all;
-    }
-    if (blockIdx.x == 0 && tid == 0) {
-      offsets[L] = carry;
-      if (num_dropped != nullptr) *num_dropped = 0;
-    }
-    // the totals of the experts outside the local range (not needed above): one expert per
-    // block, the block's threads splitting its column of chunk counts (one block summing
-    // them all would be the last to finish)
-    for (int e = int(blockIdx.x); e < E; e += int(gridDim.x)) {
-      if (e >= begin && e < begin + L) continue;
-      int tot = 0;
-      for (int b = tid; b < nblk; b += kDispatchThreads) tot += blk_all[size_t(b) * E + e];
-      int all;
-      (void)block_exclusive_scan(tot, wsum, &all);
-      if (tid == 0) counts[e] = all;
-    }
+    chunk_bases(blk_all, nblk, E, begin, L, chunk, -1, run, counts, offsets, nullptr, nullptr, num_dropped);
   } else {
     for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
   }
@@ -814,24 +990,36 @@ moe_status launch_dispatch(const DispatchArgs& a) {
     MOE_LAUNCH("dispatch_count", count_kernel, dim3(nblk), dim3(kDispatchThreads), size_t(E) * 4, a.s, a.topk_ids, n, E,
                chunk, a.scr.blk_all);
   }
-  // without a capacity cut and with a small chunk-histogram table the place kernel finds its own bases
-  const bool fused = !cap && int64_t(nblk) * E <= kFuseEntries;
+  // with a small chunk-histogram table the place (or scatter) kernel finds its own bases
+  const bool fused = int64_t(nblk) * E <= kFuseEntries;
   if (!fused) {
     MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all,
-               nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.num_dropped);
+               nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.scr.slice_off,
+               a.num_dropped);
   }
   if (cap) {
     const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
-    MOE_LAUNCH("dispatch_scatter", scatter_kernel<true>, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n,
-               begin, L, chunk, a.scr.blk_base, a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
-    const size_t cap_lds = kCapLds;
-    {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(capacity_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(cap_lds));
-      if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_capacity: LDS attribute: %s", hipGetErrorString(e));
+    auto scatter = fused ? scatter_kernel<true> : scatter_kernel<false>;
+    if (scat_lds > 65536 - 4096) {  // thousands of local experts (the block also holds ~2 KB of static LDS)
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scatter),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(scat_lds));
+      if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_scatter: LDS attribute: %s", hipGetErrorString(e));
     }
-    MOE_LAUNCH("dispatch_capacity", capacity_kernel, dim3(L), dim3(kCapThreads), cap_lds, a.s, a.scr.tmp_sorted,
-               a.scr.tmp_key, a.scr.pre_off, a.offsets, int(a.capacity), a.sorted_pairs, a.scr.tmp_final);
+    MOE_LAUNCH("dispatch_scatter", scatter, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n, begin, L, chunk, a.scr.blk_base, a.scr.blk_all,
+               nblk, E, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.slice_off, a.num_dropped,
+               a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
+    {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(cap_hist_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(kCapLds));
+      if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_cap_hist: LDS attribute: %s", hipGetErrorString(e));
+    }
+    // one block per slice slot; blocks past the last slice return at once
+    const dim3 slices(unsigned(cap_slices_max(d)));
+    MOE_LAUNCH("dispatch_cap_hist", cap_hist_kernel, slices, dim3(kCapThreads), kCapLds, a.s, a.scr.tmp_key,
+               a.scr.pre_off, a.scr.slice_off, L, int(a.capacity), a.scr.slice_hist);
+    MOE_LAUNCH("dispatch_capacity", cap_select_kernel, slices, dim3(kCapThreads), kSelLds, a.s, a.scr.tmp_sorted,
+               a.scr.tmp_key, a.scr.pre_off, a.offsets, a.scr.slice_off, a.scr.slice_hist, L, int(a.capacity),
+               a.sorted_pairs, a.scr.tmp_final);
     const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
     MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const u32x4_t*>(a.x), a.pair_row,
                a.scr.tmp_final, d->num_tokens, d->top_k, vec_per_row, static_cast<u32x4_t*>(a.x_sorted));

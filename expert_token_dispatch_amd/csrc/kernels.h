@@ -64,6 +64,9 @@ struct DispatchScratch {
   int32_t* tmp_sorted; // [T*k]       pre-capacity permutation (capacity only)
   uint32_t* tmp_key;   // [T*k]       logit keys beside it (capacity only)
   int32_t* tmp_final;  // [T*k]       final row of each pre-capacity row, -1 if cut (capacity only)
+  int32_t* slice_off;  // [L+1]       first capacity slice of each local expert (capacity only)
+  uint32_t* slice_hist; // [slices, 4096] leading-digit histogram of each slice of an expert over
+                        //             capacity (capacity only)
 };
 size_t dispatch_scratch_bytes(const moe_layer_desc* d);
 DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws);

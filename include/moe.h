@@ -263,7 +263,8 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
  * from the previous call.  MOE_ERR_UNSUPPORTED (nothing enqueued) when the
  * layer needs more scratch than the buffer holds (the MOE_STAGE_DISPATCH
  * size, moe_workspace_size, above 16 MiB: roughly T * (E + L) / 16 bytes,
- * plus 12 T k with a capacity factor); other errors as moe_dispatch. */
+ * plus 16 T k + 16 KiB * L with a capacity factor); other errors as
+ * moe_dispatch. */
 moe_status moe_dispatch_noalloc(const moe_layer_desc* d, const void* x, const int32_t* topk_ids,
                                 const float* topk_logit, int32_t* counts, int32_t* offsets,
                                 int32_t* sorted_pairs, int32_t* pair_row, void* x_sorted,

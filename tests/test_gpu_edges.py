@@ -113,14 +113,26 @@ def test_capacity_drops_everything_for_some_tokens():
     assert np.all(gpu["y"][C:] == 0)
 
 
-@pytest.mark.parametrize("case", ["max_segment", "ragged_clustered"])
+@pytest.mark.parametrize("case", ["max_segment", "ragged_clustered", "many_slices"])
 def test_capacity_cut_large_segments(case):
-    # The capacity cut keeps a segment's keys 32 per thread of a 1024-thread block: a
-    # segment of the most tokens a call takes (32768, every register full, no padding),
-    # and segments of several thousand keys that are not multiples of 1024 (padding
-    # rows) whose logits share a handful of values (many keys per radix digit, ties
-    # ranked by token).
-    if case == "max_segment":
+    # The capacity cut keeps a segment's keys 32 per thread of a 1024-thread block and
+    # ranks them in slices of 4096 rows, one block per slice: a segment of the most
+    # tokens a call takes (32768, every register full, no padding, eight slices),
+    # segments of several thousand keys that are not multiples of 1024 (padding rows)
+    # whose logits share a handful of values (many keys per radix digit, ties ranked by
+    # token across slice edges), and a local range past expert 0 with hot experts of
+    # 2 to 5 slices, experts within capacity and one that receives nothing between them.
+    if case == "many_slices":
+        s = synth.spec("skewed_capacity", T=20000, H=64, I=64, E=16, k=3, local_begin=2, L=12,
+                       capacity_factor=1.0)
+        rng = np.random.default_rng(13)
+        lg = rng.standard_normal((s.T, s.E)).astype(np.float32)
+        lg[:, 5] = -50.0                                   # local expert 3 (id 5) gets nothing
+        lg[:, 3] += 2.5                                    # hot: in most tokens' top 3
+        lg[:, 7] += 1.5
+        lg[: s.T // 2, 9] = np.round(lg[: s.T // 2, 9] * 2) / 2 + 3.0  # ties, half the tokens
+        lg[:, 13] = np.where(np.arange(s.T) % 7 < 3, 4.0, lg[:, 13])   # one tied score, 3/7 of tokens
+    elif case == "max_segment":
         s = synth.spec("skewed_capacity", T=32768, H=64, I=64, E=8, k=1, L=8, capacity_factor=0.5)
         rng = np.random.default_rng(11)
         lg = np.zeros((s.T, s.E), dtype=np.float32)
