@@ -63,6 +63,7 @@ size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   if (d->capacity_factor > 0) {
     b += 3 * align_up(size_t(n) * 4, 256);
     b += align_up(size_t(d->local_count + 1) * 4, 256);
+    b += align_up(size_t(cap_slices_max(d)) * 16, 256);
     b += align_up(size_t(cap_slices_max(d)) * kCapBins * 4, 256);
   }
   return b;
@@ -88,12 +89,21 @@ DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
     p += align_up(size_t(n) * 4, 256);
     s.slice_off = reinterpret_cast<int32_t*>(p);
     p += align_up(size_t(d->local_count + 1) * 4, 256);
+    s.slice_desc = reinterpret_cast<int32_t*>(p);
+    p += align_up(size_t(cap_slices_max(d)) * 16, 256);
     s.slice_hist = reinterpret_cast<uint32_t*>(p);
   }
   return s;
 }
 
 namespace {
+
+// The descriptors of local expert i's capacity slices: {its first slice, pre-capacity
+// segment start, segment length, first kept row}, one per slice.
+__device__ __forceinline__ void write_slice_desc(int32_t* __restrict__ slice_desc, int first, int pre, int n, int out0) {
+  const int ns = (n + kCapSlice - 1) / kCapSlice;
+  for (int q = 0; q < ns; ++q) reinterpret_cast<int4*>(slice_desc)[first + q] = make_int4(first, pre, n, out0);
+}
 
 __device__ __forceinline__ int bits_for(int maxval) { return 32 - __clz(maxval); }
 
@@ -188,6 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ pre_off,
                                                             int32_t* __restrict__ blk_base,
                                                             int32_t* __restrict__ slice_off,
+                                                            int32_t* __restrict__ slice_desc,
                                                             int64_t* __restrict__ num_dropped) {
   extern __shared__ int32_t sh[];
   int32_t* cnt = sh;          // [E]
@@ -266,7 +277,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
       pre[i] = carry_pre + ex_n;
       pre_off[i] = carry_pre + ex_n;
       offsets[i] = carry_post + ex_k;
-      if (cap >= 0) slice_off[i] = carry_sl + ex_s;
+      if (cap >= 0) {
+        slice_off[i] = carry_sl + ex_s;
+        write_slice_desc(slice_desc, carry_sl + ex_s, carry_pre + ex_n, n, carry_post + ex_k);
+      }
     }
     carry_pre += tot_n;
     carry_post += tot_k;
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
 __device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E, int begin, int L, int chunk,
                             int64_t cap, int32_t* run, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                             int32_t* __restrict__ pre_off, int32_t* __restrict__ slice_off,
-                            int64_t* __restrict__ num_dropped) {
+                            int32_t* __restrict__ slice_desc, int64_t* __restrict__ num_dropped) {
   constexpr int kWaves = kDispatchThreads / 64;
   __shared__ int wsum[kWaves];
   __shared__ int ptot[kDispatchThreads], pbef[kDispatchThreads];
@@ -392,6 +406,7 @@ __device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E
         pre_off[i0 + tid] = ex;
         offsets[i0 + tid] = ex_k;
         slice_off[i0 + tid] = ex_s;
+        write_slice_desc(slice_desc, ex_s, ex, tot, ex_k);
       }
       carry_post += all_k;
       carry_sl += all_s;
@@ -443,6 +458,7 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
                                                                    int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ pre_off,
                                                                    int32_t* __restrict__ slice_off,
+                                                                   int32_t* __restrict__ slice_desc,
                                                                    int64_t* __restrict__ num_dropped,
                                                                    int32_t* __restrict__ out_sorted,
                                                                    int32_t* __restrict__ pair_row,
@@ -456,7 +472,7 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
   const int wave = tid >> 6;
   if (FUSED) {
     chunk_bases(blk_all, nblk, E, begin, L, int(blockIdx.x), cap, run, counts, offsets, pre_off, slice_off,
-                num_dropped);
+                slice_desc, num_dropped);
   } else {
     for (int i = tid; i < L; i += kDispatchThreads) run[i] = blk_base[size_t(blockIdx.x) * L + i];
   }
@@ -522,6 +538,7 @@ constexpr int kCapWords = kCapBins * kCapCopies;      // 128 KB of LDS
 constexpr size_t kCapLds = size_t(kCapWords + 1) * 4;  // cap_hist: the counters and one word
 constexpr int kLowBins = 1024;                          // 10-bit digits of the select's last two passes
 constexpr int kRankSlots = kCapWaves + kSliceRegs * kCapWaves;  // earlier-slice sums per wave, then the slice's slots
+static_assert(kRankSlots > 64 && kRankSlots <= 128, "one wave scans the rank slots, two per lane");
 constexpr size_t kSelLds = size_t(kCapBins + 2 * kLowBins + kRankSlots + kCapWaves + 3) * 4;
 static_assert(kCapSlice % kCapThreads == 0 && kCapPerThread % kSliceRegs == 0, "slices are whole register groups");
 static_assert(kCapBins == 4 * kCapThreads, "each thread owns four digits of a pass");
@@ -581,36 +598,33 @@ __device__ void wave_pick_digit(const uint32_t* cnt, int nbins, int want, uint32
   }
 }
 
-// The local expert whose slices hold capacity block b (slice_off[i] <= b <
-// slice_off[i+1]; an expert with no rows has no slice), or -1 when b is past the
-// last slice: one round of loads, every thread testing some experts.  Every thread
-// of the block must call it.
-__device__ int slice_expert(const int32_t* __restrict__ slice_off, int L, int b, int* s_exp) {
-  if (threadIdx.x == 0) *s_exp = -1;
-  __syncthreads();
-  for (int i = threadIdx.x; i < L; i += blockDim.x)
-    if (slice_off[i] <= b && b < slice_off[i + 1]) *s_exp = i;
-  __syncthreads();
-  return *s_exp;
+// Capacity block b's slice: false when b is past the last slice (slice_off[L]);
+// else its descriptor {expert's first slice, segment start, length, first kept row}.
+// Both loads are in flight together: the grid has one block per descriptor entry, so
+// entry b is in bounds even when it is not in use (its contents are then ignored).
+__device__ __forceinline__ bool slice_of(const int32_t* __restrict__ slice_off, const int32_t* __restrict__ slice_desc,
+                                         int L, int b, int4* dsc) {
+  const int total = slice_off[L];
+  *dsc = reinterpret_cast<const int4*>(slice_desc)[b];
+  return b < total;
 }
 
 // Leading-digit histogram of one slice of an expert over capacity:
 // slice_hist[b][d] = keys of slice b whose bits 31..20 are d.
 __global__ __launch_bounds__(kCapThreads) void cap_hist_kernel(const uint32_t* __restrict__ tmp_key,
-                                                               const int32_t* __restrict__ pre_off,
-                                                               const int32_t* __restrict__ slice_off, int L, int cap,
+                                                               const int32_t* __restrict__ slice_off,
+                                                               const int32_t* __restrict__ slice_desc, int L, int cap,
                                                                uint32_t* __restrict__ slice_hist) {
   // all of the block's LDS is dynamic, so the counters start at offset 0 (aligned 16-byte accesses)
   extern __shared__ int32_t sh[];
   uint32_t* hist = reinterpret_cast<uint32_t*>(sh);  // [kCapWords]
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int i = slice_expert(slice_off, L, b, sh + kCapWords);
-  if (i < 0) return;
-  const int a = pre_off[i];
-  const int n = pre_off[i + 1] - a;
+  int4 dsc;
+  if (!slice_of(slice_off, slice_desc, L, b, &dsc)) return;
+  const int a = dsc.y, n = dsc.z;
   if (n <= cap) return;
-  const int r0 = (b - slice_off[i]) * kCapSlice;
+  const int r0 = (b - dsc.x) * kCapSlice;
   uint32_t key[kSliceRegs];
 #pragma unroll
   for (int u = 0; u < kSliceRegs; ++u) {
@@ -631,18 +645,17 @@ __global__ __launch_bounds__(kCapThreads) void cap_hist_kernel(const uint32_t* _
 
 // One slice of an expert's pre-capacity segment, rows [r0, r0 + kCapSlice) of
 // tmp_sorted (pair ids, in pair order) and tmp_key (their logit keys), segment
-// [pre_off[i], pre_off[i+1]).  Writes sorted_pairs for the slice's kept pairs (at
-// their rows from offsets[i]) and, for every row of the slice, its final row or -1
-// in tmp_final; the gather resolves pair_row through tmp_final.
+// [a, a + n).  Writes sorted_pairs for the slice's kept pairs (at their rows from
+// the expert's first kept row out0) and, for every row of the slice, its final row
+// or -1 in tmp_final; the gather resolves pair_row through tmp_final.
 // A kept key's row is (keys above the threshold before it) + min(keys equal to it
 // before it, equal keys kept), from one scan over the (register, wave) slots of the
 // slices up to this one, of packed counts (keys above the threshold in the low half,
 // equal in the high half), and the lanes below the key in its slot.
 __global__ __launch_bounds__(kCapThreads) void cap_select_kernel(const int32_t* __restrict__ tmp_sorted,
                                                                  const uint32_t* __restrict__ tmp_key,
-                                                                 const int32_t* __restrict__ pre_off,
-                                                                 const int32_t* __restrict__ offsets,
                                                                  const int32_t* __restrict__ slice_off,
+                                                                 const int32_t* __restrict__ slice_desc,
                                                                  const uint32_t* __restrict__ slice_hist, int L,
                                                                  int cap, int32_t* __restrict__ sorted_pairs,
                                                                  int32_t* __restrict__ tmp_final) {
@@ -655,12 +668,10 @@ __global__ __launch_bounds__(kCapThreads) void cap_select_kernel(const int32_t* 
   int& s_want = reinterpret_cast<int*>(wsum)[kCapWaves + 1];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int i = slice_expert(slice_off, L, b, reinterpret_cast<int*>(wsum) + kCapWaves + 2);
-  if (i < 0) return;
-  const int a = pre_off[i];
-  const int n = pre_off[i + 1] - a;
-  const int out0 = offsets[i];
-  const int sl = b - slice_off[i];
+  int4 dsc;
+  if (!slice_of(slice_off, slice_desc, L, b, &dsc)) return;
+  const int s0 = dsc.x, a = dsc.y, n = dsc.z, out0 = dsc.w;
+  const int sl = b - s0;
   const int r0 = sl * kCapSlice;
   const int32_t* seg = tmp_sorted + a;
 
@@ -711,7 +722,7 @@ __global__ __launch_bounds__(kCapThreads) void cap_select_kernel(const int32_t* 
   // leading digit: the slices' histograms summed (thread t takes digits 4t .. 4t+3),
   // no padding counted; the counters of the later passes cleared meanwhile
   {
-    const int s0 = slice_off[i], s1 = slice_off[i + 1];
+    const int s1 = s0 + nreg / kSliceRegs + (nreg % kSliceRegs != 0);  // the expert's slices: ceil(n / kCapSlice)
     u32x4_t acc = {0u, 0u, 0u, 0u};
 #pragma unroll 4
     for (int s = s0; s < s1; ++s) {
@@ -775,16 +786,17 @@ __global__ __launch_bounds__(kCapThreads) void cap_select_kernel(const int32_t* 
     }
   }
   __syncthreads();
-  {
-    const uint32_t v = tid < kRankSlots ? slot_cnt[tid] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan_u32(v, wsum, &tot);
-    if (tid < kRankSlots) slot_cnt[tid] = ex;
+  if (wave == 0) {  // exclusive scan of the kRankSlots slots by one wave: lane l holds slots l and 64 + l
+    const uint32_t v0 = slot_cnt[lane], v1 = lane < kRankSlots - 64 ? slot_cnt[64 + lane] : 0u;
+    const uint32_t i0 = wave_scan_u32(v0), i1 = wave_scan_u32(v1);
+    const uint32_t t0 = uint32_t(__builtin_amdgcn_readlane(int(i0), 63));
+    slot_cnt[lane] = i0 - v0;
+    if (lane < kRankSlots - 64) slot_cnt[64 + lane] = t0 + i1 - v1;
   }
   __syncthreads();
   // every pair-id load in flight at once, then the stores (a kept row always lands in
   // [out0, out_end); the test only keeps this kernel and the gather in bounds)
-  const int out_end = offsets[i + 1];
+  const int out_end = out0 + cap;  // an expert over capacity keeps exactly cap rows
   int32_t f[kSliceRegs], v[kSliceRegs];
 #pragma unroll
   for (int jj = 0; jj < kSliceRegs; ++jj) {
@@ -900,7 +912,7 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
   const int64_t p0 = t0 * k;
 
   if (FUSED) {
-    chunk_bases(blk_all, nblk, E, begin, L, chunk, -1, run, counts, offsets, nullptr, nullptr, num_dropped);
+    chunk_bases(blk_all, nblk, E, begin, L, chunk, -1, run, counts, offsets, nullptr, nullptr, nullptr, num_dropped);
   } else {
     for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
   }
@@ -995,7 +1007,7 @@ moe_status launch_dispatch(const DispatchArgs& a) {
   if (!fused) {
     MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all,
                nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.scr.slice_off,
-               a.num_dropped);
+               a.scr.slice_desc, a.num_dropped);
   }
   if (cap) {
     const size_t scat_lds = size_t(L) * (1 + kDispatchThreads / 64) * 4;
@@ -1006,7 +1018,8 @@ moe_status launch_dispatch(const DispatchArgs& a) {
       if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_scatter: LDS attribute: %s", hipGetErrorString(e));
     }
     MOE_LAUNCH("dispatch_scatter", scatter, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n, begin, L, chunk, a.scr.blk_base, a.scr.blk_all,
-               nblk, E, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.slice_off, a.num_dropped,
+               nblk, E, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.slice_off, a.scr.slice_desc,
+               a.num_dropped,
                a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
     {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(cap_hist_kernel),
@@ -1016,9 +1029,9 @@ moe_status launch_dispatch(const DispatchArgs& a) {
     // one block per slice slot; blocks past the last slice return at once
     const dim3 slices(unsigned(cap_slices_max(d)));
     MOE_LAUNCH("dispatch_cap_hist", cap_hist_kernel, slices, dim3(kCapThreads), kCapLds, a.s, a.scr.tmp_key,
-               a.scr.pre_off, a.scr.slice_off, L, int(a.capacity), a.scr.slice_hist);
+               a.scr.slice_off, a.scr.slice_desc, L, int(a.capacity), a.scr.slice_hist);
     MOE_LAUNCH("dispatch_capacity", cap_select_kernel, slices, dim3(kCapThreads), kSelLds, a.s, a.scr.tmp_sorted,
-               a.scr.tmp_key, a.scr.pre_off, a.offsets, a.scr.slice_off, a.scr.slice_hist, L, int(a.capacity),
+               a.scr.tmp_key, a.scr.slice_off, a.scr.slice_desc, a.scr.slice_hist, L, int(a.capacity),
                a.sorted_pairs, a.scr.tmp_final);
     const dim3 grid(unsigned((d->num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock));
     MOE_LAUNCH("dispatch_gather", gather_kernel, grid, dim3(256), 0, a.s, static_cast<const u32x4_t*>(a.x), a.pair_row,

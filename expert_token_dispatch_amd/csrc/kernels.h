@@ -65,6 +65,8 @@ struct DispatchScratch {
   uint32_t* tmp_key;   // [T*k]       logit keys beside it (capacity only)
   int32_t* tmp_final;  // [T*k]       final row of each pre-capacity row, -1 if cut (capacity only)
   int32_t* slice_off;  // [L+1]       first capacity slice of each local expert (capacity only)
+  int32_t* slice_desc; // [slices, 4] per capacity slice: its expert's first slice, pre-capacity segment
+                       //             start and length, and first kept row (capacity only)
   uint32_t* slice_hist; // [slices, 4096] leading-digit histogram of each slice of an expert over
                         //             capacity (capacity only)
 };
