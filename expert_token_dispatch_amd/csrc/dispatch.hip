@@ -59,7 +59,6 @@ size_t dispatch_scratch_bytes(const moe_layer_desc* d) {
   size_t b = 0;
   b += align_up(size_t(nblk) * d->num_experts * 4, 256);
   b += align_up(size_t(nblk) * d->local_count * 4, 256);
-  b += align_up(size_t(d->local_count + 1) * 4, 256);
   if (d->capacity_factor > 0) {
     b += 3 * align_up(size_t(n) * 4, 256);
     b += align_up(size_t(d->local_count + 1) * 4, 256);
@@ -77,8 +76,6 @@ DispatchScratch carve_dispatch_scratch(const moe_layer_desc* d, void* ws) {
   p += align_up(size_t(nblk) * d->num_experts * 4, 256);
   s.blk_base = reinterpret_cast<int32_t*>(p);
   p += align_up(size_t(nblk) * d->local_count * 4, 256);
-  s.pre_off = reinterpret_cast<int32_t*>(p);
-  p += align_up(size_t(d->local_count + 1) * 4, 256);
   const int64_t n = d->num_tokens * d->top_k;
   if (d->capacity_factor > 0) {
     s.tmp_sorted = reinterpret_cast<int32_t*>(p);
@@ -195,7 +192,7 @@ constexpr int kScanCache = 32;   // chunk counts a thread keeps in registers bet
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ blk_all, int nblk, int E,
                                                             int begin, int L, int64_t cap, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ pre_off,
+                                                            int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ blk_base,
                                                             int32_t* __restrict__ slice_off,
                                                             int32_t* __restrict__ slice_desc,
@@ -275,7 +272,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
     if (cap >= 0) ex_s = block_exclusive_scan((n + kCapSlice - 1) / kCapSlice, wsum, &tot_s);
     if (i < L) {
       pre[i] = carry_pre + ex_n;
-      pre_off[i] = carry_pre + ex_n;
       offsets[i] = carry_post + ex_k;
       if (cap >= 0) {
         slice_off[i] = carry_sl + ex_s;
@@ -288,7 +284,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
   if (tid == 0) {
     pre[L] = carry_pre;
-    pre_off[L] = carry_pre;
     offsets[L] = carry_post;
     if (cap >= 0) slice_off[L] = carry_sl;
   }
@@ -353,12 +348,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
 // writes counts [E] (the experts outside the local range one per block, its threads
 // splitting the column: one block summing them all would be the last to finish),
 // the segment offsets (after the cut when cap >= 0) and the drop count; with a cut,
-// also the pre-capacity offsets and the first capacity slice of each expert.
+// also the first capacity slice of each expert and the slices' descriptors.
 // Every thread of the block must call it.
 __device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E, int begin, int L, int chunk,
                             int64_t cap, int32_t* run, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                            int32_t* __restrict__ pre_off, int32_t* __restrict__ slice_off,
-                            int32_t* __restrict__ slice_desc, int64_t* __restrict__ num_dropped) {
+                            int32_t* __restrict__ slice_off, int32_t* __restrict__ slice_desc,
+                            int64_t* __restrict__ num_dropped) {
   constexpr int kWaves = kDispatchThreads / 64;
   __shared__ int wsum[kWaves];
   __shared__ int ptot[kDispatchThreads], pbef[kDispatchThreads];
@@ -403,7 +398,6 @@ __device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E
       const int ex_k = carry_post + block_exclusive_scan(kept, wsum, &all_k);
       const int ex_s = carry_sl + block_exclusive_scan((tot + kCapSlice - 1) / kCapSlice, wsum, &all_s);
       if (first && tid < Lg) {
-        pre_off[i0 + tid] = ex;
         offsets[i0 + tid] = ex_k;
         slice_off[i0 + tid] = ex_s;
         write_slice_desc(slice_desc, ex_s, ex, tot, ex_k);
@@ -418,10 +412,7 @@ __device__ void chunk_bases(const int32_t* __restrict__ blk_all, int nblk, int E
     if (cap >= 0) (void)block_exclusive_scan(dropped, wsum, &all_d);
     if (tid == 0) {
       offsets[L] = cap < 0 ? carry : carry_post;
-      if (cap >= 0) {
-        pre_off[L] = carry;
-        slice_off[L] = carry_sl;
-      }
+      if (cap >= 0) slice_off[L] = carry_sl;
       if (num_dropped != nullptr) *num_dropped = all_d;
     }
   }
@@ -456,7 +447,6 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
                                                                    const int32_t* __restrict__ blk_all, int nblk, int E,
                                                                    int64_t cap, int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ pre_off,
                                                                    int32_t* __restrict__ slice_off,
                                                                    int32_t* __restrict__ slice_desc,
                                                                    int64_t* __restrict__ num_dropped,
@@ -471,7 +461,7 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   if (FUSED) {
-    chunk_bases(blk_all, nblk, E, begin, L, int(blockIdx.x), cap, run, counts, offsets, pre_off, slice_off,
+    chunk_bases(blk_all, nblk, E, begin, L, int(blockIdx.x), cap, run, counts, offsets, slice_off,
                 slice_desc, num_dropped);
   } else {
     for (int i = tid; i < L; i += kDispatchThreads) run[i] = blk_base[size_t(blockIdx.x) * L + i];
@@ -912,7 +902,7 @@ __global__ __launch_bounds__(kDispatchThreads) void place_kernel(const int32_t* 
   const int64_t p0 = t0 * k;
 
   if (FUSED) {
-    chunk_bases(blk_all, nblk, E, begin, L, chunk, -1, run, counts, offsets, nullptr, nullptr, nullptr, num_dropped);
+    chunk_bases(blk_all, nblk, E, begin, L, chunk, -1, run, counts, offsets, nullptr, nullptr, num_dropped);
   } else {
     for (int q = tid; q < L; q += kDispatchThreads) run[q] = blk_base[size_t(chunk) * L + q];
   }
@@ -1006,7 +996,7 @@ moe_status launch_dispatch(const DispatchArgs& a) {
   const bool fused = int64_t(nblk) * E <= kFuseEntries;
   if (!fused) {
     MOE_LAUNCH("dispatch_scan", scan_kernel, dim3(1), dim3(kScanThreads), size_t(E + L + 1) * 4, a.s, a.scr.blk_all,
-               nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.blk_base, a.scr.slice_off,
+               nblk, E, begin, L, a.capacity, a.counts, a.offsets, a.scr.blk_base, a.scr.slice_off,
                a.scr.slice_desc, a.num_dropped);
   }
   if (cap) {
@@ -1018,7 +1008,7 @@ moe_status launch_dispatch(const DispatchArgs& a) {
       if (e != hipSuccess) return set_error(MOE_ERR_HIP, "dispatch_scatter: LDS attribute: %s", hipGetErrorString(e));
     }
     MOE_LAUNCH("dispatch_scatter", scatter, dim3(nblk), dim3(kDispatchThreads), scat_lds, a.s, a.topk_ids, n, begin, L, chunk, a.scr.blk_base, a.scr.blk_all,
-               nblk, E, a.capacity, a.counts, a.offsets, a.scr.pre_off, a.scr.slice_off, a.scr.slice_desc,
+               nblk, E, a.capacity, a.counts, a.offsets, a.scr.slice_off, a.scr.slice_desc,
                a.num_dropped,
                a.scr.tmp_sorted, a.pair_row, a.topk_logit, a.scr.tmp_key);
     {

@@ -60,7 +60,6 @@ moe_status launch_selection_bias_update(const moe_layer_desc* d, const int32_t* 
 struct DispatchScratch {
   int32_t* blk_all;    // [nblk, E]   per-block counts over all experts
   int32_t* blk_base;   // [nblk, L]   first (pre-capacity) row of each block's pairs
-  int32_t* pre_off;    // [L+1]       pre-capacity segment offsets
   int32_t* tmp_sorted; // [T*k]       pre-capacity permutation (capacity only)
   uint32_t* tmp_key;   // [T*k]       logit keys beside it (capacity only)
   int32_t* tmp_final;  // [T*k]       final row of each pre-capacity row, -1 if cut (capacity only)

@@ -252,10 +252,11 @@ moe_status moe_dispatch(const moe_layer_desc* d, const void* x, const int32_t* t
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and outputs as moe_dispatch, bit for bit, but the
  * dispatch scratch (per-chunk expert histograms, per-chunk segment bases,
- * the pre-capacity offsets and permutation) lives in a static 16 MiB device
- * buffer of the library instead of a caller workspace.  Each GPU the library
- * runs on holds its own buffer until the process ends; its address is
- * resolved on the first call on each device.  The call allocates nothing.
+ * the pre-capacity permutation and its slice tables) lives in a static
+ * 16 MiB device buffer of the library instead of a caller workspace.  Each
+ * GPU the library runs on holds its own buffer until the process ends; its
+ * address is resolved on the first call on each device.  The call allocates
+ * nothing.
  * Arguments as moe_dispatch, without ws / ws_bytes.  Every call on one GPU
  * shares that GPU's buffer: calls that overlap in time on one GPU (other
  * streams, other host threads) race and must be serialised by the caller.
