@@ -162,15 +162,18 @@ def test_zero_capacity_drops_every_pair():
     assert np.all(y == 0) and np.all(ref["y"] == 0)
 
 
-@pytest.mark.parametrize("E,L,begin,cf", [(2048, 2048, 0, 0.0), (4096, 1500, 100, 0.0), (4096, 3000, 1000, 2.0)],
+@pytest.mark.parametrize("E,L,begin,cf,T", [(2048, 2048, 0, 0.0, 3000), (4096, 1500, 100, 0.0, 3000),
+                                             (4096, 3000, 1000, 2.0, 3000), (4096, 2000, 50, 40.0, 16384)],
                          ids=lambda v: str(v))
-def test_dispatch_with_thousands_of_experts(E, L, begin, cf):
+def test_dispatch_with_thousands_of_experts(E, L, begin, cf, T):
     # Dispatch on given top-k ids with more experts than the router takes (up to the 4096
     # the descriptor allows, up to 3000 local): the chunk histogram table is past the
-    # size the place kernel sums itself, so the scan runs as its own launch over column
-    # groups of 1024 experts; with a capacity factor, the cut runs one block per local
-    # expert over segments of a few pairs.
-    s = synth.spec("gptoss_ep8_share", T=3000, H=64, I=32, E=E, k=4, local_begin=begin, L=L, capacity_factor=cf)
+    # size the place and scatter kernels sum themselves, so the scan runs as its own
+    # launch over column groups of 1024 experts (and writes the capacity slice table);
+    # with a capacity factor, the cut runs over segments of a few pairs, and with 16384
+    # tokens the crowded expert's ~5460 pairs span two 4096-row slices with equal scores
+    # across the slice edge.
+    s = synth.spec("gptoss_ep8_share", T=T, H=64, I=32, E=E, k=4, local_begin=begin, L=L, capacity_factor=cf)
     inp = synth.make_layer(s)
     layer, x = layer_of(inp)
     rng = np.random.default_rng(E + L)
@@ -191,6 +194,8 @@ def test_dispatch_with_thousands_of_experts(E, L, begin, cf):
     np.testing.assert_array_equal(np_of(g["x_sorted"])[:P], np_of(x)[d["sorted_pairs"] // s.k])
     if cf > 0:
         assert d["num_dropped"] > 0
+    if T > 3000:
+        assert d["counts"][begin + 7] > 4096 > oracle.capacity_limit(cf, s.T, s.k, s.E)
 
 
 @pytest.mark.parametrize("H,I", [(128, 512), (512, 128)], ids=["gate_up_128", "down_128"])
