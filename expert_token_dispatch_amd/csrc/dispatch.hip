@@ -507,8 +507,8 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
 // The cut keeps the cap pairs with the largest keys of each expert over capacity
 // (logit descending, equal keys in segment = token order).  Its blocks each take
 // one slice of kCapSlice consecutive pre-capacity rows of one expert (the slice
-// table comes with the offsets), so a hot expert's segment is spread over several
-// CUs:
+// descriptors are written with the offsets), so a hot expert's segment is spread
+// over several CUs:
 //   cap_hist    per slice of an expert over capacity, the histogram of the keys'
 //               leading 12-bit digit (bits 31..20);
 //   cap_select  per slice: an expert within capacity copies its rows; otherwise the
@@ -517,8 +517,8 @@ __global__ __launch_bounds__(kDispatchThreads) void scatter_kernel(const int32_t
 //               largest key from them (two 10-bit digits over the few keys that
 //               share the leading one), redundantly in every block of the expert
 //               (no grid-wide wait); then it ranks the rows of its own slice from
-//               a ballot scan over the (register, wave) slots of the slices up to
-//               its own.
+//               one scan over per-wave counts of the earlier slices and ballot
+//               counts of its own (register, wave) slots.
 constexpr int kCapThreads = 1024;
 constexpr int kCapPerThread = 32;  // register-resident keys per thread (segments up to 32768 pairs)
 constexpr int kCapWaves = kCapThreads / 64;
