@@ -21,7 +21,7 @@ namespace {
 
 constexpr int kTokensPerBlock = 4;
 
-// KB: slots whose rows are loaded together (k rounded up to 2, 4 or 8; larger k goes in batches of 8);
+// KB: slots whose rows are loaded together (k rounded up to 2, 4, 6 or 8; larger k goes in batches of 8);
 // each lane takes kSlices 16-byte slices of the row per pass, so KB * kSlices loads are in flight
 template <typename T, int KB, int kSlices>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ ys, const int32_t* __restrict__ pair_row,
@@ -88,9 +88,11 @@ moe_status launch_t(const CombineArgs& a) {
   const int k = d->top_k;
   const uint4* ys = static_cast<const uint4*>(a.y_sorted);
   uint4* y = static_cast<uint4*>(a.y);
-  // slices per lane and pass: 8 for pairs of slots, 4 for batches of eight; batches of four take 6
-  // when a row then fits fewer, fuller passes (a 2880-wide bf16 row: one pass of 384 slices instead
-  // of two of 256; measured 31.0 -> 28.6 us on the gpt-oss-like share)
+  // slices per lane and pass: 8 for pairs of slots, 4 for batches of six or eight; batches of four
+  // take 6 when a row then fits fewer, fuller passes (a 2880-wide bf16 row: one pass of 384 slices
+  // instead of two of 256; measured 31.0 -> 28.6 us on the gpt-oss-like share).  Five or six slots
+  // load as one batch of six rather than eight: 150 registers instead of 184, three waves per SIMD
+  // instead of two (skewed_capacity, k = 6: 78.6 -> 73.4 us, same box, interleaved runs)
   const auto waste = [&](int sl) { return (vec_per_row + 64 * sl - 1) / (64 * sl) * 64 * sl - vec_per_row; };
   if (k <= 2) {
     MOE_LAUNCH("combine", (combine_kernel<T, 2, 8>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k,
@@ -103,6 +105,9 @@ moe_status launch_t(const CombineArgs& a) {
       MOE_LAUNCH("combine", (combine_kernel<T, 4, 4>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k,
                  vec_per_row, y);
     }
+  } else if (k <= 6) {
+    MOE_LAUNCH("combine", (combine_kernel<T, 6, 4>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k,
+               vec_per_row, y);
   } else {
     MOE_LAUNCH("combine", (combine_kernel<T, 8, 4>), grid, dim3(256), 0, a.s, ys, a.pair_row, a.topk_w, T_, k,
                vec_per_row, y);
