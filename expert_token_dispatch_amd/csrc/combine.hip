@@ -88,7 +88,8 @@ moe_status launch_t(const CombineArgs& a) {
   const int k = d->top_k;
   const uint4* ys = static_cast<const uint4*>(a.y_sorted);
   uint4* y = static_cast<uint4*>(a.y);
-  // slices per lane and pass: 8 for pairs of slots, 4 for batches of six or eight; batches of four
+  // slices per lane and pass: 8 for pairs of slots (4: mixtral_like 35.7 -> 39.1 us, so not), 4 for
+  // batches of six or eight; batches of four
   // take 6 when a row then fits fewer, fuller passes (a 2880-wide bf16 row: one pass of 384 slices
   // instead of two of 256; measured 31.0 -> 28.6 us on the gpt-oss-like share).  Five or six slots
   // load as one batch of six rather than eight: 150 registers instead of 184, three waves per SIMD

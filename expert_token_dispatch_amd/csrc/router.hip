@@ -528,7 +528,10 @@ moe_status launch_topk_rows(const RouteArgs& a, const float* partial, int nslice
 
 template <int MAXK>
 moe_status launch_topk(const RouteArgs& a, const float* partial, int nslice, const float* bias) {
-  // one 16-lane row per token, 8 or 16 logits per lane (the router takes up to 256 experts)
+  // one 16-lane row per token, 4, 8 or 16 logits per lane (the router takes up to 256 experts);
+  // four for E <= 64 halves each round's per-lane scan (same box, interleaved: skewed_capacity
+  // 18.4 -> 15.6 us, mixtral_like 7.0 -> 6.2, tiny_fp32 5.9 -> 5.1)
+  if (a.d->num_experts <= 64) return launch_topk_rows<MAXK, 4>(a, partial, nslice, bias);
   if (a.d->num_experts <= 128) return launch_topk_rows<MAXK, 8>(a, partial, nslice, bias);
   return launch_topk_rows<MAXK, 16>(a, partial, nslice, bias);
 }
