@@ -17,22 +17,22 @@
 //             lane per distinct id touches the LDS histogram;
 //   scan      one block: totals per expert, (capacity), exclusive scans into
 //             segment offsets, and for every (chunk, expert) the first row of
-//             that chunk's pairs (range sums over chunks, then prefixes);
-//   scatter   per block again, in rounds of 256 pairs: the rank of a pair
-//             among equal experts is its rank within its wave (match-any +
-//             popcount of lower lanes) plus the counts of earlier waves and
-//             earlier rounds -- no atomics, so the order is deterministic;
-//   capacity  (only with a limit) one block per local expert: the expert's
-//             keys sit in registers (element j*1024 + thread); radix select of
-//             the C-th largest key (logit desc, then token asc) in two 16-bit
-//             passes over packed 16-bit counters, then a stable compaction from
-//             per-wave ballots and one scan over the 512 (register, wave) slots;
+//             that chunk's pairs (range sums over chunks, then prefixes); when
+//             the chunk histogram table is small (chunks x experts <= 65536)
+//             the place or scatter kernel's blocks each sum the columns they
+//             need instead, so no scan launch sits after the router;
+//   scatter   (with a capacity limit) per block again, in rounds of 256 pairs:
+//             the rank of a pair among equal experts is its rank within its
+//             wave (match-any + popcount of lower lanes) plus the counts of
+//             earlier waves and earlier rounds -- no atomics, so the order is
+//             deterministic; each pair's logit key goes beside it;
+//   capacity  (only with a limit) per 4096-row slice of an expert's segment: a
+//             leading-digit histogram of each slice, then a radix select of the
+//             C-th largest key (logit desc, then token asc) and a stable
+//             compaction of the slice (see the capacity section below);
 //   place     without a capacity cut, scatter and row copy in one kernel:
 //             ranks as in scatter, then token-major copies (one read of x[t],
-//             one write per kept local pair, 16-byte vectors); when the chunk
-//             histogram table is small (chunks x experts <= 65536) every place
-//             block also sums the columns it needs itself, so no scan launch
-//             sits between the router and the copy;
+//             one write per kept local pair, 16-byte vectors);
 //   gather    with a capacity cut, the same token-major copy after it.
 // The gather writes x_sorted with nontemporal stores: a capacity-limited layer
 // has many pairs (hundreds of MB of rows, more than the last-level cache), so
