@@ -51,8 +51,9 @@ def _both(s):
 
 
 def test_noalloc_dispatch_matches_workspace_dispatch_call_after_call():
-    # capacity path (scan, scatter, capacity cut, gather), then a smaller call of the same
-    # kind, then the fused no-capacity path, then a smaller one of that
+    # capacity path (scatter with the scan folded in, slice histograms, capacity cut over a
+    # hot expert's two 4096-row slices, gather), then a smaller call of the same kind, then
+    # the fused no-capacity path, then a smaller one of that
     cases = [
         synth.spec("skewed_capacity", T=6000, H=256, I=64),
         synth.spec("skewed_capacity", T=900, H=256, I=64),
